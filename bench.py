@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed-weight product on one MI355X.
+
+Headline (one JSON line on stdout): decode GEMV of the Llama-70B gate/up
+projection, K = 8192 inputs x N = 28672 outputs, group RTN 4-bit, groups of
+64 with fp16 scale + offset, bf16 activations, batch 1.  A step is one
+launch of that GEMV on the next copy of a rotating pool of distinct packed
+weights (>= 2 GiB, larger than the 256 MB Infinity Cache plus L2, so every
+step streams its bytes from HBM).  value = compressed bytes per step x steps
+/ wall time of the timed region (inputs resident in HBM, bracketed by
+torch.cuda.synchronize()).
+
+Also reported:
+  roofline      HBM bytes/launch (algorithmic: codes + meta) / average kernel
+                time measured with HIP events on the launch stream, against the
+                8 TB/s HBM3E peak; `traffic` comes from the committed rocprofv3
+                FETCH_SIZE/WRITE_SIZE summary when it matches the current kernel
+                source, else null.
+  cpu_baseline  the fp64 CPU oracle (unpack codes, rebuild W_hat, multiply) on a
+                bounded sample of rows of the same matrix.
+  rows          every other row of the hot path, timed the same way: batch 16,
+                the mixed-width layer shapes, the binary low-rank GEMV, prefill
+                GEMM in both formats (MFMA utilisation), whole-layer tok/s
+                equivalents.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["compressed_gemv_amd/csrc/gemv_group.hip", "compressed_gemv_amd/csrc/common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_b1_gate_8192x28672_4b_g64_traffic.md")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """Bytes/launch from the committed pmc summary, if it matches the source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--pool-gib", type=float, default=2.0)
+    ap.add_argument("--no-rows", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch one plain 1 GiB device copy (pmc calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+                         "(the product shards by output rows with no exchange; see the design notes). "
+                         "Run with --gpus 1.\n")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import compressed_gemv_amd as cg
+    from workloads import LAYER_SHAPES, MIXED_SETS, N_LAYERS, ATTN, layer_weights, layer_x, binlr_factors
+
+    cg.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf16(a):
+        return to_dev(a.view(np.int16)).view(torch.bfloat16)
+
+    def pool_of(tensors, nbytes):
+        n = max(2, int(args.pool_gib * (1 << 30) // nbytes) + 1)
+        return [tuple(t.clone() for t in tensors) for _ in range(n)]
+
+    def time_launches(fn, steps, warmup):
+        """(wall seconds, event seconds) over `steps` launches after `warmup`."""
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            fn(warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return t1 - t0, e0.elapsed_time(e1) * 1e-3
+
+    # ------------------------------------------------------------ headline
+    K, N = LAYER_SHAPES["gate"]
+    bits, group = 4, 64
+    log(f"generating gate weights {N}x{K}")
+    W = layer_weights("gate")
+    codes, meta = cg.qpack_group(to_dev(W), bits, group)
+    nbytes = codes.numel() + meta.numel() * 4
+    assert nbytes == 132_120_576
+    pool = pool_of((codes, meta), nbytes)
+    x = bf16(layer_x(K, 1))
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+    def step(i):
+        c, m = pool[i % len(pool)]
+        cg.qgemv_group(c, m, N, K, bits, group, x, y=y)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    wall, ev = time_launches(step, args.steps, args.warmup)
+    value = nbytes * args.steps / wall / 1e9
+    achieved = nbytes * args.steps / ev / 1e9
+    log(f"headline: {wall / args.steps * 1e6:.2f} us/step wall, {ev / args.steps * 1e6:.2f} us/launch events, "
+        f"{achieved:.0f} GB/s")
+    del pool
+    torch.cuda.empty_cache()
+
+    rows = {}
+    if not args.no_rows:
+        rows = measure_rows(cg, torch, np, dev, W, to_dev, bf16, pool_of, time_launches, log,
+                            LAYER_SHAPES, MIXED_SETS, N_LAYERS, ATTN, layer_weights, layer_x, binlr_factors)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(np, W, bits, group, log)
+
+    traffic = committed_traffic()
+    out = {
+        "metric": "compressed-weight GEMV GB/s (% HBM peak) at 8192x28672, batch 1",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode GEMV, Llama-70B gate/up projection K=8192 x N=28672, group-RTN 4-bit, "
+                        "groups of 64 with fp16 scale+offset, bf16 activations, batch 1",
+            "K": K, "N": N, "bits": bits, "group": group, "batch": 1,
+            "compressed_bytes_per_step": nbytes,
+            "rotating_pool_copies": max(2, int(args.pool_gib * (1 << 30) // nbytes) + 1),
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "tok_s_equivalent_80_layers_4b_g64": round(value * 1e9 / (N_LAYERS * layer_bytes(4, 64, 4, 64)), 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "gemv_b1_kernel<4,64,bf16>",
+            "per_launch_us": round(ev / args.steps * 1e6, 3),
+            "kernel_source_sha": kernel_source_sha(),
+        },
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _group_bytes(N, K, bits, group):
+    return N * K * bits // 8 + N * (K // group) * 4
+
+
+def layer_bytes(attn_bits, attn_group, mlp_bits, mlp_group):
+    from workloads import LAYER_SHAPES, ATTN
+    tot = 0
+    for name, (K, N) in LAYER_SHAPES.items():
+        if name in ATTN:
+            tot += _group_bytes(N, K, attn_bits, attn_group)
+        else:
+            tot += _group_bytes(N, K, mlp_bits, mlp_group)
+    return tot
+
+
+def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launches, log,
+                 LAYER_SHAPES, MIXED_SETS, N_LAYERS, ATTN, layer_weights, layer_x, binlr_factors):
+    rows = {}
+    steps, warm = 200, 20
+
+    def gemv_row(name, W, bits, group, B):
+        N, K = W.shape
+        codes, meta = cg.qpack_group(to_dev(W), bits, group)
+        nbytes = codes.numel() + meta.numel() * 4
+        pool = pool_of((codes, meta), nbytes)
+        x = bf16(layer_x(K, B))
+        y = torch.empty((B, N), dtype=torch.float32, device=dev)
+
+        def f(i):
+            c, m = pool[i % len(pool)]
+            cg.qgemv_group(c, m, N, K, bits, group, x, y=y)
+        wall, ev = time_launches(f, steps, warm)
+        gbs = nbytes * steps / ev / 1e9
+        del pool
+        torch.cuda.empty_cache()
+        return {"us": round(ev / steps * 1e6, 3), "GB/s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / 8000.0, 2), "bytes": nbytes}
+
+    # batch 16 on the headline shape
+    rows["gemv_4b_g64_gate_B16"] = gemv_row("gate", W_gate, 4, 64, 16)
+    log("B16:", rows["gemv_4b_g64_gate_B16"])
+    # whole 4-bit layer set at batch 1, and the mixed-width sets
+    for label, spec in [("4b_g64", {"attn_bits": 4, "mlp_bits": 4, "group": 64})] + list(MIXED_SETS.items()):
+        per = {}
+        t_layer = 0.0
+        for name in ["q", "k", "v", "o", "gate", "up", "down"]:
+            bits = spec["attn_bits"] if name in ATTN else spec["mlp_bits"]
+            Wn = W_gate if name in ("gate", "up") else layer_weights(name)
+            r = gemv_row(name, Wn, bits, spec["group"], 1)
+            per[name] = r
+            t_layer += r["us"]
+        layer_b = sum(v["bytes"] for v in per.values())
+        rows[f"layer_set_{label}_B1"] = {
+            "sum_kernel_us_per_layer": round(t_layer, 2),
+            "GB/s": round(layer_b / (t_layer * 1e-6) / 1e9, 1),
+            "tok_s_equivalent_80_layers": round(1.0 / (N_LAYERS * t_layer * 1e-6), 1),
+            "per_matrix": per,
+        }
+        log(label, rows[f"layer_set_{label}_B1"]["GB/s"], "GB/s")
+    # mixed widths at batch 8 (MLP shape)
+    for bits in (3, 2):
+        rows[f"gemv_{bits}b_g32_gate_B8"] = gemv_row("gate", W_gate, bits, 32, 8)
+    for bits in (6, 5):
+        rows[f"gemv_{bits}b_g32_q_B8"] = gemv_row("q", layer_weights("q"), bits, 32, 8)
+
+    # binary low-rank GEMV
+    for (K, N, r) in [(8192, 28672, 4096), (8192, 8192, 2048)]:
+        U, V, s1, s2 = binlr_factors(K, N, r)
+        ub, vb = cg.qpack_binlr(to_dev(U), to_dev(V))
+        nbytes = (r * (N + K)) // 8 + 2 * (N + K)
+        pool = pool_of((ub, vb), ub.numel() * 4 + vb.numel() * 4)
+        s1d, s2d = to_dev(s1.view(np.int16)), to_dev(s2.view(np.int16))
+        x = bf16(layer_x(K, 1, config=4))
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(cg.qbinlr_sizes(N, K, r, 1)[2], dtype=torch.uint8, device=dev)
+
+        def f(i):
+            a, b = pool[i % len(pool)]
+            cg.qgemv_binlr(a, b, s1d, s2d, N, K, r, x, y=y, ws=ws)
+        wall, ev = time_launches(f, steps, warm)
+        gbs = nbytes * steps / ev / 1e9
+        rows[f"binlr_gemv_{K}x{N}_r{r}_B1"] = {
+            "us": round(ev / steps * 1e6, 3), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / 8000.0, 2),
+            "bytes": nbytes,
+            "tok_s_equivalent_5.35GB_model": round(gbs * 1e9 / 5.35e9, 1),
+        }
+        log("binlr", rows[f"binlr_gemv_{K}x{N}_r{r}_B1"])
+        del pool
+        torch.cuda.empty_cache()
+
+    # prefill GEMM, both formats
+    K, N = 8192, 28672
+    codes, meta = cg.qpack_group(to_dev(W_gate), 4, 64)
+    wq = cg.make_qweight_group(codes, meta, N, K, 4, 64)
+    U, V, s1, s2 = binlr_factors(8192, 28672, 4096)
+    ub, vb = cg.qpack_binlr(to_dev(U), to_dev(V))
+    s1d, s2d = to_dev(s1.view(np.int16)), to_dev(s2.view(np.int16))
+    wb = cg.make_qweight_binlr(ub, vb, s1d, s2d, N, K, 4096)
+    for M in (512, 4096):
+        X = bf16(layer_x(K, M, config=5))
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        for label, w, flops in [("rtn_4b_g64", wq, 2.0 * M * N * K), ("binlr_r4096", wb, 2.0 * M * 4096 * (K + N))]:
+            ws = None
+            need = cg.qgemm_prefill_ws(w, M)
+            if need:
+                ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            it = 5 if M == 4096 else 10
+            wall, ev = time_launches(lambda i: cg.qgemm_prefill(w, X, Y=Y, ws=ws), it, 2)
+            tf = flops * it / ev / 1e12
+            rows[f"prefill_{label}_M{M}"] = {"us": round(ev / it * 1e6, 1), "TFLOP/s": round(tf, 1),
+                                             "mfma_util_vs_2.5PF": round(tf / 2500.0, 4)}
+            log("prefill", label, M, rows[f"prefill_{label}_M{M}"])
+    return rows
+
+
+def cpu_baseline(np, W, bits, group, log):
+    """The oracle as it stands, on a bounded sample of rows of the same matrix:
+    unpack codes -> rebuild W_hat (fp64) -> multiply, as GB/s of compressed
+    bytes.  Offline quantize/pack of the sample is not timed."""
+    import oracle
+    from workloads import layer_x
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    N, K = W.shape
+    x = oracle.product.bf16_to_f64(layer_x(K, 1))
+    R = 512
+    per_row = K * bits // 8 + (K // group) * 4
+    best = None
+    while True:
+        sub = W[:R]
+        q, s, o = oracle.rtn.quantize(sub, bits, group)
+        words = oracle.fmt.pack_codes(q, bits)
+        meta = oracle.fmt.pack_meta(s, o)
+        t0 = time.perf_counter()
+        W_hat = oracle.product.what_group(words, meta, R, K, bits, group)
+        _ = oracle.product.matmul_ref(W_hat, x)
+        dt = time.perf_counter() - t0
+        best = (R, dt)
+        log(f"cpu oracle: {R} rows in {dt:.2f} s")
+        if dt >= 8.0 or R >= N:
+            break
+        R = min(N, R * 2)
+    R, dt = best
+    return {
+        "value": round(R * per_row / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{R} of {N} rows of the same 8192x28672 4-bit g64 matrix "
+                  f"({R * per_row} compressed bytes): unpack + rebuild W_hat in fp64 (numpy, one thread) "
+                  f"+ fp64 product (BLAS, {threads} threads), {dt:.2f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,242 @@
+"""Python binding of libqgemv (the MI355X compressed-weight product).
+
+Thin marshalling over the C ABI in include/qgemv.h: every function here has
+the name of the C entry point it calls, takes torch tensors that already
+live on the GPU, allocates outputs with torch when none are given, passes
+raw device pointers and torch's current HIP stream, and raises QError on a
+non-zero status.  All arithmetic runs in the HIP kernels; there is no CPU
+fallback, and any call fails loudly when the shared library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "QError", "load", "lib_path", "q_abi_version", "q_format_version", "q_status_str",
+    "qgroup_sizes", "qpack_group", "qunpack_group", "qgemv_group",
+    "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr",
+    "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
+]
+
+Q_OK, Q_EINVAL, Q_EALIGN, Q_EUNSUPPORTED, Q_ERANGE, Q_EWORKSPACE, Q_EHIP = 0, -1, -2, -3, -4, -5, -6
+Q_F32, Q_BF16, Q_F16 = 0, 1, 2
+Q_FMT_GROUP, Q_FMT_BINLR = 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libqgemv.so")
+
+
+class QError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({q_status_str(status)})")
+
+
+class qweight(ctypes.Structure):
+    _fields_ = [
+        ("format", ctypes.c_int), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("bits", ctypes.c_int), ("group", ctypes.c_int),
+        ("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+        ("r", ctypes.c_int64), ("ubits", ctypes.c_void_p), ("vtbits", ctypes.c_void_p),
+        ("s1", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+    ]
+
+
+def load() -> ctypes.CDLL:
+    """Load libqgemv.so from the package directory (raises if it is missing)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libqgemv.so not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    I64, I32, P, SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "q_abi_version": (I32, []),
+        "q_format_version": (I32, []),
+        "q_status_str": (ctypes.c_char_p, [I32]),
+        "qgroup_sizes": (I32, [I64, I64, I32, I32, SZ, SZ]),
+        "qpack_group": (I32, [P, I64, I64, I32, I32, P, P, P]),
+        "qunpack_group": (I32, [P, P, I64, I64, I32, I32, P, P, P]),
+        "qgemv_group": (I32, [P, P, I64, I64, I32, I32, P, I32, I64, P, I32, P]),
+        "qbinlr_sizes": (I32, [I64, I64, I64, I64, SZ, SZ, SZ]),
+        "qpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
+        "qunpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
+        "qgemv_binlr": (I32, [P, P, P, P, I64, I64, I64, P, I32, I64, P, I32, P, ctypes.c_size_t, P]),
+        "qgemm_prefill_ws": (I32, [ctypes.POINTER(qweight), I64, SZ]),
+        "qgemm_prefill": (I32, [ctypes.POINTER(qweight), P, I32, I64, P, I32, P, ctypes.c_size_t, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != Q_OK:
+        raise QError(status, what)
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return Q_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return Q_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+
+
+def q_abi_version() -> int:
+    return load().q_abi_version()
+
+
+def q_format_version() -> int:
+    return load().q_format_version()
+
+
+def q_status_str(status: int) -> str:
+    return load().q_status_str(status).decode()
+
+
+# ------------------------------------------------------------------ group RTN
+def qgroup_sizes(N: int, K: int, bits: int, group: int):
+    c, m = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().qgroup_sizes(N, K, bits, group, ctypes.byref(c), ctypes.byref(m)), "qgroup_sizes")
+    return c.value, m.value
+
+
+def qpack_group(W: torch.Tensor, bits: int, group: int, codes=None, meta=None, stream=None):
+    """Quantize + pack fp32 W[N][K] -> (codes uint8[N*K*b/8], meta int32[N*K/g])."""
+    _need_cuda(W)
+    N, K = W.shape
+    cb, mb = qgroup_sizes(N, K, bits, group)
+    if codes is None:
+        codes = torch.empty(cb, dtype=torch.uint8, device=W.device)
+    if meta is None:
+        meta = torch.empty(mb // 4, dtype=torch.int32, device=W.device)
+    _check(load().qpack_group(_ptr(W), N, K, bits, group, _ptr(codes), _ptr(meta), _stream(stream)),
+           "qpack_group")
+    return codes, meta
+
+
+def qunpack_group(codes, meta, N: int, K: int, bits: int, group: int, want_w: bool = False, stream=None):
+    q = torch.empty((N, K), dtype=torch.uint8, device=codes.device)
+    w = torch.empty((N, K), dtype=torch.float32, device=codes.device) if want_w else None
+    _check(load().qunpack_group(_ptr(codes), _ptr(meta), N, K, bits, group, _ptr(q), _ptr(w),
+                                _stream(stream)), "qunpack_group")
+    return (q, w) if want_w else q
+
+
+def qgemv_group(codes, meta, N: int, K: int, bits: int, group: int, x: torch.Tensor,
+                y: Optional[torch.Tensor] = None, y_dtype=torch.float32, stream=None):
+    """y[B][N] = x[B][K] W_hat^T; x is bf16 (or int16/uint16 bf16 bits) or fp32."""
+    _need_cuda(codes, meta, x, y)
+    B = x.shape[0] if x.dim() == 2 else 1
+    if y is None:
+        y = torch.empty((B, N), dtype=y_dtype, device=x.device)
+    _check(load().qgemv_group(_ptr(codes), _ptr(meta), N, K, bits, group, _ptr(x), _dtype_code(x), B,
+                              _ptr(y), _dtype_code(y), _stream(stream)), "qgemv_group")
+    return y
+
+
+# ---------------------------------------------------------------- binary LR
+def qbinlr_sizes(N: int, K: int, r: int, B: int = 1):
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().qbinlr_sizes(N, K, r, B, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "qbinlr_sizes")
+    return a.value, b.value, c.value
+
+
+def qpack_binlr(U: torch.Tensor, V: torch.Tensor, ubits=None, vtbits=None, stream=None):
+    _need_cuda(U, V)
+    N, r = U.shape
+    K = V.shape[0]
+    ub, vb, _ = qbinlr_sizes(N, K, r)
+    if ubits is None:
+        ubits = torch.empty(ub // 4, dtype=torch.int32, device=U.device)
+    if vtbits is None:
+        vtbits = torch.empty(vb // 4, dtype=torch.int32, device=U.device)
+    _check(load().qpack_binlr(_ptr(U), _ptr(V), N, K, r, _ptr(ubits), _ptr(vtbits), _stream(stream)),
+           "qpack_binlr")
+    return ubits, vtbits
+
+
+def qunpack_binlr(ubits, vtbits, N: int, K: int, r: int, stream=None):
+    U = torch.empty((N, r), dtype=torch.int8, device=ubits.device)
+    V = torch.empty((K, r), dtype=torch.int8, device=ubits.device)
+    _check(load().qunpack_binlr(_ptr(ubits), _ptr(vtbits), N, K, r, _ptr(U), _ptr(V), _stream(stream)),
+           "qunpack_binlr")
+    return U, V
+
+
+def qgemv_binlr(ubits, vtbits, s1, s2, N: int, K: int, r: int, x: torch.Tensor,
+                y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                y_dtype=torch.float32, stream=None):
+    _need_cuda(ubits, vtbits, s1, s2, x, y, ws)
+    B = x.shape[0] if x.dim() == 2 else 1
+    _, _, wsb = qbinlr_sizes(N, K, r, B)
+    if ws is None:
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((B, N), dtype=y_dtype, device=x.device)
+    _check(load().qgemv_binlr(_ptr(ubits), _ptr(vtbits), _ptr(s1), _ptr(s2), N, K, r, _ptr(x),
+                              _dtype_code(x), B, _ptr(y), _dtype_code(y), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "qgemv_binlr")
+    return y
+
+
+# ------------------------------------------------------------------ prefill
+def make_qweight_group(codes, meta, N, K, bits, group) -> qweight:
+    return qweight(Q_FMT_GROUP, N, K, bits, group, codes.data_ptr(), meta.data_ptr(), 0, None, None, None, None)
+
+
+def make_qweight_binlr(ubits, vtbits, s1, s2, N, K, r) -> qweight:
+    return qweight(Q_FMT_BINLR, N, K, 0, 0, None, None, r, ubits.data_ptr(), vtbits.data_ptr(),
+                   s1.data_ptr(), s2.data_ptr())
+
+
+def qgemm_prefill_ws(w: qweight, M: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().qgemm_prefill_ws(ctypes.byref(w), M, ctypes.byref(n)), "qgemm_prefill_ws")
+    return n.value
+
+
+def qgemm_prefill(w: qweight, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, y_dtype=torch.float32, stream=None):
+    _need_cuda(X, Y, ws)
+    M = X.shape[0]
+    need = qgemm_prefill_ws(w, M)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=X.device)
+    if Y is None:
+        Y = torch.empty((M, w.N), dtype=y_dtype, device=X.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().qgemm_prefill(ctypes.byref(w), _ptr(X), _dtype_code(X), M, _ptr(Y), _dtype_code(Y),
+                                _ptr(ws), nbytes, _stream(stream)), "qgemm_prefill")
+    return Y

@@ -1,0 +1,217 @@
+// C ABI of the compressed-weight product (declared in include/qgemv.h):
+// argument validation, size queries, status codes, dispatch to the kernels.
+// Validation runs on the host before any HIP call, so bad arguments are
+// reported without touching the GPU.
+#include "qgemv.h"
+
+#include "launch.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int group_args_ok(int64_t N, int64_t K, int bits, int group) {
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return Q_EINVAL;
+  if (bits < 2 || bits > 6) return Q_EINVAL;
+  if (group != 32 && group != 64) return Q_EINVAL;
+  if (K % group) return Q_EINVAL;
+  if ((N * (K / 32)) > (int64_t)1 << 34) return Q_EUNSUPPORTED;
+  return Q_OK;
+}
+
+int64_t padded_words(int64_t n) { return ((n + 31) / 32 + 3) / 4 * 4; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? Q_OK : Q_EHIP; }
+
+int dtype_ok(int d) { return d == Q_F32 || d == Q_BF16; }
+
+// B = 1 keeps a K-slice of activations in registers; at most 4 slices.
+int64_t gemv_b1_max_k(int x_dtype) { return x_dtype == Q_F32 ? 4 * 64 * 2 * 32 : 4 * 64 * 4 * 32; }
+
+}  // namespace
+
+extern "C" {
+
+int q_abi_version(void) { return Q_ABI_VERSION; }
+int q_format_version(void) { return Q_FORMAT_VERSION; }
+
+const char* q_status_str(int status) {
+  switch (status) {
+    case Q_OK: return "ok";
+    case Q_EINVAL: return "invalid argument";
+    case Q_EALIGN: return "misaligned buffer";
+    case Q_EUNSUPPORTED: return "unsupported parameter combination";
+    case Q_ERANGE: return "data out of range (non-finite weight, fp16 overflow or entry not +-1)";
+    case Q_EWORKSPACE: return "workspace missing or too small";
+    case Q_EHIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int qgroup_sizes(int64_t N, int64_t K, int bits, int group, size_t* codes_bytes,
+                 size_t* meta_bytes) {
+  const int st = group_args_ok(N, K, bits, group);
+  if (st != Q_OK) return st;
+  if (codes_bytes) *codes_bytes = (size_t)(N * K / 8 * bits);
+  if (meta_bytes) *meta_bytes = (size_t)(N * (K / group) * 4);
+  return Q_OK;
+}
+
+int qpack_group(const float* W, int64_t N, int64_t K, int bits, int group, void* codes,
+                void* meta, hipStream_t stream) {
+  const int st = group_args_ok(N, K, bits, group);
+  if (st != Q_OK) return st;
+  if (!W || !codes || !meta) return Q_EINVAL;
+  if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(meta, 16)) return Q_EALIGN;
+  hipError_t e;
+  int* status = qg::pack_status_ptr(&e);
+  if (!status) return Q_EHIP;
+  if ((e = qg::launch_zero_status(status, stream)) != hipSuccess) return Q_EHIP;
+  e = qg::launch_pack_group(W, N, K, bits, group, static_cast<uint32_t*>(codes),
+                            static_cast<uint32_t*>(meta), status, stream);
+  if (e != hipSuccess) return Q_EHIP;
+  int host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return Q_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return Q_EHIP;
+  return host ? Q_ERANGE : Q_OK;
+}
+
+int qunpack_group(const void* codes, const void* meta, int64_t N, int64_t K, int bits,
+                  int group, uint8_t* q_out, float* w_out, hipStream_t stream) {
+  const int st = group_args_ok(N, K, bits, group);
+  if (st != Q_OK) return st;
+  if (!codes || !meta || !q_out) return Q_EINVAL;
+  if (!aligned(codes, 4) || !aligned(meta, 4) || !aligned(q_out, 4) || (w_out && !aligned(w_out, 4)))
+    return Q_EALIGN;
+  return hip_status(qg::launch_unpack_group(static_cast<const uint32_t*>(codes),
+                                            static_cast<const uint32_t*>(meta), N, K, bits,
+                                            group, q_out, w_out, stream));
+}
+
+int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K, int bits, int group,
+                const void* x, int x_dtype, int64_t B, void* y, int y_dtype, hipStream_t stream) {
+  const int st = group_args_ok(N, K, bits, group);
+  if (st != Q_OK) return st;
+  if (!codes || !meta || !x || !y) return Q_EINVAL;
+  if (B < 1 || B > 16) return Q_EINVAL;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return Q_EINVAL;
+  if (!aligned(codes, 16) || !aligned(meta, 16) || !aligned(x, 16) || !aligned(y, 4))
+    return Q_EALIGN;
+  if (B == 1 && K > gemv_b1_max_k(x_dtype)) return Q_EUNSUPPORTED;
+  if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
+  if (N > INT32_MAX || K > INT32_MAX) return Q_EUNSUPPORTED;
+  return hip_status(qg::launch_gemv_group(static_cast<const uint32_t*>(codes),
+                                          static_cast<const uint32_t*>(meta), N, K, bits, group,
+                                          x, x_dtype, B, y, y_dtype, stream));
+}
+
+int qbinlr_sizes(int64_t N, int64_t K, int64_t r, int64_t B, size_t* ubits_bytes,
+                 size_t* vtbits_bytes, size_t* ws_bytes) {
+  if (N < 1 || K < 1 || r < 1 || N > kMaxDim || K > kMaxDim || r > kMaxDim) return Q_EINVAL;
+  if (B < 1 || B > 16) return Q_EINVAL;
+  if (ubits_bytes) *ubits_bytes = (size_t)(N * padded_words(r) * 4);
+  if (vtbits_bytes) *vtbits_bytes = (size_t)(r * padded_words(K) * 4);
+  if (ws_bytes) *ws_bytes = (size_t)(B * padded_words(r) * 32 * 4);
+  return Q_OK;
+}
+
+int qpack_binlr(const int8_t* U, const int8_t* V, int64_t N, int64_t K, int64_t r, void* ubits,
+                void* vtbits, hipStream_t stream) {
+  if (qbinlr_sizes(N, K, r, 1, nullptr, nullptr, nullptr) != Q_OK) return Q_EINVAL;
+  if (!U || !V || !ubits || !vtbits) return Q_EINVAL;
+  if (!aligned(ubits, 16) || !aligned(vtbits, 16)) return Q_EALIGN;
+  hipError_t e;
+  int* status = qg::pack_status_ptr(&e);
+  if (!status) return Q_EHIP;
+  if ((e = qg::launch_zero_status(status, stream)) != hipSuccess) return Q_EHIP;
+  e = qg::launch_pack_binlr(U, V, N, K, r, static_cast<uint32_t*>(ubits),
+                            static_cast<uint32_t*>(vtbits), status, stream);
+  if (e != hipSuccess) return Q_EHIP;
+  int host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return Q_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return Q_EHIP;
+  return host ? Q_ERANGE : Q_OK;
+}
+
+int qunpack_binlr(const void* ubits, const void* vtbits, int64_t N, int64_t K, int64_t r,
+                  int8_t* U_out, int8_t* V_out, hipStream_t stream) {
+  if (qbinlr_sizes(N, K, r, 1, nullptr, nullptr, nullptr) != Q_OK) return Q_EINVAL;
+  if (!ubits || !vtbits || (!U_out && !V_out)) return Q_EINVAL;
+  if (!aligned(ubits, 4) || !aligned(vtbits, 4)) return Q_EALIGN;
+  return hip_status(qg::launch_unpack_binlr(static_cast<const uint32_t*>(ubits),
+                                            static_cast<const uint32_t*>(vtbits), N, K, r,
+                                            U_out, V_out, stream));
+}
+
+int qgemv_binlr(const void* ubits, const void* vtbits, const uint16_t* s1, const uint16_t* s2,
+                int64_t N, int64_t K, int64_t r, const void* x, int x_dtype, int64_t B, void* y,
+                int y_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  size_t need = 0;
+  const int st = qbinlr_sizes(N, K, r, B, nullptr, nullptr, &need);
+  if (st != Q_OK) return st;
+  if (!ubits || !vtbits || !s1 || !s2 || !x || !y) return Q_EINVAL;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return Q_EINVAL;
+  if (!ws || ws_bytes < need) return Q_EWORKSPACE;
+  if (!aligned(ubits, 16) || !aligned(vtbits, 16) || !aligned(ws, 16) || !aligned(x, 4) ||
+      !aligned(y, 4) || !aligned(s1, 2) || !aligned(s2, 2))
+    return Q_EALIGN;
+  // each stage keeps a slice of its input vector in registers: at most
+  // 4 slices x 4 iterations x 64 lanes x 32 entries
+  if (K > 4 * 4 * 64 * 32 || r > 4 * 4 * 64 * 32) return Q_EUNSUPPORTED;
+  return hip_status(qg::launch_gemv_binlr(
+      static_cast<const uint32_t*>(ubits), static_cast<const uint32_t*>(vtbits), s1, s2, N, K, r,
+      x, x_dtype, B, y, y_dtype, static_cast<float*>(ws), stream));
+}
+
+int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes) {
+  if (!w || !ws_bytes || M < 1 || M > kMaxDim) return Q_EINVAL;
+  if (w->format == Q_FMT_GROUP) {
+    const int st = group_args_ok(w->N, w->K, w->bits, w->group);
+    if (st != Q_OK) return st;
+    *ws_bytes = 0;
+    return Q_OK;
+  }
+  if (w->format == Q_FMT_BINLR) {
+    const int st = qbinlr_sizes(w->N, w->K, w->r, 1, nullptr, nullptr, nullptr);
+    if (st != Q_OK) return st;
+    *ws_bytes = (size_t)(M * padded_words(w->r) * 32 * 2);
+    return Q_OK;
+  }
+  return Q_EINVAL;
+}
+
+int qgemm_prefill(const qweight* w, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  size_t need = 0;
+  const int st = qgemm_prefill_ws(w, M, &need);
+  if (st != Q_OK) return st;
+  if (!X || !Y) return Q_EINVAL;
+  if (x_dtype != Q_BF16) return Q_EUNSUPPORTED;
+  if (!dtype_ok(y_dtype)) return Q_EINVAL;
+  if (!aligned(X, 16) || !aligned(Y, 4)) return Q_EALIGN;
+  if (M > INT32_MAX) return Q_EUNSUPPORTED;
+  if (w->format == Q_FMT_GROUP) {
+    if (!w->codes || !w->meta) return Q_EINVAL;
+    if (!aligned(w->codes, 4) || !aligned(w->meta, 4)) return Q_EALIGN;
+    return hip_status(qg::launch_gemm_group(static_cast<const uint32_t*>(w->codes),
+                                            static_cast<const uint32_t*>(w->meta), w->N, w->K,
+                                            w->bits, w->group, static_cast<const uint16_t*>(X),
+                                            M, Y, y_dtype, stream));
+  }
+  if (!w->ubits || !w->vtbits || !w->s1 || !w->s2) return Q_EINVAL;
+  if (w->K % 8) return Q_EUNSUPPORTED;  // 16-byte row loads of X
+  if (!ws || ws_bytes < need) return Q_EWORKSPACE;
+  if (!aligned(ws, 16) || !aligned(w->ubits, 4) || !aligned(w->vtbits, 4)) return Q_EALIGN;
+  return hip_status(qg::launch_gemm_binlr(
+      static_cast<const uint32_t*>(w->ubits), static_cast<const uint32_t*>(w->vtbits), w->s1,
+      w->s2, w->N, w->K, w->r, static_cast<const uint16_t*>(X), M, Y, y_dtype,
+      static_cast<uint16_t*>(ws), stream));
+}
+
+}  // extern "C"

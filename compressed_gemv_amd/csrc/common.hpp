@@ -1,0 +1,126 @@
+// Device helpers shared by the gfx950 kernels: bf16/fp16 bit helpers, wave
+// reductions, and the decode of the packed group-RTN unit.
+//
+// Packed unit (format version 1): 32 codes of b bits in b little-endian u32
+// words.  Each 16-bit half of a word holds F = 16/b fields from bit 0 up; the
+// bits above the fields hold the codes that do not fit (b = 3, 5, 6).  Field
+// j of the low half and field j of the high half of one word form a code
+// pair; a pair becomes one bf16x2 operand with a single shift and a masked
+// OR into 0x4300 (bf16 128.0, whose 7 mantissa bits weigh 1, 2, ..., 64).
+// A b-bit code placed at mantissa bit p reads as 128 + q*2^p, so the
+// matching activation is pre-scaled by 2^-p (exact in bf16) and the bias
+// 128*x*2^-p is removed once per unit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kBias2 = 0x43004300u;  // two bf16 128.0
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---------------------------------------------------------------- unit layout
+// Pair k of a unit (k = 0..15): low-half code ca, high-half code cb and the
+// mantissa bit p the fields land on after decode.
+struct PairInfo { int ca, cb, p; };
+
+template <int B> struct Unit {
+  static constexpr int F = 16 / B;                 // fields per half-word
+  static constexpr int kRegularPairs = F * B;      // F pairs per word, B words
+  // shift that brings field j near bit 0, and its landing bit p
+  static constexpr int shift_of(int j) {
+    return B == 2 ? 6 * (j / 3) : B == 3 ? 6 * (j / 2) : B * j;
+  }
+  static constexpr int p_of(int j) {
+    return B == 2 ? 2 * (j % 3) : B == 3 ? 3 * (j % 2) : 0;
+  }
+  static constexpr PairInfo pair(int k) {
+    if (k < kRegularPairs) {
+      const int w = k / F, j = k % F;
+      return PairInfo{2 * F * w + j, 2 * F * w + F + j, p_of(j)};
+    }
+    if (B == 3 || B == 5) return PairInfo{30, 31, 0};
+    const int pp = k - kRegularPairs;               // B == 6: spare pairs
+    return PairInfo{24 + pp, 28 + pp, 0};
+  }
+};
+
+// Decode one unit (B words) into 16 bf16x2 operands (128 + q*2^p per lane).
+template <int B>
+__device__ __forceinline__ void decode_unit(const uint32_t (&w)[B], uint32_t (&pr)[16]) {
+  using U = Unit<B>;
+#pragma unroll
+  for (int k = 0; k < U::kRegularPairs; ++k) {
+    const int wi = k / U::F, j = k % U::F;
+    const uint32_t m = ((1u << B) - 1u) << U::p_of(j);
+    const uint32_t mask = m | (m << 16);
+    pr[k] = ((w[wi] >> U::shift_of(j)) & mask) | kBias2;
+  }
+  if constexpr (B == 3 || B == 5) {
+    uint32_t t = kBias2;
+#pragma unroll
+    for (int i = 0; i < B; ++i) t |= (w[i] >> (15 - i)) & (0x00010001u << i);
+    pr[15] = t;
+  } else if constexpr (B == 6) {
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      pr[12 + pp] = ((w[pp] >> 12) & 0x000F000Fu) |
+                    ((w[4 + pp / 2] >> (8 + 2 * (pp % 2))) & 0x00300030u) | kBias2;
+    }
+  }
+}
+
+// Codes of one unit as fp32 values q (exact), natural code order.
+template <int B>
+__device__ __forceinline__ void unit_codes_f32(const uint32_t (&w)[B], float (&q)[32]) {
+  uint32_t pr[16];
+  decode_unit<B>(w, pr);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const PairInfo pi = Unit<B>::pair(k);
+    const float inv = 1.0f / (float)(1 << pi.p);
+    q[pi.ca] = (bf16_lo_to_f32(pr[k]) - 128.0f) * inv;
+    q[pi.cb] = (bf16_hi_to_f32(pr[k]) - 128.0f) * inv;
+  }
+}
+
+}  // namespace qg

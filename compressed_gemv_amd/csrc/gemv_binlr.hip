@@ -1,0 +1,188 @@
+// Binary low-rank GEMV, W ~ s1 (.) (U+-1 V+-1^T) (.) s2^T ("70B en 4GB de
+// VRAM...", section 1, NanoQuant formulation), read right to left:
+//   stage 1  t = V^T (s2 (.) x)       rows of VTbits, reduction over K
+//   stage 2  y = s1 (.) (U t)         rows of Ubits,  reduction over r
+// Both stages are one kernel: a +-1 row dotted with a vector v,
+//   sum_k (2 b_k - 1) v_k = 2 * sum_{b_k = 1} v_k - sum_k v_k.
+// A lane owns one 32-bit word (32 signs) per row.  Bit j of the low half and
+// bit j of the high half form a pair; one shift and one masked OR turn a
+// pair into a bf16x2 operand 128 + b*2^p (p = landing mantissa bit), so the
+// matching v is pre-scaled by 2^-p and the bias 128*v*2^-p is removed once
+// per word.  v (s2*x in stage 1, t in stage 2) is fp32 and is carried as
+// bf16 hi + lo halves (two v_dot2 per pair, 2^-16 relative residual).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace qg {
+
+// word layout of a 32-sign word: pair j (0..15) = bits (j, 16+j)
+__device__ __forceinline__ constexpr int bin_shift(int j) { return j < 7 ? 0 : (j < 14 ? 7 : 14); }
+__device__ __forceinline__ constexpr int bin_p(int j) { return j - bin_shift(j); }
+
+// MODE 0: v = s2 * x (x bf16), output t (fp32)
+// MODE 1: v = s2 * x (x fp32), output t (fp32)
+// MODE 2: v = t (fp32), output y = s1 * dot (fp32 or bf16)
+template <int MODE, int UI, int RPW>
+__global__ __launch_bounds__(256) void bin_gemv_kernel(
+    const uint32_t* __restrict__ bits, int R, int Wn, int Lk, const void* __restrict__ vin,
+    const uint16_t* __restrict__ vscale, const uint16_t* __restrict__ oscale,
+    void* __restrict__ out, int y_bf16, int S, int RS, int WSL, int TMAX, int64_t in_bstride,
+    int64_t out_bstride) {
+  extern __shared__ float part[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sl = wave % S, rs = wave / S;
+  const int b = blockIdx.y;
+  const int Wv = (Lk + 31) >> 5;   // words holding real entries
+
+  uint32_t xp[UI][32];
+  float negC[UI], vsum[UI];
+  int widx[UI];
+#pragma unroll
+  for (int it = 0; it < UI; ++it) {
+    const int lw = it * 64 + lane;
+    const int wi = sl * WSL + lw;
+    const bool ok = (lw < WSL) && (wi < Wv);
+    widx[it] = ok ? wi : -1;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.f;
+    if (ok) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int k = wi * 32 + i;
+        if (k < Lk) {
+          float xv;
+          if constexpr (MODE == 0) xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k]);
+          else xv = static_cast<const float*>(vin)[in_bstride * b + k];
+          if constexpr (MODE != 2) xv *= f16_bits_to_f32(vscale[k]);
+          v[i] = xv;
+        }
+      }
+    }
+    float c = 0.f, vs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float sc = 1.0f / (float)(1 << bin_p(j));
+      const float a = v[j] * sc, bb = v[16 + j] * sc;
+      const uint32_t ah = f32_to_bf16_rne(a), bh = f32_to_bf16_rne(bb);
+      const uint32_t al = f32_to_bf16_rne(a - bf16_bits_to_f32(ah));
+      const uint32_t bl = f32_to_bf16_rne(bb - bf16_bits_to_f32(bh));
+      xp[it][2 * j] = ah | (bh << 16);
+      xp[it][2 * j + 1] = al | (bl << 16);
+      c += (bf16_bits_to_f32(ah) + bf16_bits_to_f32(al)) + (bf16_bits_to_f32(bh) + bf16_bits_to_f32(bl));
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) vs += v[i];
+    negC[it] = -128.0f * c;
+    vsum[it] = vs;
+  }
+
+  const int nstreams = gridDim.x * RS;
+  const int stream = blockIdx.x * RS + rs;
+  for (int m0 = 0;; m0 += RPW) {
+    const int row0 = stream + m0 * nstreams;
+    if (row0 >= R) break;
+    uint32_t wv[RPW][UI];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = row0 + r * nstreams;
+#pragma unroll
+      for (int it = 0; it < UI; ++it)
+        wv[r][it] = (row < R && widx[it] >= 0) ? bits[(size_t)row * Wn + widx[it]] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int it = 0; it < UI; ++it) {
+        float a = negC[it];
+        const uint32_t w = wv[r][it];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t m = 0x00010001u << bin_p(j);
+          const uint32_t pr = ((w >> bin_shift(j)) & m) | kBias2;
+          a = dot2_bf16(pr, xp[it][2 * j], a);
+          a = dot2_bf16(pr, xp[it][2 * j + 1], a);
+        }
+        acc += 2.0f * a - vsum[it];
+      }
+      const float total = wave_sum(acc);
+      const int row = row0 + r * nstreams;
+      if (row < R && lane == 0) {
+        if (S == 1) {
+          if constexpr (MODE == 2) {
+            const float yv = total * f16_bits_to_f32(oscale[row]);
+            if (y_bf16) static_cast<uint16_t*>(out)[out_bstride * b + row] = (uint16_t)f32_to_bf16_rne(yv);
+            else static_cast<float*>(out)[out_bstride * b + row] = yv;
+          } else {
+            static_cast<float*>(out)[out_bstride * b + row] = total;
+          }
+        } else {
+          part[((size_t)rs * TMAX + (m0 + r)) * S + sl] = total;
+        }
+      }
+    }
+  }
+  if (S > 1) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < RS * TMAX; idx += blockDim.x) {
+      const int rs_ = idx / TMAX, m = idx % TMAX;
+      const int row = blockIdx.x * RS + rs_ + m * nstreams;
+      if (row < R) {
+        float t = 0.f;
+        for (int j = 0; j < S; ++j) t += part[(size_t)idx * S + j];
+        if constexpr (MODE == 2) {
+          const float yv = t * f16_bits_to_f32(oscale[row]);
+          if (y_bf16) static_cast<uint16_t*>(out)[out_bstride * b + row] = (uint16_t)f32_to_bf16_rne(yv);
+          else static_cast<float*>(out)[out_bstride * b + row] = yv;
+        } else {
+          static_cast<float*>(out)[out_bstride * b + row] = t;
+        }
+      }
+    }
+  }
+}
+
+template <int MODE>
+static hipError_t bin_gemv_t(const uint32_t* bits, int64_t R, int64_t Wn, int64_t Lk,
+                             const void* vin, const uint16_t* vscale, const uint16_t* oscale,
+                             void* out, int y_bf16, int64_t B, int64_t in_bstride,
+                             int64_t out_bstride, hipStream_t s) {
+  constexpr int UI = 4, RPW = 2;
+  const int Wv = (int)((Lk + 31) / 32);
+  const int S = (Wv + 64 * UI - 1) / (64 * UI);
+  if (S > 4) return hipErrorInvalidValue;
+  const int RS = 4 / S;
+  const int WSL = (Wv + S - 1) / S;
+  const int threads = 64 * S * RS;
+  const int64_t streams_wanted = (R + 7) / 8;
+  int64_t blocks = (streams_wanted + RS - 1) / RS;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 2048) blocks = 2048;
+  const int64_t nstreams = blocks * RS;
+  const int TMAX = (int)((R + nstreams - 1) / nstreams);
+  const size_t lds = S > 1 ? (size_t)RS * TMAX * S * sizeof(float) : 0;
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bin_gemv_kernel<MODE, UI, RPW>), dim3((unsigned)blocks, (unsigned)B),
+                     dim3(threads), lds, s, bits, (int)R, (int)Wn, (int)Lk, vin, vscale, oscale,
+                     out, y_bf16, S, RS, WSL, TMAX, in_bstride, out_bstride);
+  return hipGetLastError();
+}
+
+static int64_t pw(int64_t n) { return ((n + 31) / 32 + 3) / 4 * 4; }
+
+hipError_t launch_gemv_binlr(const uint32_t* ubits, const uint32_t* vtbits,
+                             const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
+                             int64_t r, const void* x, int x_dtype, int64_t B, void* y,
+                             int y_dtype, float* t_ws, hipStream_t s) {
+  const int64_t rp = pw(r) * 32;   // workspace row stride of t
+  hipError_t e;
+  if (x_dtype == 1)
+    e = bin_gemv_t<0>(vtbits, r, pw(K), K, x, s2, nullptr, t_ws, 0, B, K, rp, s);
+  else
+    e = bin_gemv_t<1>(vtbits, r, pw(K), K, x, s2, nullptr, t_ws, 0, B, K, rp, s);
+  if (e != hipSuccess) return e;
+  return bin_gemv_t<2>(ubits, N, pw(r), r, t_ws, nullptr, s1, y, y_dtype == 1, B, rp, N, s);
+}
+
+}  // namespace qg

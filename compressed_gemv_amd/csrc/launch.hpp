@@ -1,0 +1,42 @@
+// Internal launchers (C++ linkage) called by the C ABI layer after argument
+// validation.  Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+// status word shared by the packers (per device)
+int* pack_status_ptr(hipError_t* err);
+
+hipError_t launch_pack_group(const float* W, int64_t N, int64_t K, int bits, int group,
+                             uint32_t* codes, uint32_t* meta, int* status, hipStream_t s);
+hipError_t launch_unpack_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
+                               int64_t K, int bits, int group, uint8_t* q, float* w,
+                               hipStream_t s);
+hipError_t launch_pack_binlr(const int8_t* U, const int8_t* V, int64_t N, int64_t K,
+                             int64_t r, uint32_t* ubits, uint32_t* vtbits, int* status,
+                             hipStream_t s);
+hipError_t launch_unpack_binlr(const uint32_t* ubits, const uint32_t* vtbits, int64_t N,
+                               int64_t K, int64_t r, int8_t* U, int8_t* V, hipStream_t s);
+hipError_t launch_zero_status(int* status, hipStream_t s);
+
+hipError_t launch_gemv_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
+                             int64_t K, int bits, int group, const void* x, int x_dtype,
+                             int64_t B, void* y, int y_dtype, hipStream_t s);
+
+hipError_t launch_gemv_binlr(const uint32_t* ubits, const uint32_t* vtbits,
+                             const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
+                             int64_t r, const void* x, int x_dtype, int64_t B, void* y,
+                             int y_dtype, float* t_ws, hipStream_t s);
+
+hipError_t launch_gemm_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
+                             int64_t K, int bits, int group, const uint16_t* X, int64_t M,
+                             void* Y, int y_dtype, hipStream_t s);
+hipError_t launch_gemm_binlr(const uint32_t* ubits, const uint32_t* vtbits,
+                             const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
+                             int64_t r, const uint16_t* X, int64_t M, void* Y, int y_dtype,
+                             uint16_t* T_ws, hipStream_t s);
+
+}  // namespace qg

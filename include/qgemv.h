@@ -1,0 +1,173 @@
+/*
+ * qgemv.h - C ABI of the MI355X (gfx950) compressed-weight matrix product.
+ *
+ * Two weight formats:
+ *   group RTN   b-bit codes (b = 2..6) in groups of g = 32 or 64 consecutive
+ *               inputs, each group with an fp16 scale s and an fp16 offset o,
+ *               w_hat = s*q + o.  Group-wise asymmetric round-to-nearest
+ *               ("Métodos de cuantización de LLM para ejecutar un modelo de
+ *               70B en una sola GPU", RTN paragraph; "TurboQuant: cuantizar
+ *               modelos grandes para que quepan en local", "Compresión por
+ *               bloques" and "Asignación de bits por capa").
+ *   binary LR   W ~ s1 (.) (U+-1 . V+-1^T) (.) s2^T, U: N x r, V: K x r,
+ *               s1 (N) and s2 (K) fp16 channel scales ("70B en 4GB de VRAM:
+ *               la compresión neural de 2026, ¿es real?", section 1,
+ *               NanoQuant, formulation bullet).
+ *
+ * Shapes: W has N outputs and K inputs and is stored output-major (the
+ * reduction dimension K is contiguous).  Activations x/X are [B][K] or
+ * [M][K] row-major; outputs y/Y are [B][N] or [M][N] row-major.
+ *
+ * Ownership: every data pointer is a DEVICE pointer owned by the caller.
+ * The library never allocates or frees device memory.  Entry points that
+ * need scratch take a caller-provided workspace whose size comes from the
+ * matching *_sizes / *_ws query (host-only functions).
+ *
+ * Streams: compute calls are asynchronous on the caller's stream.  qpack_*
+ * synchronize the stream to report data errors.  Device faults surface at
+ * the caller's next synchronization.
+ *
+ * Errors: every entry point returns Q_OK (0) or a negative status; nothing
+ * is launched when argument validation fails.  Launch failures are returned
+ * as Q_EHIP.  No exception crosses the ABI.  Calls are reentrant, except
+ * that qpack_* calls on one device share a device status word and must not
+ * run concurrently with each other.
+ *
+ * Packed layout (format version 1):
+ *   codes  row n is K/32 units of 32 codes; a unit is b little-endian u32
+ *          words.  Each 16-bit half of a word holds floor(16/b) b-bit fields
+ *          from bit 0 up; regular code c of a unit sits in word c/(2F), half
+ *          (c%(2F))/F, field c%F (F = floor(16/b)).  The spare bits above
+ *          the fields hold the remaining codes (b = 3, 5: codes 30, 31 with
+ *          bit i in word i, bit 15 / bit 31; b = 6: codes 24..31, c = 24+4h+p,
+ *          low 4 bits in word p bits 16h+12.., top 2 bits in word 4+p/2 bits
+ *          16h+12+2(p%2)..).  N*K*b/8 bytes, no padding.
+ *   meta   [N][K/g] u32: bits 0..15 fp16 scale s, bits 16..31 fp16 offset o.
+ *   Ubits  [N][rw] u32, U[n][l] = +1 <-> bit (l%32) of word l/32 set.
+ *   VTbits [r][Kw] u32, V[k][l] = +1 <-> bit (k%32) of word k/32 of row l.
+ *          rw = ceil(r/32), Kw = ceil(K/32), each rounded up to a multiple of
+ *          4 words; padding bits are 0 and contribute nothing.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  Q_OK = 0,
+  Q_EINVAL = -1,        /* bad shape, null pointer, unsupported parameter value */
+  Q_EALIGN = -2,        /* a buffer is not aligned as required below */
+  Q_EUNSUPPORTED = -3,  /* valid but not implemented (dtype, size limit) */
+  Q_ERANGE = -4,        /* data error: non-finite weight, fp16 overflow, entry not +-1 */
+  Q_EWORKSPACE = -5,    /* workspace missing or smaller than the query said */
+  Q_EHIP = -6           /* a HIP runtime call or kernel launch failed */
+};
+enum { Q_F32 = 0, Q_BF16 = 1, Q_F16 = 2 };
+enum { Q_FMT_GROUP = 1, Q_FMT_BINLR = 2 };
+
+#define Q_ABI_VERSION 1
+#define Q_FORMAT_VERSION 1
+
+int q_abi_version(void);
+/* Format version of the packed buffers this library reads and writes. */
+int q_format_version(void);
+/* Static string for a status code; never NULL. */
+const char* q_status_str(int status);
+
+/* ---------------------------------------------------------------- group RTN
+ * Byte sizes of the codes and meta buffers (host only, no GPU needed).
+ * Requires N >= 1, K >= 1, K % group == 0, bits in 2..6, group in {32, 64}.
+ */
+int qgroup_sizes(int64_t N, int64_t K, int bits, int group,
+                 size_t* codes_bytes, size_t* meta_bytes);
+
+/* Quantize and pack W[N][K] (fp32, device) with group-wise RTN
+ * ("Métodos de cuantización...", RTN paragraph; "TurboQuant...",
+ * "Compresión por bloques"): per group o = largest fp16 <= min, s = smallest
+ * fp16 >= (max - o)/(2^b - 1) (fp64), q = rint((w - o)/s) in fp64, ties to
+ * even.  codes and meta must be 16-byte aligned and sized by qgroup_sizes.
+ * Synchronizes `stream`; returns Q_ERANGE (buffers then undefined) if a
+ * weight is non-finite or a constant leaves the fp16 range. */
+int qpack_group(const float* W, int64_t N, int64_t K, int bits, int group,
+                void* codes, void* meta, hipStream_t stream);
+
+/* Inverse of the packing, for tests: q_out[N][K] (uint8 codes, required)
+ * and, when w_out is not NULL, w_out[N][K] = s*q + o in fp32. Asynchronous. */
+int qunpack_group(const void* codes, const void* meta, int64_t N, int64_t K,
+                  int bits, int group, uint8_t* q_out, float* w_out,
+                  hipStream_t stream);
+
+/* Decode GEMV: y[b][n] = sum_k (s*q[n][k] + o) * x[b][k] for b < B
+ * ("AirLLM corre un modelo 70B...", "Por qué es lento": a decode step moves
+ * every weight byte once, so it is bound by the bytes read).
+ * x: [B][K], x_dtype Q_BF16 or Q_F32; y: [B][N], y_dtype Q_F32 or Q_BF16;
+ * accumulation in fp32.  1 <= B <= 16.  codes/meta 16-byte aligned, x and y
+ * 4-byte aligned (x bf16: 2-byte aligned when K is odd is not possible since
+ * K % 32 == 0).  Asynchronous on `stream`. */
+int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K,
+                int bits, int group, const void* x, int x_dtype, int64_t B,
+                void* y, int y_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------- binary LR
+ * Sizes of Ubits, VTbits and of the qgemv_binlr workspace for batch B
+ * (host only).  r >= 1, N >= 1, K >= 1, 1 <= B <= 16. */
+int qbinlr_sizes(int64_t N, int64_t K, int64_t r, int64_t B,
+                 size_t* ubits_bytes, size_t* vtbits_bytes, size_t* ws_bytes);
+
+/* Pack +-1 factors ("70B en 4GB de VRAM...", section 1, formulation):
+ * U[N][r] and V[K][r] int8 (device) -> Ubits[N][rw], VTbits[r][Kw].
+ * Synchronizes `stream`; Q_ERANGE if an entry is not +1 or -1. */
+int qpack_binlr(const int8_t* U, const int8_t* V, int64_t N, int64_t K,
+                int64_t r, void* ubits, void* vtbits, hipStream_t stream);
+
+/* Inverse of qpack_binlr, for tests.  Asynchronous. */
+int qunpack_binlr(const void* ubits, const void* vtbits, int64_t N, int64_t K,
+                  int64_t r, int8_t* U_out, int8_t* V_out, hipStream_t stream);
+
+/* Binary GEMV in two stages ("70B en 4GB de VRAM...", section 1: the
+ * factored form read right to left): t[b] = V^T (s2 (.) x[b]) into the
+ * workspace (fp32), then y[b] = s1 (.) (U t[b]).  s1, s2: fp16 bits (device).
+ * x_dtype Q_BF16 or Q_F32, y_dtype Q_F32 or Q_BF16, 1 <= B <= 16.
+ * ws: device, ws_bytes >= the qbinlr_sizes value, 16-byte aligned. */
+int qgemv_binlr(const void* ubits, const void* vtbits, const uint16_t* s1,
+                const uint16_t* s2, int64_t N, int64_t K, int64_t r,
+                const void* x, int x_dtype, int64_t B, void* y, int y_dtype,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------- prefill */
+typedef struct qweight {
+  int format;                 /* Q_FMT_GROUP or Q_FMT_BINLR */
+  int64_t N, K;
+  int bits, group;            /* Q_FMT_GROUP */
+  const void* codes;
+  const void* meta;
+  int64_t r;                  /* Q_FMT_BINLR */
+  const void* ubits;
+  const void* vtbits;
+  const uint16_t* s1;
+  const uint16_t* s2;
+} qweight;
+
+/* Workspace bytes qgemm_prefill needs for M token rows (host only). */
+int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes);
+
+/* Prefill GEMM Y[M][N] = X[M][K] W_hat^T with X bf16 (x_dtype Q_BF16).
+ * Weight tiles are decoded to bf16 in LDS and fed to MFMA with fp32
+ * accumulation.  Group RTN: one pass.  Binary: T = (X (.) s2) V into the
+ * workspace as bf16, then Y = (T U^T) (.) s1 ("70B en 4GB de VRAM...",
+ * section 1; the pages' GEMM kernels for this format).  y_dtype Q_F32 or
+ * Q_BF16.  Asynchronous. */
+int qgemm_prefill(const qweight* w, const void* X, int x_dtype, int64_t M,
+                  void* Y, int y_dtype, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMV_H */

@@ -1,0 +1,45 @@
+"""Helpers shared by the GPU parity tests (inputs go to the device; expected
+values always come from the CPU oracle)."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+TOL = 2e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return oracle.product.bf16_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy()
+
+
+def group_reference(W, bits, group):
+    """Oracle codes/meta words and W_hat for fp32 W."""
+    q, s, o = oracle.rtn.quantize(W, bits, group)
+    words = oracle.fmt.pack_codes(q, bits)
+    meta = oracle.fmt.pack_meta(s, o)
+    return q, s, o, words, meta, oracle.rtn.dequantize(q, s, o, group)
+
+
+def check_err(y, y_ref, D, tol=TOL):
+    err = oracle.product.normalized_error(y, y_ref, D)
+    assert err <= tol, f"normalized error {err:.3e} > {tol}"
+    return err

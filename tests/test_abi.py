@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every entry point include/qgemv.h
+declares, answers the host-only size queries and rejects bad arguments with
+the documented status codes before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_gemv_amd as cg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qgemv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cg.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return cg.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 13, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_versions_and_status_strings(lib):
+    assert cg.q_abi_version() == 1
+    assert cg.q_format_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        s = cg.q_status_str(st)
+        assert s and s != "unknown status"
+    assert cg.q_status_str(-99) == "unknown status"
+
+
+def test_size_queries(lib):
+    assert cg.qgroup_sizes(28672, 8192, 4, 64) == (117_440_512, 14_680_064)
+    assert cg.qgroup_sizes(512, 512, 4, 32) == (131_072, 32_768)
+    for b in (2, 3, 5, 6):
+        c, m = cg.qgroup_sizes(8192, 8192, b, 32)
+        assert c == 8192 * 8192 * b // 8 and m == 8192 * 256 * 4
+    ub, vb, ws = cg.qbinlr_sizes(28672, 8192, 4096, 1)
+    assert ub == 14_680_064 and vb == 4_194_304 and ws == 4096 * 4
+    ub, vb, ws = cg.qbinlr_sizes(10, 40, 3, 2)   # padding to 4-word rows
+    assert ub == 10 * 16 and vb == 3 * 16 and ws == 2 * 128 * 4
+    w = cg.qweight(cg.Q_FMT_BINLR, 28672, 8192, 0, 0, None, None, 4096, None, None, None, None)
+    assert cg.qgemm_prefill_ws(w, 512) == 512 * 4096 * 2
+    w = cg.qweight(cg.Q_FMT_GROUP, 28672, 8192, 4, 64, None, None, 0, None, None, None, None)
+    assert cg.qgemm_prefill_ws(w, 512) == 0
+
+
+@pytest.mark.parametrize("args", [
+    (100, 100, 4, 32),      # K not a multiple of the group
+    (100, 128, 7, 32),      # bits out of range
+    (100, 128, 4, 48),      # group not 32/64
+    (0, 128, 4, 32),        # empty
+])
+def test_size_query_rejects(lib, args):
+    c, m = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.qgroup_sizes(*args, ctypes.byref(c), ctypes.byref(m)) == cg.Q_EINVAL
+
+
+def test_entry_points_validate_before_touching_the_gpu(lib):
+    P = ctypes.c_void_p
+    good, odd = P(0x10000), P(0x10004)
+    s = P(0)
+    # null pointers
+    assert lib.qgemv_group(P(0), good, 64, 128, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EINVAL
+    # batch out of range
+    assert lib.qgemv_group(good, good, 64, 128, 4, 32, good, cg.Q_BF16, 17, good, cg.Q_F32, s) == cg.Q_EINVAL
+    # misaligned codes
+    assert lib.qgemv_group(odd, good, 64, 128, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EALIGN
+    # unsupported: fp32 activations with B > 1, K beyond the register-resident limit
+    assert lib.qgemv_group(good, good, 64, 128, 4, 32, good, cg.Q_F32, 2, good, cg.Q_F32, s) == cg.Q_EUNSUPPORTED
+    assert lib.qgemv_group(good, good, 64, 65536, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EUNSUPPORTED
+    # bad dtype
+    assert lib.qgemv_group(good, good, 64, 128, 4, 32, good, 7, 1, good, cg.Q_F32, s) == cg.Q_EINVAL
+    # packer: bad shape, alignment
+    assert lib.qpack_group(good, 64, 100, 4, 32, good, good, s) == cg.Q_EINVAL
+    assert lib.qpack_group(good, 64, 128, 4, 32, odd, good, s) == cg.Q_EALIGN
+    # binary: workspace too small
+    assert lib.qgemv_binlr(good, good, good, good, 64, 128, 16, good, cg.Q_BF16, 1, good, cg.Q_F32,
+                           good, 4, s) == cg.Q_EWORKSPACE
+    assert lib.qgemv_binlr(good, good, good, good, 64, 128, 16, good, cg.Q_BF16, 1, good, cg.Q_F32,
+                           P(0), 1 << 20, s) == cg.Q_EWORKSPACE
+    assert lib.qpack_binlr(good, good, 64, 128, 0, good, good, s) == cg.Q_EINVAL
+    # prefill
+    w = cg.qweight(cg.Q_FMT_GROUP, 64, 128, 4, 32, 0x10000, 0x10000, 0, None, None, None, None)
+    assert lib.qgemm_prefill(ctypes.byref(w), good, cg.Q_F32, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EUNSUPPORTED
+    w.format = 9
+    assert lib.qgemm_prefill(ctypes.byref(w), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
+    wb = cg.qweight(cg.Q_FMT_BINLR, 64, 128, 0, 0, None, None, 16, 0x10000, 0x10000, 0x10000, 0x10000)
+    assert lib.qgemm_prefill(ctypes.byref(wb), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EWORKSPACE

@@ -1,0 +1,100 @@
+"""GPU parity of the prefill GEMM (both formats) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, check_err, dev, dev_bf16, group_reference, host, say
+from workloads import binlr_factors, gen_binlr, gen_weights, gen_x_bf16, layer_weights, layer_x, rng_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("bits,group", [(4, 64), (4, 32), (2, 32), (3, 32), (5, 64), (6, 32)])
+def test_rtn_small(gpu, bits, group):
+    M, N, K = 40, 200, 384
+    W = gen_weights(N, K, rng_for(70, bits * 100 + group), outliers=True)
+    _, _, _, words, meta, W_hat = group_reference(W, bits, group)
+    X = gen_x_bf16(M, K, rng_for(71, bits))
+    w = gpu.make_qweight_group(cd := dev(words.view(np.uint8).reshape(-1)), md := dev(meta.view(np.int32).reshape(-1)),
+                               N, K, bits, group)
+    Y = host(gpu.qgemm_prefill(w, dev_bf16(X)))
+    Xv = oracle.product.bf16_to_f64(X)
+    check_err(Y, oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv))
+    # each prefill row equals the GEMV of that row within the bound
+    y8 = host(gpu.qgemv_group(cd, md, N, K, bits, group, dev_bf16(X[:8])))
+    check_err(Y[:8], y8.astype(np.float64), oracle.product.abs_denominator(W_hat, Xv[:8]))
+
+
+def test_rtn_integer_exact(gpu):
+    rng = np.random.default_rng(72)
+    M, N, K, g = 130, 140, 256, 32
+    W = rng.integers(0, 16, size=(N, K)).astype(np.float32)
+    W[:, ::g] = 0
+    W[:, 1::g] = 15
+    codes, meta = gpu.qpack_group(dev(W), 4, g)
+    Xi = rng.integers(-3, 4, size=(M, K)).astype(np.float32)
+    Xb = (Xi.view(np.uint32) >> 16).astype(np.uint16)
+    Y = host(gpu.qgemm_prefill(gpu.make_qweight_group(codes, meta, N, K, 4, g), dev_bf16(Xb)))
+    assert np.array_equal(Y, (Xi.astype(np.int64) @ W.astype(np.int64).T).astype(np.float64))
+
+
+@pytest.mark.parametrize("M,N,K,r", [(40, 200, 136, 45), (130, 70, 256, 300)])
+def test_binlr_small(gpu, M, N, K, r):
+    U, V, s1, s2 = gen_binlr(N, K, r, rng_for(73, M + r))
+    W = oracle.binlr.reconstruct(U, V, s1, s2)
+    ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
+    X = gen_x_bf16(M, K, rng_for(74, M))
+    s1d, s2d = dev(s1.view(np.int16)), dev(s2.view(np.int16))
+    Y = host(gpu.qgemm_prefill(gpu.make_qweight_binlr(ubd, vbd, s1d, s2d, N, K, r), dev_bf16(X)))
+    Xv = oracle.product.bf16_to_f64(X)
+    check_err(Y, oracle.product.matmul_ref(W, Xv), oracle.product.abs_denominator(W, Xv))
+
+
+def test_binlr_integer_exact(gpu):
+    """s1 = s2 = 1, X in {-1, 0, 1}, small K so every T entry is bf16-exact."""
+    rng = np.random.default_rng(75)
+    M, N, K, r = 64, 96, 128, 40
+    U, V, _, _ = gen_binlr(N, K, r, rng)
+    one = dev(np.full(max(N, K), 0x3C00, np.uint16).view(np.int16))
+    ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
+    Xi = rng.integers(-1, 2, size=(M, K)).astype(np.float32)
+    Xb = (Xi.view(np.uint32) >> 16).astype(np.uint16)
+    Y = host(gpu.qgemm_prefill(gpu.make_qweight_binlr(ubd, vbd, one, one, N, K, r), dev_bf16(Xb)))
+    C = oracle.binlr.sign_product(U, V)
+    assert np.array_equal(Y, (Xi.astype(np.int64) @ C.T).astype(np.float64))
+
+
+@pytest.mark.parametrize("M", [512])
+def test_full_rtn(gpu, M):
+    say(f"prefill full RTN M={M}")
+    W = layer_weights("gate")
+    N, K = W.shape
+    codes, meta = gpu.qpack_group(dev(W), 4, 64)
+    X = layer_x(K, M, config=5)
+    Y = gpu.qgemm_prefill(gpu.make_qweight_group(codes, meta, N, K, 4, 64), dev_bf16(X))
+    rows = np.random.default_rng(5).choice(M, 12, replace=False)
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(6).choice(N, 60, replace=False)]))
+    Ys = host(Y)[np.ix_(rows, cols)]
+    _, _, _, _, _, W_hat = group_reference(W[cols], 4, 64)
+    Xv = oracle.product.bf16_to_f64(X[rows])
+    err = check_err(Ys, oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv))
+    say(f"  err={err:.3e}")
+
+
+def test_full_binlr(gpu):
+    K, N, r = 8192, 28672, 4096
+    say("prefill full binary M=512")
+    U, V, s1, s2 = binlr_factors(K, N, r)
+    ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
+    M = 512
+    X = layer_x(K, M, config=5)
+    Y = gpu.qgemm_prefill(gpu.make_qweight_binlr(ubd, vbd, dev(s1.view(np.int16)), dev(s2.view(np.int16)), N, K, r),
+                          dev_bf16(X))
+    rows = np.random.default_rng(7).choice(M, 8, replace=False)
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(8).choice(N, 40, replace=False)]))
+    Ys = host(Y)[np.ix_(rows, cols)]
+    W = oracle.binlr.reconstruct(U[cols], V, s1[cols], s2)
+    Xv = oracle.product.bf16_to_f64(X[rows])
+    err = check_err(Ys, oracle.product.matmul_ref(W, Xv), oracle.product.abs_denominator(W, Xv))
+    say(f"  err={err:.3e}")
