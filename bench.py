@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ["compressed_gemv_amd/csrc/gemv_group.hip", "compressed_gemv_amd/csrc/common.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_b1_gate_8192x28672_4b_g64_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_b1_gate_8192x28672_4b_g64.md")
 
 
 def kernel_source_sha() -> str:
@@ -325,23 +325,25 @@ def cpu_baseline(np, W, bits, group, log):
         threads = 1
     N, K = W.shape
     x = oracle.product.bf16_to_f64(layer_x(K, 1))
-    R = 512
     per_row = K * bits // 8 + (K // group) * 4
-    best = None
-    while True:
+
+    def timed(R):
         sub = W[:R]
-        q, s, o = oracle.rtn.quantize(sub, bits, group)
+        q, s, o = oracle.rtn.quantize(sub, bits, group)       # offline: not timed
         words = oracle.fmt.pack_codes(q, bits)
         meta = oracle.fmt.pack_meta(s, o)
         t0 = time.perf_counter()
         W_hat = oracle.product.what_group(words, meta, R, K, bits, group)
         _ = oracle.product.matmul_ref(W_hat, x)
-        dt = time.perf_counter() - t0
-        best = (R, dt)
-        log(f"cpu oracle: {R} rows in {dt:.2f} s")
-        if dt >= 8.0 or R >= N:
-            break
-        R = min(N, R * 2)
+        return time.perf_counter() - t0
+
+    # probe a small sample, then size the measured sample to ~10 s of work
+    R0 = min(N, 1024)
+    t0 = timed(R0)
+    R = int(min(N, max(R0, R0 * 10.0 / max(t0, 1e-3))))
+    dt = timed(R) if R != R0 else t0
+    log(f"cpu oracle: {R} rows in {dt:.2f} s")
+    best = (R, dt)
     R, dt = best
     return {
         "value": round(R * per_row / dt / 1e9, 4),

@@ -29,8 +29,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? Q_OK : Q_EHIP; }
 
 int dtype_ok(int d) { return d == Q_F32 || d == Q_BF16; }
 
-// B = 1 keeps a K-slice of activations in registers; at most 4 slices.
-int64_t gemv_b1_max_k(int x_dtype) { return x_dtype == Q_F32 ? 4 * 64 * 2 * 32 : 4 * 64 * 4 * 32; }
+// B = 1 keeps a K-slice of activations in registers; at most 8 slices of
+// 64 lanes x UI units x 32 inputs.
+#ifndef QG_B1_UI
+#define QG_B1_UI 2
+#endif
+int64_t gemv_b1_max_k(int x_dtype) { return x_dtype == Q_F32 ? 8 * 64 * 2 * 32 : 8 * 64 * QG_B1_UI * 32; }
 
 }  // namespace
 
@@ -162,8 +166,8 @@ int qgemv_binlr(const void* ubits, const void* vtbits, const uint16_t* s1, const
       !aligned(y, 4) || !aligned(s1, 2) || !aligned(s2, 2))
     return Q_EALIGN;
   // each stage keeps a slice of its input vector in registers: at most
-  // 4 slices x 4 iterations x 64 lanes x 32 entries
-  if (K > 4 * 4 * 64 * 32 || r > 4 * 4 * 64 * 32) return Q_EUNSUPPORTED;
+  // 8 slices x 2 words x 64 lanes x 32 entries
+  if (K > 8 * 2 * 64 * 32 || r > 8 * 2 * 64 * 32) return Q_EUNSUPPORTED;
   return hip_status(qg::launch_gemv_binlr(
       static_cast<const uint32_t*>(ubits), static_cast<const uint32_t*>(vtbits), s1, s2, N, K, r,
       x, x_dtype, B, y, y_dtype, static_cast<float*>(ws), stream));

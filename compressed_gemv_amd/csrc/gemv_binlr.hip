@@ -13,6 +13,10 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#ifndef QG_BIN_RPW
+#define QG_BIN_RPW 8   // rows per pipeline stage (each row is one 4-byte word per lane)
+#endif
+
 namespace qg {
 
 // word layout of a 32-sign word: pair j (0..15) = bits (j, 16+j)
@@ -23,39 +27,88 @@ __device__ __forceinline__ constexpr int bin_p(int j) { return j - bin_shift(j);
 // MODE 1: v = s2 * x (x fp32), output t (fp32)
 // MODE 2: v = t (fp32), output y = s1 * dot (fp32 or bf16)
 template <int MODE, int UI, int RPW>
-__global__ __launch_bounds__(256) void bin_gemv_kernel(
+__global__ __launch_bounds__(512) void bin_gemv_kernel(
     const uint32_t* __restrict__ bits, int R, int Wn, int Lk, const void* __restrict__ vin,
     const uint16_t* __restrict__ vscale, const uint16_t* __restrict__ oscale,
     void* __restrict__ out, int y_bf16, int S, int RS, int WSL, int TMAX, int64_t in_bstride,
-    int64_t out_bstride) {
+    int64_t out_bstride, int vec_ok) {
   extern __shared__ float part[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sl = wave % S, rs = wave / S;
   const int b = blockIdx.y;
   const int Wv = (Lk + 31) >> 5;   // words holding real entries
 
-  uint32_t xp[UI][32];
-  float negC[UI], vsum[UI];
   int widx[UI];
 #pragma unroll
   for (int it = 0; it < UI; ++it) {
     const int lw = it * 64 + lane;
     const int wi = sl * WSL + lw;
-    const bool ok = (lw < WSL) && (wi < Wv);
-    widx[it] = ok ? wi : -1;
+    widx[it] = ((lw < WSL) && (wi < Wv)) ? wi : -1;
+  }
+  const int nstreams = gridDim.x * RS;
+  const int stream = blockIdx.x * RS + rs;
+  uint32_t wa[RPW][UI], wb[RPW][UI];
+  auto load = [&](uint32_t (&w)[RPW][UI], int row0) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = row0 + r * nstreams;
+#pragma unroll
+      for (int it = 0; it < UI; ++it)
+        w[r][it] = (row < R && widx[it] >= 0) ? __builtin_nontemporal_load(bits + (size_t)row * Wn + widx[it]) : 0u;
+    }
+  };
+  if (stream < R) load(wa, stream);
+
+  uint32_t xp[UI][32];
+  float negC[UI], vsum[UI];
+#pragma unroll
+  for (int it = 0; it < UI; ++it) {
     float v[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = 0.f;
-    if (ok) {
+    const int wi = widx[it];
+    if (wi >= 0) {
+      const int k0 = wi * 32;
+      if (vec_ok && k0 + 32 <= Lk) {
+        if constexpr (MODE == 0) {
+          const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(vin) + in_bstride * b + k0);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int k = wi * 32 + i;
-        if (k < Lk) {
-          float xv;
-          if constexpr (MODE == 0) xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k]);
-          else xv = static_cast<const float*>(vin)[in_bstride * b + k];
-          if constexpr (MODE != 2) xv *= f16_bits_to_f32(vscale[k]);
-          v[i] = xv;
+          for (int i = 0; i < 4; ++i) {
+            const u32x4_t t = src[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { v[8 * i + 2 * j] = bf16_lo_to_f32(t[j]); v[8 * i + 2 * j + 1] = bf16_hi_to_f32(t[j]); }
+          }
+        } else {
+          const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(vin) + in_bstride * b + k0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float4 t = src[i];
+            v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+          }
+        }
+        if constexpr (MODE != 2) {
+          const u32x4_t* sp = reinterpret_cast<const u32x4_t*>(vscale + k0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const u32x4_t t = sp[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              v[8 * i + 2 * j] *= f16_bits_to_f32(t[j] & 0xFFFFu);
+              v[8 * i + 2 * j + 1] *= f16_bits_to_f32(t[j] >> 16);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int k = k0 + i;
+          if (k < Lk) {
+            float xv;
+            if constexpr (MODE == 0) xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k]);
+            else xv = static_cast<const float*>(vin)[in_bstride * b + k];
+            if constexpr (MODE != 2) xv *= f16_bits_to_f32(vscale[k]);
+            v[i] = xv;
+          }
         }
       }
     }
@@ -77,30 +130,27 @@ __global__ __launch_bounds__(256) void bin_gemv_kernel(
     vsum[it] = vs;
   }
 
-  const int nstreams = gridDim.x * RS;
-  const int stream = blockIdx.x * RS + rs;
-  for (int m0 = 0;; m0 += RPW) {
-    const int row0 = stream + m0 * nstreams;
-    if (row0 >= R) break;
-    uint32_t wv[RPW][UI];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int row = row0 + r * nstreams;
-#pragma unroll
-      for (int it = 0; it < UI; ++it)
-        wv[r][it] = (row < R && widx[it] >= 0) ? bits[(size_t)row * Wn + widx[it]] : 0u;
+  auto emit = [&](int row, float total) {
+    if constexpr (MODE == 2) {
+      const float yv = total * f16_bits_to_f32(oscale[row]);
+      if (y_bf16) static_cast<uint16_t*>(out)[out_bstride * b + row] = (uint16_t)f32_to_bf16_rne(yv);
+      else static_cast<float*>(out)[out_bstride * b + row] = yv;
+    } else {
+      static_cast<float*>(out)[out_bstride * b + row] = total;
     }
+  };
+  auto compute = [&](const uint32_t (&w)[RPW][UI], int row0, int m0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       float acc = 0.f;
 #pragma unroll
       for (int it = 0; it < UI; ++it) {
         float a = negC[it];
-        const uint32_t w = wv[r][it];
+        const uint32_t ww = w[r][it];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const uint32_t m = 0x00010001u << bin_p(j);
-          const uint32_t pr = ((w >> bin_shift(j)) & m) | kBias2;
+          const uint32_t pr = ((ww >> bin_shift(j)) & m) | kBias2;
           a = dot2_bf16(pr, xp[it][2 * j], a);
           a = dot2_bf16(pr, xp[it][2 * j + 1], a);
         }
@@ -109,19 +159,24 @@ __global__ __launch_bounds__(256) void bin_gemv_kernel(
       const float total = wave_sum(acc);
       const int row = row0 + r * nstreams;
       if (row < R && lane == 0) {
-        if (S == 1) {
-          if constexpr (MODE == 2) {
-            const float yv = total * f16_bits_to_f32(oscale[row]);
-            if (y_bf16) static_cast<uint16_t*>(out)[out_bstride * b + row] = (uint16_t)f32_to_bf16_rne(yv);
-            else static_cast<float*>(out)[out_bstride * b + row] = yv;
-          } else {
-            static_cast<float*>(out)[out_bstride * b + row] = total;
-          }
-        } else {
-          part[((size_t)rs * TMAX + (m0 + r)) * S + sl] = total;
-        }
+        if (S == 1) emit(row, total);
+        else part[((size_t)rs * TMAX + (m0 + r)) * S + sl] = total;
       }
     }
+  };
+
+  int row0 = stream, m0 = 0;
+  const int step = RPW * nstreams;
+  while (row0 < R) {
+    const int row1 = row0 + step;
+    if (row1 < R) load(wb, row1);
+    compute(wa, row0, m0);
+    if (row1 >= R) break;
+    const int row2 = row1 + step;
+    if (row2 < R) load(wa, row2);
+    compute(wb, row1, m0 + RPW);
+    row0 = row2;
+    m0 += 2 * RPW;
   }
   if (S > 1) {
     __syncthreads();
@@ -131,13 +186,7 @@ __global__ __launch_bounds__(256) void bin_gemv_kernel(
       if (row < R) {
         float t = 0.f;
         for (int j = 0; j < S; ++j) t += part[(size_t)idx * S + j];
-        if constexpr (MODE == 2) {
-          const float yv = t * f16_bits_to_f32(oscale[row]);
-          if (y_bf16) static_cast<uint16_t*>(out)[out_bstride * b + row] = (uint16_t)f32_to_bf16_rne(yv);
-          else static_cast<float*>(out)[out_bstride * b + row] = yv;
-        } else {
-          static_cast<float*>(out)[out_bstride * b + row] = t;
-        }
+        emit(row, t);
       }
     }
   }
@@ -148,24 +197,29 @@ static hipError_t bin_gemv_t(const uint32_t* bits, int64_t R, int64_t Wn, int64_
                              const void* vin, const uint16_t* vscale, const uint16_t* oscale,
                              void* out, int y_bf16, int64_t B, int64_t in_bstride,
                              int64_t out_bstride, hipStream_t s) {
-  constexpr int UI = 4, RPW = 2;
+  constexpr int UI = 2, RPW = QG_BIN_RPW;
+  constexpr int64_t kTargetWaves = 2048;
   const int Wv = (int)((Lk + 31) / 32);
-  const int S = (Wv + 64 * UI - 1) / (64 * UI);
-  if (S > 4) return hipErrorInvalidValue;
-  const int RS = 4 / S;
+  int S = (Wv + 64 * UI - 1) / (64 * UI);
+  if (S > 8) return hipErrorInvalidValue;
+  while (S < 4 && R * S < kTargetWaves && (Wv + 2 * S - 1) / (2 * S) >= 64) S *= 2;
+  const int RS = S <= 4 ? 4 / S : 1;
   const int WSL = (Wv + S - 1) / S;
   const int threads = 64 * S * RS;
-  const int64_t streams_wanted = (R + 7) / 8;
-  int64_t blocks = (streams_wanted + RS - 1) / RS;
+  int64_t nstreams_wanted = kTargetWaves / S;
+  if (nstreams_wanted > R) nstreams_wanted = R;
+  int64_t blocks = (nstreams_wanted + RS - 1) / RS;
   if (blocks < 1) blocks = 1;
-  if (blocks > 2048) blocks = 2048;
   const int64_t nstreams = blocks * RS;
   const int TMAX = (int)((R + nstreams - 1) / nstreams);
   const size_t lds = S > 1 ? (size_t)RS * TMAX * S * sizeof(float) : 0;
   if (lds > 64 * 1024) return hipErrorInvalidValue;
+  const size_t esz = MODE == 0 ? 2 : 4;
+  const int vec_ok = ((reinterpret_cast<uintptr_t>(vin) % 16) == 0 && ((in_bstride * esz) % 16) == 0 &&
+                      (MODE == 2 || (reinterpret_cast<uintptr_t>(vscale) % 16) == 0)) ? 1 : 0;
   hipLaunchKernelGGL((bin_gemv_kernel<MODE, UI, RPW>), dim3((unsigned)blocks, (unsigned)B),
                      dim3(threads), lds, s, bits, (int)R, (int)Wn, (int)Lk, vin, vscale, oscale,
-                     out, y_bf16, S, RS, WSL, TMAX, in_bstride, out_bstride);
+                     out, y_bf16, S, RS, WSL, TMAX, in_bstride, out_bstride, vec_ok);
   return hipGetLastError();
 }
 

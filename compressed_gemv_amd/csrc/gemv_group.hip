@@ -22,29 +22,50 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+// Tile parameters of the B = 1 kernel (compile-time).
+#ifndef QG_B1_UI
+#define QG_B1_UI 2        // units per lane held in registers (K-slice = 2048*UI inputs)
+#endif
+#ifndef QG_B1_RPW
+#define QG_B1_RPW 2       // rows decoded per pipeline stage
+#endif
+#ifndef QG_B1_WAVES
+#define QG_B1_WAVES 0     // target waves per launch; 0 = by shape (8 or 16 per CU)
+#endif
+
 namespace qg {
 
+// Packed weights are read exactly once per call: nontemporal loads keep them
+// from displacing the activations in the caches (measured on MI355X: ~7.1
+// TB/s streaming with nontemporal 16-byte loads vs ~6.3 TB/s without).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <int B>
 __device__ __forceinline__ void load_unit(const uint32_t* __restrict__ p, uint32_t (&w)[B]) {
   if constexpr (B == 4) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   } else if constexpr (B == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    w[0] = v[0]; w[1] = v[1];
   } else if constexpr (B == 6) {
-    const uint2* q = reinterpret_cast<const uint2*>(p);
+    const u32x2_t* q = reinterpret_cast<const u32x2_t*>(p);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) { const uint2 v = q[i]; w[2 * i] = v.x; w[2 * i + 1] = v.y; }
+    for (int i = 0; i < 3; ++i) {
+      const u32x2_t v = __builtin_nontemporal_load(q + i);
+      w[2 * i] = v[0]; w[2 * i + 1] = v[1];
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = p[i];
+    for (int i = 0; i < B; ++i) w[i] = __builtin_nontemporal_load(p + i);
   }
+}
+__device__ __forceinline__ uint32_t load_meta(const uint32_t* __restrict__ p) {
+  return __builtin_nontemporal_load(p);
 }
 
 // ------------------------------------------------------------------ B = 1
 template <int BITS, int G, bool XF32, int UI, int RPW>
-__global__ __launch_bounds__(256) void gemv_b1_kernel(
+__global__ __launch_bounds__(512) void gemv_b1_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
     const void* __restrict__ xin, void* __restrict__ yout, int y_bf16, int S, int RS, int USL,
     int TMAX) {
@@ -55,15 +76,46 @@ __global__ __launch_bounds__(256) void gemv_b1_kernel(
   const int U = K >> 5;
   const int GN = K / G;
 
-  uint32_t xp[UI][16 * XS];
-  float negC[UI], xsum[UI];
   int uidx[UI];
 #pragma unroll
   for (int it = 0; it < UI; ++it) {
     const int lu = it * 64 + lane;
     const int u = sl * USL + lu;
-    const bool v = (lu < USL) && (u < U);
-    uidx[it] = v ? u : -1;
+    uidx[it] = ((lu < USL) && (u < U)) ? u : -1;
+  }
+  const int nstreams = gridDim.x * RS;
+  const int stream = blockIdx.x * RS + rs;
+
+  // Rows are visited in chunks of RPW; the loads of the next chunk are issued
+  // before the current chunk is decoded (two register buffers, ping-pong).
+  // The first chunk is requested before the activations are prepared.
+  uint32_t wa[RPW][UI][BITS], ma[RPW][UI];
+  uint32_t wb[RPW][UI][BITS], mb[RPW][UI];
+  auto load = [&](uint32_t (&w)[RPW][UI][BITS], uint32_t (&m)[RPW][UI], int row0) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = row0 + r * nstreams;
+#pragma unroll
+      for (int it = 0; it < UI; ++it) {
+        if (row < N && uidx[it] >= 0) {
+          load_unit<BITS>(codes + ((size_t)row * U + uidx[it]) * BITS, w[r][it]);
+          m[r][it] = load_meta(meta + (size_t)row * GN + (uidx[it] * 32) / G);
+        } else {
+#pragma unroll
+          for (int i = 0; i < BITS; ++i) w[r][it][i] = 0u;
+          m[r][it] = 0u;
+        }
+      }
+    }
+  };
+  if (stream < N) load(wa, ma, stream);
+
+  uint32_t xp[UI][16 * XS];
+  float negC[UI], xsum[UI];
+#pragma unroll
+  for (int it = 0; it < UI; ++it) {
+    const bool v = uidx[it] >= 0;
+    const int u = uidx[it];
     float xv[32];
     if (v) {
       if constexpr (XF32) {
@@ -113,43 +165,22 @@ __global__ __launch_bounds__(256) void gemv_b1_kernel(
     xsum[it] = xs;
   }
 
-  const int nstreams = gridDim.x * RS;
-  const int stream = blockIdx.x * RS + rs;
-  for (int m0 = 0;; m0 += RPW) {
-    const int row0 = stream + m0 * nstreams;
-    if (row0 >= N) break;
-    uint32_t wv[RPW][UI][BITS];
-    uint32_t mv[RPW][UI];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int row = row0 + r * nstreams;
-#pragma unroll
-      for (int it = 0; it < UI; ++it) {
-        if (row < N && uidx[it] >= 0) {
-          load_unit<BITS>(codes + ((size_t)row * U + uidx[it]) * BITS, wv[r][it]);
-          mv[r][it] = meta[(size_t)row * GN + (uidx[it] * 32) / G];
-        } else {
-#pragma unroll
-          for (int i = 0; i < BITS; ++i) wv[r][it][i] = 0u;
-          mv[r][it] = 0u;
-        }
-      }
-    }
+  auto compute = [&](const uint32_t (&w)[RPW][UI][BITS], const uint32_t (&m)[RPW][UI], int row0, int m0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       float acc_row = 0.f;
 #pragma unroll
       for (int it = 0; it < UI; ++it) {
         uint32_t pr[16];
-        decode_unit<BITS>(wv[r][it], pr);
+        decode_unit<BITS>(w[r][it], pr);
         float a = negC[it];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           a = dot2_bf16(pr[k], xp[it][k * XS], a);
           if constexpr (XF32) a = dot2_bf16(pr[k], xp[it][k * XS + 1], a);
         }
-        const float s = f16_bits_to_f32(mv[r][it] & 0xFFFFu);
-        const float o = f16_bits_to_f32(mv[r][it] >> 16);
+        const float s = f16_bits_to_f32(m[r][it] & 0xFFFFu);
+        const float o = f16_bits_to_f32(m[r][it] >> 16);
         acc_row = __builtin_fmaf(s, a, __builtin_fmaf(o, xsum[it], acc_row));
       }
       const float total = wave_sum(acc_row);
@@ -163,6 +194,20 @@ __global__ __launch_bounds__(256) void gemv_b1_kernel(
         }
       }
     }
+  };
+
+  int row0 = stream, m0 = 0;
+  const int step = RPW * nstreams;
+  while (row0 < N) {
+    const int row1 = row0 + step;
+    if (row1 < N) load(wb, mb, row1);
+    compute(wa, ma, row0, m0);
+    if (row1 >= N) break;
+    const int row2 = row1 + step;
+    if (row2 < N) load(wa, ma, row2);
+    compute(wb, mb, row1, m0 + RPW);
+    row0 = row2;
+    m0 += 2 * RPW;
   }
   if (S > 1) {
     __syncthreads();
@@ -180,65 +225,98 @@ __global__ __launch_bounds__(256) void gemv_b1_kernel(
 }
 
 // --------------------------------------------------------------- B = 2..16
-template <int BITS, int G>
+// A workgroup owns RT 16-row tiles; its 4 waves split K (wave w takes unit
+// quads w, w+4, ...), so the activation fragments a wave loads are reused by
+// RT tiles.  Lane (r, kg) = (lane % 16, lane / 16) decodes unit 4*q + kg of
+// row r of every tile; the 4 lane groups therefore cover 4 consecutive units
+// (128 inputs) per MFMA quad, and the activation lane (b, kg) loads the
+// matching 8-wide slices of x[b].  Partial sums of the 4 waves meet in LDS.
+template <int BITS, int G, int RT>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
     const uint16_t* __restrict__ x, int B, void* __restrict__ yout, int y_bf16) {
+  __shared__ float red[4][RT * 4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * 4 + wave) * 16;
-  if (row0 >= N) return;
+  const int row_base = blockIdx.x * (16 * RT);
   const int r = lane & 15, kg = lane >> 4;
-  const int row = row0 + r;
-  const bool rvalid = row < N;
   const int U = K >> 5, GN = K / G;
   const int bcol = lane & 15;
   const bool bvalid = bcol < B;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const int nq = (U + 3) >> 2;
-  for (int qi = 0; qi < nq; ++qi) {
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  struct Buf { u32x4_t xb[4]; uint32_t w[RT][BITS]; uint32_t m[RT]; };
+  auto load = [&](Buf& b, int qi) {
     const int u = 4 * qi + kg;
     const bool uvalid = u < U;
-    uint32_t w[BITS];
-    uint32_t m = 0u;
-    if (rvalid && uvalid) {
-      load_unit<BITS>(codes + ((size_t)row * U + u) * BITS, w);
-      m = meta[(size_t)row * GN + (u * 32) / G];
-    } else {
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) w[i] = 0u;
-    }
-    u32x4_t xb[4];
     if (bvalid && uvalid) {
       const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)bcol * K + (size_t)u * 32);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) xb[t] = src[t];
+      for (int t = 0; t < 4; ++t) b.xb[t] = src[t];
     } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) xb[t] = u32x4_t{0u, 0u, 0u, 0u};
+      for (int t = 0; t < 4; ++t) b.xb[t] = u32x4_t{0u, 0u, 0u, 0u};
     }
-    float qf[32];
-    unit_codes_f32<BITS>(w, qf);
-    const float s = f16_bits_to_f32(m & 0xFFFFu), o = f16_bits_to_f32(m >> 16);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4_t a;
+    for (int t = 0; t < RT; ++t) {
+      const int row = row_base + 16 * t + r;
+      if (row < N && uvalid) {
+        load_unit<BITS>(codes + ((size_t)row * U + u) * BITS, b.w[t]);
+        b.m[t] = load_meta(meta + (size_t)row * GN + (u * 32) / G);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        a[j] = pack_bf16x2(__builtin_fmaf(s, qf[8 * t + 2 * j], o),
-                           __builtin_fmaf(s, qf[8 * t + 2 * j + 1], o));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                    __builtin_bit_cast(bf16x8_t, xb[t]), acc,
-                                                    0, 0, 0);
-    }
-  }
-  if (bvalid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ro = row0 + 4 * kg + i;
-      if (ro < N) {
-        if (y_bf16) static_cast<uint16_t*>(yout)[(size_t)bcol * N + ro] = (uint16_t)f32_to_bf16_rne(acc[i]);
-        else static_cast<float*>(yout)[(size_t)bcol * N + ro] = acc[i];
+        for (int i = 0; i < BITS; ++i) b.w[t][i] = 0u;
+        b.m[t] = 0u;
       }
+    }
+  };
+  auto compute = [&](const Buf& b) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      float qf[32];
+      unit_codes_f32<BITS>(b.w[t], qf);
+      const float s = f16_bits_to_f32(b.m[t] & 0xFFFFu), o = f16_bits_to_f32(b.m[t] >> 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4_t a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a[e] = cvt_pk_bf16(__builtin_fmaf(s, qf[8 * j + 2 * e], o), __builtin_fmaf(s, qf[8 * j + 2 * e + 1], o));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                         __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nq = (U + 3) >> 2;
+  Buf b0, b1;
+  int qi = wave;
+  if (qi < nq) load(b0, qi);
+  while (qi < nq) {
+    const int q1 = qi + 4;
+    if (q1 < nq) load(b1, q1);
+    compute(b0);
+    if (q1 >= nq) break;
+    const int q2 = q1 + 4;
+    if (q2 < nq) load(b0, q2);
+    compute(b1);
+    qi = q2;
+  }
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][t * 4 + i][lane] = acc[t][i];
+  __syncthreads();
+  // lane holds D[4*kg + i][bcol] of each tile: row 16t + 4kg + i, batch bcol
+  for (int v = threadIdx.x; v < RT * 4 * 64; v += 256) {
+    const int ti = v / 64, ln = v % 64;
+    const float sum = (red[0][ti][ln] + red[1][ti][ln]) + (red[2][ti][ln] + red[3][ti][ln]);
+    const int t = ti / 4, i = ti % 4;
+    const int b = ln & 15, row = row_base + 16 * t + 4 * (ln >> 4) + i;
+    if (b < B && row < N) {
+      if (y_bf16) static_cast<uint16_t*>(yout)[(size_t)b * N + row] = (uint16_t)f32_to_bf16_rne(sum);
+      else static_cast<float*>(yout)[(size_t)b * N + row] = sum;
     }
   }
 }
@@ -247,16 +325,19 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
 template <int BITS, int G, bool XF32, int UI, int RPW>
 static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
                             const void* x, void* y, int y_bf16, hipStream_t s) {
+  const int64_t kTargetWaves = QG_B1_WAVES ? QG_B1_WAVES : (N >= 16384 ? 4096 : 2048);
   const int U = (int)(K / 32);
-  const int S = (U + 64 * UI - 1) / (64 * UI);
-  if (S > 4) return hipErrorInvalidValue;
-  const int RS = 4 / S;
+  int S = (U + 64 * UI - 1) / (64 * UI);
+  if (S > 8) return hipErrorInvalidValue;
+  // short matrices: split K further so the grid still has ~8 waves per CU
+  while (S < 4 && N * S < kTargetWaves && (U + 2 * S - 1) / (2 * S) >= 64) S *= 2;
+  const int RS = S <= 4 ? 4 / S : 1;   // 256 threads, or 64*S (<= 512) for long rows
   const int USL = (U + S - 1) / S;
   const int threads = 64 * S * RS;
-  const int64_t streams_wanted = (N + 15) / 16;  // about 16 rows per wave
-  int64_t blocks = (streams_wanted + RS - 1) / RS;
+  int64_t nstreams_wanted = kTargetWaves / S;
+  if (nstreams_wanted > N) nstreams_wanted = N;
+  int64_t blocks = (nstreams_wanted + RS - 1) / RS;
   if (blocks < 1) blocks = 1;
-  if (blocks > 2048) blocks = 2048;
   const int64_t nstreams = blocks * RS;
   const int TMAX = (int)((N + nstreams - 1) / nstreams);
   const size_t lds = S > 1 ? (size_t)RS * TMAX * S * sizeof(float) : 0;
@@ -270,10 +351,17 @@ static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t
 template <int BITS, int G>
 static hipError_t gemv_mfma_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
                               const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s) {
-  const int64_t tiles = (N + 15) / 16;
-  const int64_t blocks = (tiles + 3) / 4;
-  hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G>), dim3((unsigned)blocks), dim3(256), 0, s, codes,
-                     meta, (int)N, (int)K, x, (int)B, y, y_bf16);
+  // largest row-tile count that still gives >= 256 workgroups
+  if ((N + 63) / 64 >= 256) {
+    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, 4>), dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s,
+                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16);
+  } else if ((N + 31) / 32 >= 256) {
+    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, 2>), dim3((unsigned)((N + 31) / 32)), dim3(256), 0, s,
+                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16);
+  } else {
+    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, 1>), dim3((unsigned)((N + 15) / 16)), dim3(256), 0, s,
+                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16);
+  }
   return hipGetLastError();
 }
 
@@ -283,7 +371,7 @@ static hipError_t gemv_dispatch(const uint32_t* codes, const uint32_t* meta, int
                                 int y_bf16, hipStream_t s) {
   if (B == 1) {
     if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s);
-    return gemv_b1_t<BITS, G, false, 4, 2>(codes, meta, N, K, x, y, y_bf16, s);
+    return gemv_b1_t<BITS, G, false, QG_B1_UI, QG_B1_RPW>(codes, meta, N, K, x, y, y_bf16, s);
   }
   if (x_dtype != 1) return hipErrorInvalidValue;
   return gemv_mfma_t<BITS, G>(codes, meta, N, K, static_cast<const uint16_t*>(x), B, y, y_bf16, s);
