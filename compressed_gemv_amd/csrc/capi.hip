@@ -19,7 +19,8 @@ int group_args_ok(int64_t N, int64_t K, int bits, int group) {
   if (bits < 2 || bits > 6) return Q_EINVAL;
   if (group != 32 && group != 64) return Q_EINVAL;
   if (K % group) return Q_EINVAL;
-  if ((N * (K / 32)) > (int64_t)1 << 34) return Q_EUNSUPPORTED;
+  // the kernels address codes and meta through 32-bit buffer offsets
+  if (N * K / 8 * bits >= ((int64_t)1 << 32)) return Q_EUNSUPPORTED;
   return Q_OK;
 }
 
@@ -30,11 +31,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? Q_OK : Q_EHIP; }
 int dtype_ok(int d) { return d == Q_F32 || d == Q_BF16; }
 
 // B = 1 keeps a K-slice of activations in registers; at most 8 slices of
-// 64 lanes x UI units x 32 inputs.
-#ifndef QG_B1_UI
-#define QG_B1_UI 2
-#endif
-int64_t gemv_b1_max_k(int x_dtype) { return x_dtype == Q_F32 ? 8 * 64 * 2 * 32 : 8 * 64 * QG_B1_UI * 32; }
+// 64 lanes x UI units x 32 inputs (UI = 4 for bf16 rows longer than 16384,
+// 2 for fp32 activations).
+int64_t gemv_b1_max_k(int x_dtype) { return x_dtype == Q_F32 ? 8 * 64 * 2 * 32 : 8 * 64 * 4 * 32; }
 
 }  // namespace
 
@@ -118,6 +117,9 @@ int qbinlr_sizes(int64_t N, int64_t K, int64_t r, int64_t B, size_t* ubits_bytes
                  size_t* vtbits_bytes, size_t* ws_bytes) {
   if (N < 1 || K < 1 || r < 1 || N > kMaxDim || K > kMaxDim || r > kMaxDim) return Q_EINVAL;
   if (B < 1 || B > 16) return Q_EINVAL;
+  // sign words are addressed through 32-bit buffer offsets
+  if (N * padded_words(r) * 4 >= ((int64_t)1 << 32) || r * padded_words(K) * 4 >= ((int64_t)1 << 32))
+    return Q_EUNSUPPORTED;
   if (ubits_bytes) *ubits_bytes = (size_t)(N * padded_words(r) * 4);
   if (vtbits_bytes) *vtbits_bytes = (size_t)(r * padded_words(K) * 4);
   if (ws_bytes) *ws_bytes = (size_t)(B * padded_words(r) * 32 * 4);

@@ -76,12 +76,53 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// ------------------------------------------------------------- buffer loads
+// Weight streams are read through buffer resources: 32-bit byte offsets, the
+// wave-uniform row offset in an SGPR, hardware range checking (a load past
+// num_records returns 0, so no lane ever needs a branch or a clamp to stay
+// in bounds).  aux = 2 sets the nontemporal bit: the packed weights are read
+// once per call (measured on MI355X: ~7.1 TB/s streaming with nontemporal
+// 16-byte loads vs ~6.3 TB/s without).
+constexpr int kNT = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int B>
+__device__ __forceinline__ void buf_load_unit(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              uint32_t (&w)[B]) {
+  if constexpr (B == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNT);
+    w[0] = v[0]; w[1] = v[1];
+  } else if constexpr (B == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, kNT);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+    if constexpr (B == 5) {
+      w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 16, soff, kNT);
+    } else if constexpr (B == 6) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 16, soff, kNT);
+      w[4] = t[0]; w[5] = t[1];
+    }
+  }
+}
+__device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNT);
+}
+
 // ---------------------------------------------------------------- unit layout
 // Pair k of a unit (k = 0..15): low-half code ca, high-half code cb and the
 // mantissa bit p the fields land on after decode.
 struct PairInfo { int ca, cb, p; };
 
 template <int B> struct Unit {
+  // landing-bit classes: codes decoded at mantissa bit p = 0, 2, 4 (b = 2),
+  // p = 0, 3 (b = 3), p = 0 (b >= 4)
+  static constexpr int NCLS = B == 2 ? 3 : (B == 3 ? 2 : 1);
+  static constexpr int cls_of_p(int p) { return B == 2 ? p / 2 : (B == 3 ? p / 3 : 0); }
   static constexpr int F = 16 / B;                 // fields per half-word
   static constexpr int kRegularPairs = F * B;      // F pairs per word, B words
   // shift that brings field j near bit 0, and its landing bit p
@@ -102,29 +143,42 @@ template <int B> struct Unit {
   }
 };
 
+// The bias is kept in an opaque register so (x & mask) | bias compiles to a
+// single v_and_or_b32 (gfx9 VOP3 takes no literal operands; with both
+// constants visible the compiler would emit v_and_b32 + v_or_b32 instead).
+__device__ __forceinline__ uint32_t opaque_bias() {
+  uint32_t b = kBias2;
+  asm volatile("" : "+v"(b));
+  return b;
+}
+
 // Decode one unit (B words) into 16 bf16x2 operands (128 + q*2^p per lane).
 template <int B>
-__device__ __forceinline__ void decode_unit(const uint32_t (&w)[B], uint32_t (&pr)[16]) {
+__device__ __forceinline__ void decode_unit(const uint32_t (&w)[B], uint32_t (&pr)[16], uint32_t bias) {
   using U = Unit<B>;
 #pragma unroll
   for (int k = 0; k < U::kRegularPairs; ++k) {
     const int wi = k / U::F, j = k % U::F;
     const uint32_t m = ((1u << B) - 1u) << U::p_of(j);
     const uint32_t mask = m | (m << 16);
-    pr[k] = ((w[wi] >> U::shift_of(j)) & mask) | kBias2;
+    pr[k] = ((w[wi] >> U::shift_of(j)) & mask) | bias;
   }
   if constexpr (B == 3 || B == 5) {
-    uint32_t t = kBias2;
+    uint32_t t = bias;
 #pragma unroll
-    for (int i = 0; i < B; ++i) t |= (w[i] >> (15 - i)) & (0x00010001u << i);
+    for (int i = 0; i < B; ++i) t = ((w[i] >> (15 - i)) & (0x00010001u << i)) | t;
     pr[15] = t;
   } else if constexpr (B == 6) {
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      pr[12 + pp] = ((w[pp] >> 12) & 0x000F000Fu) |
-                    ((w[4 + pp / 2] >> (8 + 2 * (pp % 2))) & 0x00300030u) | kBias2;
+      const uint32_t lo = ((w[pp] >> 12) & 0x000F000Fu) | bias;
+      pr[12 + pp] = ((w[4 + pp / 2] >> (8 + 2 * (pp % 2))) & 0x00300030u) | lo;
     }
   }
+}
+template <int B>
+__device__ __forceinline__ void decode_unit(const uint32_t (&w)[B], uint32_t (&pr)[16]) {
+  decode_unit<B>(w, pr, kBias2);
 }
 
 // Codes of one unit as fp32 values q (exact), natural code order.

@@ -33,7 +33,8 @@ __global__ __launch_bounds__(512) void bin_gemv_kernel(
     void* __restrict__ out, int y_bf16, int S, int RS, int WSL, int TMAX, int64_t in_bstride,
     int64_t out_bstride, int vec_ok) {
   extern __shared__ float part[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sl = wave % S, rs = wave / S;
   const int b = blockIdx.y;
   const int Wv = (Lk + 31) >> 5;   // words holding real entries
@@ -48,16 +49,45 @@ __global__ __launch_bounds__(512) void bin_gemv_kernel(
   const int nstreams = gridDim.x * RS;
   const int stream = blockIdx.x * RS + rs;
   uint32_t wa[RPW][UI], wb[RPW][UI];
+  // Sign words through a buffer resource: rows past R read 0 (never stored),
+  // lanes without a word have zero activations.
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(bits, (uint32_t)((size_t)R * Wn * 4));
+  uint32_t wvoff[UI];
+#pragma unroll
+  for (int it = 0; it < UI; ++it) wvoff[it] = (uint32_t)(sl * WSL + it * 64 + lane) * 4;
+  const uint32_t wrow = (uint32_t)Wn * 4;
   auto load = [&](uint32_t (&w)[RPW][UI], int row0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      const int row = row0 + r * nstreams;
+      const uint32_t row = (uint32_t)(row0 + r * nstreams);
 #pragma unroll
-      for (int it = 0; it < UI; ++it)
-        w[r][it] = (row < R && widx[it] >= 0) ? __builtin_nontemporal_load(bits + (size_t)row * Wn + widx[it]) : 0u;
+      for (int it = 0; it < UI; ++it) w[r][it] = buf_load_u32(brs, wvoff[it], row * wrow);
     }
   };
-  if (stream < R) load(wa, stream);
+  const int step = RPW * nstreams;
+  const int nst = stream < R ? (R - stream + step - 1) / step : 0;
+
+  // vector: clamped unconditional loads before the first weight stage
+  constexpr int XW = MODE == 0 ? 4 : 8;
+  u32x4_t vraw[UI][XW], sraw[UI][4];
+  const bool vec_tile = vec_ok && (Lk % 32 == 0);
+  if (vec_tile) {
+#pragma unroll
+    for (int it = 0; it < UI; ++it) {
+      const int k0 = (widx[it] >= 0 ? widx[it] : 0) * 32;
+      const u32x4_t* src = MODE == 0
+          ? reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(vin) + in_bstride * b + k0)
+          : reinterpret_cast<const u32x4_t*>(static_cast<const float*>(vin) + in_bstride * b + k0);
+#pragma unroll
+      for (int i = 0; i < XW; ++i) vraw[it][i] = src[i];
+      if constexpr (MODE != 2) {
+        const u32x4_t* sp = reinterpret_cast<const u32x4_t*>(vscale + k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sraw[it][i] = sp[i];
+      }
+    }
+  }
+  if (nst > 0) load(wa, stream);
 
   uint32_t xp[UI][32];
   float negC[UI], vsum[UI];
@@ -67,48 +97,39 @@ __global__ __launch_bounds__(512) void bin_gemv_kernel(
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = 0.f;
     const int wi = widx[it];
-    if (wi >= 0) {
+    if (vec_tile) {
+      const bool ok = wi >= 0;
+#pragma unroll
+      for (int i = 0; i < XW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (MODE == 0) {
+            v[8 * i + 2 * j] = ok ? bf16_lo_to_f32(vraw[it][i][j]) : 0.f;
+            v[8 * i + 2 * j + 1] = ok ? bf16_hi_to_f32(vraw[it][i][j]) : 0.f;
+          } else {
+            v[4 * i + j] = ok ? __uint_as_float(vraw[it][i][j]) : 0.f;
+          }
+        }
+      if constexpr (MODE != 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[8 * i + 2 * j] *= f16_bits_to_f32(sraw[it][i][j] & 0xFFFFu);
+            v[8 * i + 2 * j + 1] *= f16_bits_to_f32(sraw[it][i][j] >> 16);
+          }
+      }
+    } else if (wi >= 0) {
       const int k0 = wi * 32;
-      if (vec_ok && k0 + 32 <= Lk) {
-        if constexpr (MODE == 0) {
-          const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(vin) + in_bstride * b + k0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const u32x4_t t = src[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { v[8 * i + 2 * j] = bf16_lo_to_f32(t[j]); v[8 * i + 2 * j + 1] = bf16_hi_to_f32(t[j]); }
-          }
-        } else {
-          const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(vin) + in_bstride * b + k0);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float4 t = src[i];
-            v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-          }
-        }
-        if constexpr (MODE != 2) {
-          const u32x4_t* sp = reinterpret_cast<const u32x4_t*>(vscale + k0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const u32x4_t t = sp[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              v[8 * i + 2 * j] *= f16_bits_to_f32(t[j] & 0xFFFFu);
-              v[8 * i + 2 * j + 1] *= f16_bits_to_f32(t[j] >> 16);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int k = k0 + i;
-          if (k < Lk) {
-            float xv;
-            if constexpr (MODE == 0) xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k]);
-            else xv = static_cast<const float*>(vin)[in_bstride * b + k];
-            if constexpr (MODE != 2) xv *= f16_bits_to_f32(vscale[k]);
-            v[i] = xv;
-          }
+      for (int i = 0; i < 32; ++i) {
+        const int k = k0 + i;
+        if (k < Lk) {
+          float xv;
+          if constexpr (MODE == 0) xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k]);
+          else xv = static_cast<const float*>(vin)[in_bstride * b + k];
+          if constexpr (MODE != 2) xv *= f16_bits_to_f32(vscale[k]);
+          v[i] = xv;
         }
       }
     }
@@ -139,6 +160,7 @@ __global__ __launch_bounds__(512) void bin_gemv_kernel(
       static_cast<float*>(out)[out_bstride * b + row] = total;
     }
   };
+  const uint32_t bias = opaque_bias();
   auto compute = [&](const uint32_t (&w)[RPW][UI], int row0, int m0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
@@ -150,7 +172,7 @@ __global__ __launch_bounds__(512) void bin_gemv_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const uint32_t m = 0x00010001u << bin_p(j);
-          const uint32_t pr = ((ww >> bin_shift(j)) & m) | kBias2;
+          const uint32_t pr = ((ww >> bin_shift(j)) & m) | bias;
           a = dot2_bf16(pr, xp[it][2 * j], a);
           a = dot2_bf16(pr, xp[it][2 * j + 1], a);
         }
@@ -165,18 +187,20 @@ __global__ __launch_bounds__(512) void bin_gemv_kernel(
     }
   };
 
-  int row0 = stream, m0 = 0;
-  const int step = RPW * nstreams;
-  while (row0 < R) {
-    const int row1 = row0 + step;
-    if (row1 < R) load(wb, row1);
-    compute(wa, row0, m0);
-    if (row1 >= R) break;
-    const int row2 = row1 + step;
-    if (row2 < R) load(wa, row2);
-    compute(wb, row1, m0 + RPW);
-    row0 = row2;
-    m0 += 2 * RPW;
+  int st = 0;
+  while (st + 2 < nst) {
+    load(wb, stream + (st + 1) * step);
+    compute(wa, stream + st * step, st * RPW);
+    load(wa, stream + (st + 2) * step);
+    compute(wb, stream + (st + 1) * step, (st + 1) * RPW);
+    st += 2;
+  }
+  if (st + 1 < nst) {
+    load(wb, stream + (st + 1) * step);
+    compute(wa, stream + st * step, st * RPW);
+    compute(wb, stream + (st + 1) * step, (st + 1) * RPW);
+  } else if (st < nst) {
+    compute(wa, stream + st * step, st * RPW);
   }
   if (S > 1) {
     __syncthreads();

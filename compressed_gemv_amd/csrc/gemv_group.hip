@@ -6,6 +6,8 @@
 // packed codes with coalesced vector loads, never write dequantized weights
 // anywhere, and keep the per-weight ALU work small:
 //
+// Weight streams are read with nontemporal buffer loads (see common.hpp).
+//
 //  * B = 1 (VALU): a lane owns one 32-code unit per row.  Its activations
 //    are turned once into bf16 pairs pre-scaled for the landing bit of each
 //    code (see common.hpp) and held in registers for every row the wave
@@ -22,46 +24,23 @@
 #include "common.hpp"
 #include "launch.hpp"
 
-// Tile parameters of the B = 1 kernel (compile-time).
+// Tile parameters of the B = 1 kernel.  UI = units per lane held in
+// registers (a K-slice covers 2048*UI inputs), RPW = rows per pipeline
+// stage, target waves per launch.  Measured on MI355X: 4-bit codes and long
+// rows (K > 16384) run best with UI = 4 and 1024 waves (one per SIMD, deep
+// per-wave streams); 2/3/5/6-bit with UI = 2 and 2048 waves (more waves to
+// cover their longer decode).  QG_B1_UI / QG_B1_WAVES force one choice.
 #ifndef QG_B1_UI
-#define QG_B1_UI 2        // units per lane held in registers (K-slice = 2048*UI inputs)
+#define QG_B1_UI 0
 #endif
 #ifndef QG_B1_RPW
-#define QG_B1_RPW 2       // rows decoded per pipeline stage
+#define QG_B1_RPW 2
 #endif
 #ifndef QG_B1_WAVES
-#define QG_B1_WAVES 0     // target waves per launch; 0 = by shape (8 or 16 per CU)
+#define QG_B1_WAVES 0
 #endif
 
 namespace qg {
-
-// Packed weights are read exactly once per call: nontemporal loads keep them
-// from displacing the activations in the caches (measured on MI355X: ~7.1
-// TB/s streaming with nontemporal 16-byte loads vs ~6.3 TB/s without).
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-template <int B>
-__device__ __forceinline__ void load_unit(const uint32_t* __restrict__ p, uint32_t (&w)[B]) {
-  if constexpr (B == 4) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-  } else if constexpr (B == 2) {
-    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-    w[0] = v[0]; w[1] = v[1];
-  } else if constexpr (B == 6) {
-    const u32x2_t* q = reinterpret_cast<const u32x2_t*>(p);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const u32x2_t v = __builtin_nontemporal_load(q + i);
-      w[2 * i] = v[0]; w[2 * i + 1] = v[1];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = __builtin_nontemporal_load(p + i);
-  }
-}
-__device__ __forceinline__ uint32_t load_meta(const uint32_t* __restrict__ p) {
-  return __builtin_nontemporal_load(p);
-}
 
 // ------------------------------------------------------------------ B = 1
 template <int BITS, int G, bool XF32, int UI, int RPW>
@@ -71,7 +50,8 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
     int TMAX) {
   extern __shared__ float part[];
   constexpr int XS = XF32 ? 2 : 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sl = wave % S, rs = wave / S;
   const int U = K >> 5;
   const int GN = K / G;
@@ -91,80 +71,110 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   // The first chunk is requested before the activations are prepared.
   uint32_t wa[RPW][UI][BITS], ma[RPW][UI];
   uint32_t wb[RPW][UI][BITS], mb[RPW][UI];
+  // Weight loads go through buffer resources (row offset in soffset, the
+  // lane's unit offset in voffset).  A lane without a unit reads whatever
+  // lies at its offset (or 0 past the end): its activation pairs are zero.
+  // Rows past N read 0 and are never stored.  No branches around loads, so
+  // the next stage stays in flight while the current one is decoded.
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
+  uint32_t cvoff[UI], mvoff[UI];
+#pragma unroll
+  for (int it = 0; it < UI; ++it) {
+    const int u = sl * USL + it * 64 + lane;
+    cvoff[it] = (uint32_t)u * (BITS * 4);
+    mvoff[it] = (uint32_t)((u * 32) / G) * 4;
+  }
+  const uint32_t crow = (uint32_t)U * BITS * 4, mrow = (uint32_t)GN * 4;
   auto load = [&](uint32_t (&w)[RPW][UI][BITS], uint32_t (&m)[RPW][UI], int row0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      const int row = row0 + r * nstreams;
+      const uint32_t row = (uint32_t)(row0 + r * nstreams);
 #pragma unroll
       for (int it = 0; it < UI; ++it) {
-        if (row < N && uidx[it] >= 0) {
-          load_unit<BITS>(codes + ((size_t)row * U + uidx[it]) * BITS, w[r][it]);
-          m[r][it] = load_meta(meta + (size_t)row * GN + (uidx[it] * 32) / G);
-        } else {
-#pragma unroll
-          for (int i = 0; i < BITS; ++i) w[r][it][i] = 0u;
-          m[r][it] = 0u;
-        }
+        buf_load_unit<BITS>(crs, cvoff[it], row * crow, w[r][it]);
+        m[r][it] = buf_load_u32(mrs, mvoff[it], row * mrow);
       }
     }
   };
-  if (stream < N) load(wa, ma, stream);
+  // activations first (in-order vmcnt: waiting for them must not wait for
+  // the weight stream), then the first weight stage, then the prep.
+  constexpr int XW = XF32 ? 8 : 4;   // 16-byte loads per unit of activations
+  u32x4_t xraw[UI][XW];
+#pragma unroll
+  for (int it = 0; it < UI; ++it) {
+    const int u = uidx[it] >= 0 ? uidx[it] : 0;
+    const u32x4_t* src = XF32 ? reinterpret_cast<const u32x4_t*>(static_cast<const float*>(xin) + (size_t)u * 32)
+                              : reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(xin) + (size_t)u * 32);
+#pragma unroll
+    for (int i = 0; i < XW; ++i) xraw[it][i] = src[i];
+  }
+  const int step = RPW * nstreams;
+  const int nst = stream < N ? (N - stream + step - 1) / step : 0;   // stages of this stream
+  if (nst > 0) load(wa, ma, stream);
 
+  // Activation prep.  Pair k of a unit holds x[ca] (low bf16) and x[cb]
+  // (high bf16), unscaled; codes that land on mantissa bit p are summed in
+  // their own accumulator and rescaled by 2^-p once per unit, so the pairs
+  // are plain byte permutes of the raw bf16 words.  Per class the
+  // accumulator starts at -128 * (sum of its x), which cancels the 128 bias.
+  // fp32 activations are split into bf16 hi + lo pairs (two dot2 per pair).
+  using UN = Unit<BITS>;
+  constexpr int NC = UN::NCLS;
+  constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 (1, 1)
   uint32_t xp[UI][16 * XS];
-  float negC[UI], xsum[UI];
+  float negC[UI][NC], xsum[UI];
 #pragma unroll
   for (int it = 0; it < UI; ++it) {
     const bool v = uidx[it] >= 0;
-    const int u = uidx[it];
-    float xv[32];
-    if (v) {
-      if constexpr (XF32) {
-        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(xin) + (size_t)u * 32);
+    float cs[NC];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 t = src[i];
-          xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
-        }
-      } else {
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(xin) + (size_t)u * 32);
+    for (int c = 0; c < NC; ++c) cs[c] = 0.f;
+    if constexpr (!XF32) {
+      uint32_t xr[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4_t t = src[i];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            xv[8 * i + 2 * j] = bf16_lo_to_f32(t[j]);
-            xv[8 * i + 2 * j + 1] = bf16_hi_to_f32(t[j]);
-          }
-        }
+        for (int j = 0; j < 4; ++j) xr[4 * i + j] = v ? xraw[it][i][j] : 0u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const PairInfo pi = UN::pair(k);
+        const uint32_t lo = (pi.ca & 1) ? (xr[pi.ca >> 1] >> 16) : (xr[pi.ca >> 1] & 0xFFFFu);
+        const uint32_t hi = (pi.cb & 1) ? (xr[pi.cb >> 1] & 0xFFFF0000u) : (xr[pi.cb >> 1] << 16);
+        xp[it][k] = lo | hi;
+        const int c = UN::cls_of_p(pi.p);
+        cs[c] = dot2_bf16(xp[it][k], kOnes, cs[c]);
       }
     } else {
+      float xv[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) xv[i] = 0.f;
-    }
-    float c = 0.f, xs = 0.f;
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const PairInfo pi = Unit<BITS>::pair(k);
-      const float sc = 1.0f / (float)(1 << pi.p);
-      const float a = xv[pi.ca] * sc, b = xv[pi.cb] * sc;
-      if constexpr (XF32) {
+        for (int j = 0; j < 4; ++j) xv[4 * i + j] = v ? __uint_as_float(xraw[it][i][j]) : 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const PairInfo pi = UN::pair(k);
+        const float a = xv[pi.ca], b = xv[pi.cb];
         const uint32_t ah = f32_to_bf16_rne(a), bh = f32_to_bf16_rne(b);
-        const float al = a - bf16_bits_to_f32(ah), bl = b - bf16_bits_to_f32(bh);
-        const uint32_t alb = f32_to_bf16_rne(al), blb = f32_to_bf16_rne(bl);
+        const uint32_t al = f32_to_bf16_rne(a - bf16_bits_to_f32(ah));
+        const uint32_t bl = f32_to_bf16_rne(b - bf16_bits_to_f32(bh));
         xp[it][2 * k] = ah | (bh << 16);
-        xp[it][2 * k + 1] = alb | (blb << 16);
-        c += (bf16_bits_to_f32(ah) + bf16_bits_to_f32(alb)) + (bf16_bits_to_f32(bh) + bf16_bits_to_f32(blb));
-      } else {
-        xp[it][k] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-        c += a + b;
+        xp[it][2 * k + 1] = al | (bl << 16);
+        const int c = UN::cls_of_p(pi.p);
+        cs[c] = dot2_bf16(xp[it][2 * k], kOnes, cs[c]);
+        cs[c] = dot2_bf16(xp[it][2 * k + 1], kOnes, cs[c]);
       }
     }
+    float xs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) xs += xv[i];
-    negC[it] = -128.0f * c;
+    for (int c = 0; c < NC; ++c) {
+      negC[it][c] = -128.0f * cs[c];
+      xs += cs[c];
+    }
     xsum[it] = xs;
   }
 
+  const uint32_t bias = opaque_bias();
   auto compute = [&](const uint32_t (&w)[RPW][UI][BITS], const uint32_t (&m)[RPW][UI], int row0, int m0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
@@ -172,16 +182,24 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 #pragma unroll
       for (int it = 0; it < UI; ++it) {
         uint32_t pr[16];
-        decode_unit<BITS>(w[r][it], pr);
-        float a = negC[it];
+        decode_unit<BITS>(w[r][it], pr, bias);
+        constexpr int NCH = NC > 1 ? NC : 2;   // independent dot2 chains
+        float a[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) a[c] = c < NC ? negC[it][c] : 0.f;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          a = dot2_bf16(pr[k], xp[it][k * XS], a);
-          if constexpr (XF32) a = dot2_bf16(pr[k], xp[it][k * XS + 1], a);
+          const int c = NC > 1 ? UN::cls_of_p(UN::pair(k).p) : (k & 1);
+          a[c] = dot2_bf16(pr[k], xp[it][k * XS], a[c]);
+          if constexpr (XF32) a[c] = dot2_bf16(pr[k], xp[it][k * XS + 1], a[c]);
         }
+        float sq;
+        if constexpr (BITS == 2) sq = a[0] + 0.25f * a[1] + 0.0625f * a[2];
+        else if constexpr (BITS == 3) sq = a[0] + 0.125f * a[1];
+        else sq = a[0] + a[1];
         const float s = f16_bits_to_f32(m[r][it] & 0xFFFFu);
         const float o = f16_bits_to_f32(m[r][it] >> 16);
-        acc_row = __builtin_fmaf(s, a, __builtin_fmaf(o, xsum[it], acc_row));
+        acc_row = __builtin_fmaf(s, sq, __builtin_fmaf(o, xsum[it], acc_row));
       }
       const float total = wave_sum(acc_row);
       const int row = row0 + r * nstreams;
@@ -196,18 +214,23 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
     }
   };
 
-  int row0 = stream, m0 = 0;
-  const int step = RPW * nstreams;
-  while (row0 < N) {
-    const int row1 = row0 + step;
-    if (row1 < N) load(wb, mb, row1);
-    compute(wa, ma, row0, m0);
-    if (row1 >= N) break;
-    const int row2 = row1 + step;
-    if (row2 < N) load(wa, ma, row2);
-    compute(wb, mb, row1, m0 + RPW);
-    row0 = row2;
-    m0 += 2 * RPW;
+  // Stage st covers rows stream + (st*RPW + r)*nstreams.  Inside the loop
+  // every load is unconditional, so the wait before decoding a stage covers
+  // exactly that stage's loads and the next stage stays in flight.
+  int st = 0;
+  while (st + 2 < nst) {
+    load(wb, mb, stream + (st + 1) * step);
+    compute(wa, ma, stream + st * step, st * RPW);
+    load(wa, ma, stream + (st + 2) * step);
+    compute(wb, mb, stream + (st + 1) * step, (st + 1) * RPW);
+    st += 2;
+  }
+  if (st + 1 < nst) {
+    load(wb, mb, stream + (st + 1) * step);
+    compute(wa, ma, stream + st * step, st * RPW);
+    compute(wb, mb, stream + (st + 1) * step, (st + 1) * RPW);
+  } else if (st < nst) {
+    compute(wa, ma, stream + st * step, st * RPW);
   }
   if (S > 1) {
     __syncthreads();
@@ -236,39 +259,36 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
     const uint16_t* __restrict__ x, int B, void* __restrict__ yout, int y_bf16) {
   __shared__ float red[4][RT * 4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row_base = blockIdx.x * (16 * RT);
   const int r = lane & 15, kg = lane >> 4;
   const int U = K >> 5, GN = K / G;
   const int bcol = lane & 15;
-  const bool bvalid = bcol < B;
   f32x4_t acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  struct Buf { u32x4_t xb[4]; uint32_t w[RT][BITS]; uint32_t m[RT]; };
+  struct Buf { u32x4_t xb[4]; uint32_t w[RT][BITS]; uint32_t m[RT]; bool uvalid; };
+  // Branch-free loads: a lane past B reads a valid activation row (its
+  // column is never stored); weights go through buffer resources (rows past
+  // N read 0 and are never stored; a unit past K reads 0 and its activations
+  // are zeroed at use).
+  const int bc = bcol < B ? bcol : B - 1;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
   auto load = [&](Buf& b, int qi) {
-    const int u = 4 * qi + kg;
-    const bool uvalid = u < U;
-    if (bvalid && uvalid) {
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)bcol * K + (size_t)u * 32);
+    const int u0 = 4 * qi + kg;
+    b.uvalid = u0 < U;
+    const int u = b.uvalid ? u0 : 0;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)bc * K + (size_t)u * 32);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b.xb[t] = src[t];
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) b.xb[t] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int t = 0; t < 4; ++t) b.xb[t] = src[t];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const int row = row_base + 16 * t + r;
-      if (row < N && uvalid) {
-        load_unit<BITS>(codes + ((size_t)row * U + u) * BITS, b.w[t]);
-        b.m[t] = load_meta(meta + (size_t)row * GN + (u * 32) / G);
-      } else {
-#pragma unroll
-        for (int i = 0; i < BITS; ++i) b.w[t][i] = 0u;
-        b.m[t] = 0u;
-      }
+      const uint32_t row = (uint32_t)(row_base + 16 * t + r);
+      buf_load_unit<BITS>(crs, (row * (uint32_t)U + (uint32_t)u0) * (BITS * 4), 0u, b.w[t]);
+      b.m[t] = buf_load_u32(mrs, (row * (uint32_t)GN + (uint32_t)((u0 * 32) / G)) * 4, 0u);
     }
   };
   auto compute = [&](const Buf& b) {
@@ -283,25 +303,31 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           a[e] = cvt_pk_bf16(__builtin_fmaf(s, qf[8 * j + 2 * e], o), __builtin_fmaf(s, qf[8 * j + 2 * e + 1], o));
+        const u32x4_t xv = b.uvalid ? b.xb[j] : u32x4_t{0u, 0u, 0u, 0u};
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                         __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
+                                                         __builtin_bit_cast(bf16x8_t, xv), acc[t], 0, 0, 0);
       }
     }
   };
 
   const int nq = (U + 3) >> 2;
+  const int nit = wave < nq ? (nq - wave + 3) / 4 : 0;   // quads of this wave
   Buf b0, b1;
-  int qi = wave;
-  if (qi < nq) load(b0, qi);
-  while (qi < nq) {
-    const int q1 = qi + 4;
-    if (q1 < nq) load(b1, q1);
+  if (nit > 0) load(b0, wave);
+  int it = 0;
+  while (it + 2 < nit) {
+    load(b1, wave + 4 * (it + 1));
     compute(b0);
-    if (q1 >= nq) break;
-    const int q2 = q1 + 4;
-    if (q2 < nq) load(b0, q2);
+    load(b0, wave + 4 * (it + 2));
     compute(b1);
-    qi = q2;
+    it += 2;
+  }
+  if (it + 1 < nit) {
+    load(b1, wave + 4 * (it + 1));
+    compute(b0);
+    compute(b1);
+  } else if (it < nit) {
+    compute(b0);
   }
 #pragma unroll
   for (int t = 0; t < RT; ++t)
@@ -325,7 +351,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
 template <int BITS, int G, bool XF32, int UI, int RPW>
 static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
                             const void* x, void* y, int y_bf16, hipStream_t s) {
-  const int64_t kTargetWaves = QG_B1_WAVES ? QG_B1_WAVES : (N >= 16384 ? 4096 : 2048);
+  const int64_t kTargetWaves = QG_B1_WAVES ? QG_B1_WAVES : (UI >= 4 ? 1024 : 2048);
   const int U = (int)(K / 32);
   int S = (U + 64 * UI - 1) / (64 * UI);
   if (S > 8) return hipErrorInvalidValue;
@@ -371,7 +397,9 @@ static hipError_t gemv_dispatch(const uint32_t* codes, const uint32_t* meta, int
                                 int y_bf16, hipStream_t s) {
   if (B == 1) {
     if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s);
-    return gemv_b1_t<BITS, G, false, QG_B1_UI, QG_B1_RPW>(codes, meta, N, K, x, y, y_bf16, s);
+    const bool wide = QG_B1_UI ? QG_B1_UI >= 4 : (BITS == 4 || K > 16384);
+    if (wide) return gemv_b1_t<BITS, G, false, 4, QG_B1_RPW>(codes, meta, N, K, x, y, y_bf16, s);
+    return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW>(codes, meta, N, K, x, y, y_bf16, s);
   }
   if (x_dtype != 1) return hipErrorInvalidValue;
   return gemv_mfma_t<BITS, G>(codes, meta, N, K, static_cast<const uint16_t*>(x), B, y, y_bf16, s);

@@ -82,7 +82,8 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemv_group(odd, good, 64, 128, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EALIGN
     # unsupported: fp32 activations with B > 1, K beyond the register-resident limit
     assert lib.qgemv_group(good, good, 64, 128, 4, 32, good, cg.Q_F32, 2, good, cg.Q_F32, s) == cg.Q_EUNSUPPORTED
-    assert lib.qgemv_group(good, good, 64, 65536, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EUNSUPPORTED
+    assert lib.qgemv_group(good, good, 64, 131072, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EUNSUPPORTED
+    assert lib.qgemv_group(good, good, 64, 65536, 4, 32, good, cg.Q_F32, 1, good, cg.Q_F32, s) == cg.Q_EUNSUPPORTED
     # bad dtype
     assert lib.qgemv_group(good, good, 64, 128, 4, 32, good, 7, 1, good, cg.Q_F32, s) == cg.Q_EINVAL
     # packer: bad shape, alignment
