@@ -102,17 +102,45 @@ def main():
         n = max(2, int(args.pool_gib * (1 << 30) // nbytes) + 1)
         return [tuple(t.clone() for t in tensors) for _ in range(n)]
 
-    def time_launches(fn, steps, warmup):
-        """(wall seconds, event seconds) over `steps` launches after `warmup`."""
+    def capture(fn, idx):
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in idx:
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def time_launches(fn, steps, warmup, period=None):
+        """(wall seconds, event seconds) over exactly `steps` launches after `warmup`.
+
+        The launches are captured into a HIP graph of `period` steps (one per
+        rotating-pool copy) replayed steps // period times, plus a graph of
+        the remaining steps % period, so the host's per-call cost (Python
+        binding, two launches for the binary path) never starves the GPU;
+        every replayed kernel still streams its own copy.  Events are
+        recorded on the stream the kernels run on.
+        """
+        period = min(period or 1, steps)
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
+        g = capture(fn, range(period))
+        reps, rem = divmod(steps, period)
+        tail = capture(fn, range(rem)) if rem else None
         stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record(stream)
-        for i in range(steps):
-            fn(warmup + i)
+        for _ in range(reps):
+            g.replay()
+        if tail is not None:
+            tail.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -140,7 +168,7 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    wall, ev = time_launches(step, args.steps, args.warmup)
+    wall, ev = time_launches(step, args.steps, args.warmup, period=len(pool))
     value = nbytes * args.steps / wall / 1e9
     achieved = nbytes * args.steps / ev / 1e9
     log(f"headline: {wall / args.steps * 1e6:.2f} us/step wall, {ev / args.steps * 1e6:.2f} us/launch events, "
@@ -228,7 +256,7 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         def f(i):
             c, m = pool[i % len(pool)]
             cg.qgemv_group(c, m, N, K, bits, group, x, y=y)
-        wall, ev = time_launches(f, steps, warm)
+        wall, ev = time_launches(f, steps, warm, period=len(pool))
         gbs = nbytes * steps / ev / 1e9
         del pool
         torch.cuda.empty_cache()
@@ -276,7 +304,7 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         def f(i):
             a, b = pool[i % len(pool)]
             cg.qgemv_binlr(a, b, s1d, s2d, N, K, r, x, y=y, ws=ws)
-        wall, ev = time_launches(f, steps, warm)
+        wall, ev = time_launches(f, steps, warm, period=len(pool))
         gbs = nbytes * steps / ev / 1e9
         rows[f"binlr_gemv_{K}x{N}_r{r}_B1"] = {
             "us": round(ev / steps * 1e6, 3), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / 8000.0, 2),
@@ -304,7 +332,7 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
             if need:
                 ws = torch.empty(need, dtype=torch.uint8, device=dev)
             it = 5 if M == 4096 else 10
-            wall, ev = time_launches(lambda i: cg.qgemm_prefill(w, X, Y=Y, ws=ws), it, 2)
+            wall, ev = time_launches(lambda i: cg.qgemm_prefill(w, X, Y=Y, ws=ws), it, 2, period=1)
             tf = flops * it / ev / 1e12
             rows[f"prefill_{label}_M{M}"] = {"us": round(ev / it * 1e6, 1), "TFLOP/s": round(tf, 1),
                                              "mfma_util_vs_2.5PF": round(tf / 2500.0, 4)}

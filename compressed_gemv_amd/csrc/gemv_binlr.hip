@@ -133,20 +133,23 @@ __global__ __launch_bounds__(512) void bin_gemv_kernel(
         }
       }
     }
+    // pairs (v_j, v_16+j) pre-scaled by 2^-p (exact), split into bf16
+    // hi + lo with the hardware round-to-nearest conversion; the sums come
+    // out of v_dot2 against (1, 1) on the very operands the rows will use.
+    constexpr uint32_t kOnes = 0x3F803F80u;
     float c = 0.f, vs = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float sc = 1.0f / (float)(1 << bin_p(j));
       const float a = v[j] * sc, bb = v[16 + j] * sc;
-      const uint32_t ah = f32_to_bf16_rne(a), bh = f32_to_bf16_rne(bb);
-      const uint32_t al = f32_to_bf16_rne(a - bf16_bits_to_f32(ah));
-      const uint32_t bl = f32_to_bf16_rne(bb - bf16_bits_to_f32(bh));
-      xp[it][2 * j] = ah | (bh << 16);
-      xp[it][2 * j + 1] = al | (bl << 16);
-      c += (bf16_bits_to_f32(ah) + bf16_bits_to_f32(al)) + (bf16_bits_to_f32(bh) + bf16_bits_to_f32(bl));
+      const uint32_t hi = cvt_pk_bf16(a, bb);
+      const uint32_t lo = cvt_pk_bf16(a - bf16_lo_to_f32(hi), bb - bf16_hi_to_f32(hi));
+      xp[it][2 * j] = hi;
+      xp[it][2 * j + 1] = lo;
+      c = dot2_bf16(hi, kOnes, c);
+      c = dot2_bf16(lo, kOnes, c);
+      vs += v[j] + v[16 + j];
     }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) vs += v[i];
     negC[it] = -128.0f * c;
     vsum[it] = vs;
   }
@@ -190,13 +193,16 @@ __global__ __launch_bounds__(512) void bin_gemv_kernel(
   int st = 0;
   while (st + 2 < nst) {
     load(wb, stream + (st + 1) * step);
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(wa, stream + st * step, st * RPW);
     load(wa, stream + (st + 2) * step);
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(wb, stream + (st + 1) * step, (st + 1) * RPW);
     st += 2;
   }
   if (st + 1 < nst) {
     load(wb, stream + (st + 1) * step);
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(wa, stream + st * step, st * RPW);
     compute(wb, stream + (st + 1) * step, (st + 1) * RPW);
   } else if (st < nst) {
@@ -230,9 +236,11 @@ static hipError_t bin_gemv_t(const uint32_t* bits, int64_t R, int64_t Wn, int64_
   const int RS = S <= 4 ? 4 / S : 1;
   const int WSL = (Wv + S - 1) / S;
   const int threads = 64 * S * RS;
-  int64_t nstreams_wanted = kTargetWaves / S;
-  if (nstreams_wanted > R) nstreams_wanted = R;
-  int64_t blocks = (nstreams_wanted + RS - 1) / RS;
+  // rows per stream: a whole number of RPW-row stages, no decoded-but-idle rows
+  const int64_t streams_target = kTargetWaves / S;
+  const int64_t stages = (R + RPW * streams_target - 1) / (RPW * streams_target);
+  const int64_t rows_per_stream = RPW * stages;
+  int64_t blocks = ((R + rows_per_stream - 1) / rows_per_stream + RS - 1) / RS;
   if (blocks < 1) blocks = 1;
   const int64_t nstreams = blocks * RS;
   const int TMAX = (int)((R + nstreams - 1) / nstreams);

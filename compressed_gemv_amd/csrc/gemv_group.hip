@@ -27,14 +27,15 @@
 // Tile parameters of the B = 1 kernel.  UI = units per lane held in
 // registers (a K-slice covers 2048*UI inputs), RPW = rows per pipeline
 // stage, target waves per launch.  Measured on MI355X: 4-bit codes and long
-// rows (K > 16384) run best with UI = 4 and 1024 waves (one per SIMD, deep
-// per-wave streams); 2/3/5/6-bit with UI = 2 and 2048 waves (more waves to
-// cover their longer decode).  QG_B1_UI / QG_B1_WAVES force one choice.
+// rows (K > 16384) run best with UI = 4, one row per stage and 1024 waves
+// (one per SIMD, deep per-wave streams); 2/3/5/6-bit with UI = 2, two rows
+// per stage and 2048 waves (more waves to cover their longer decode).
+// QG_B1_UI / QG_B1_RPW / QG_B1_WAVES force one choice.
 #ifndef QG_B1_UI
 #define QG_B1_UI 0
 #endif
 #ifndef QG_B1_RPW
-#define QG_B1_RPW 2
+#define QG_B1_RPW 0       // 0 = by width: 1 row per stage with UI = 4, 2 with UI = 2
 #endif
 #ifndef QG_B1_WAVES
 #define QG_B1_WAVES 0
@@ -220,13 +221,16 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   int st = 0;
   while (st + 2 < nst) {
     load(wb, mb, stream + (st + 1) * step);
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(wa, ma, stream + st * step, st * RPW);
     load(wa, ma, stream + (st + 2) * step);
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(wb, mb, stream + (st + 1) * step, (st + 1) * RPW);
     st += 2;
   }
   if (st + 1 < nst) {
     load(wb, mb, stream + (st + 1) * step);
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(wa, ma, stream + st * step, st * RPW);
     compute(wb, mb, stream + (st + 1) * step, (st + 1) * RPW);
   } else if (st < nst) {
@@ -269,21 +273,23 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  struct Buf { u32x4_t xb[4]; uint32_t w[RT][BITS]; uint32_t m[RT]; bool uvalid; };
-  // Branch-free loads: a lane past B reads a valid activation row (its
-  // column is never stored); weights go through buffer resources (rows past
-  // N read 0 and are never stored; a unit past K reads 0 and its activations
-  // are zeroed at use).
+  struct Buf { u32x4_t xb[4]; uint32_t w[RT][BITS]; uint32_t m[RT]; };
+  // Branch-free loads through buffer resources.  Activations: a lane past B
+  // reads a valid activation row (its column is never stored), a unit past K
+  // gets an out-of-range offset and reads 0.  Weights: rows past N read 0
+  // and are never stored.
   const int bc = bcol < B ? bcol : B - 1;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)((size_t)B * K * 2));
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
   auto load = [&](Buf& b, int qi) {
     const int u0 = 4 * qi + kg;
-    b.uvalid = u0 < U;
-    const int u = b.uvalid ? u0 : 0;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)bc * K + (size_t)u * 32);
+    const uint32_t xo = u0 < U ? (uint32_t)((bc * K + u0 * 32) * 2) : 0xFFFFFF00u;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) b.xb[t] = src[t];
+    for (int t = 0; t < 4; ++t) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * t, 0, 0);
+      b.xb[t] = u32x4_t{v[0], v[1], v[2], v[3]};
+    }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const uint32_t row = (uint32_t)(row_base + 16 * t + r);
@@ -291,21 +297,37 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
       b.m[t] = buf_load_u32(mrs, (row * (uint32_t)GN + (uint32_t)((u0 * 32) / G)) * 4, 0u);
     }
   };
+  using UN = Unit<BITS>;
+  const uint32_t bias = opaque_bias();
   auto compute = [&](const Buf& b) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      float qf[32];
-      unit_codes_f32<BITS>(b.w[t], qf);
+      uint32_t pr[16];
+      decode_unit<BITS>(b.w[t], pr, bias);
+      // a pair lane reads 128 + q*2^p: w_hat = f * (s*2^-p) + (o - 128*s*2^-p)
       const float s = f16_bits_to_f32(b.m[t] & 0xFFFFu), o = f16_bits_to_f32(b.m[t] >> 16);
+      float sp[UN::NCLS], op[UN::NCLS];
+#pragma unroll
+      for (int c = 0; c < UN::NCLS; ++c) {
+        const float pc = BITS == 2 ? (float)(1 << (2 * c)) : (BITS == 3 ? (float)(1 << (3 * c)) : 1.0f);
+        sp[c] = s / pc;
+        op[c] = __builtin_fmaf(-128.0f, sp[c], o);
+      }
+      float wv[32];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const PairInfo pi = UN::pair(k);
+        const int c = UN::cls_of_p(pi.p);
+        wv[pi.ca] = __builtin_fmaf(bf16_lo_to_f32(pr[k]), sp[c], op[c]);
+        wv[pi.cb] = __builtin_fmaf(bf16_hi_to_f32(pr[k]), sp[c], op[c]);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x4_t a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          a[e] = cvt_pk_bf16(__builtin_fmaf(s, qf[8 * j + 2 * e], o), __builtin_fmaf(s, qf[8 * j + 2 * e + 1], o));
-        const u32x4_t xv = b.uvalid ? b.xb[j] : u32x4_t{0u, 0u, 0u, 0u};
+        for (int e = 0; e < 4; ++e) a[e] = cvt_pk_bf16(wv[8 * j + 2 * e], wv[8 * j + 2 * e + 1]);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                         __builtin_bit_cast(bf16x8_t, xv), acc[t], 0, 0, 0);
+                                                         __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
       }
     }
   };
@@ -317,13 +339,16 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   int it = 0;
   while (it + 2 < nit) {
     load(b1, wave + 4 * (it + 1));
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(b0);
     load(b0, wave + 4 * (it + 2));
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(b1);
     it += 2;
   }
   if (it + 1 < nit) {
     load(b1, wave + 4 * (it + 1));
+    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(b0);
     compute(b1);
   } else if (it < nit) {
@@ -360,9 +385,11 @@ static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t
   const int RS = S <= 4 ? 4 / S : 1;   // 256 threads, or 64*S (<= 512) for long rows
   const int USL = (U + S - 1) / S;
   const int threads = 64 * S * RS;
-  int64_t nstreams_wanted = kTargetWaves / S;
-  if (nstreams_wanted > N) nstreams_wanted = N;
-  int64_t blocks = (nstreams_wanted + RS - 1) / RS;
+  // rows per stream: a whole number of RPW-row stages
+  const int64_t streams_target = kTargetWaves / S;
+  const int64_t stages = (N + RPW * streams_target - 1) / (RPW * streams_target);
+  const int64_t rows_per_stream = RPW * stages;
+  int64_t blocks = ((N + rows_per_stream - 1) / rows_per_stream + RS - 1) / RS;
   if (blocks < 1) blocks = 1;
   const int64_t nstreams = blocks * RS;
   const int TMAX = (int)((N + nstreams - 1) / nstreams);
@@ -398,8 +425,8 @@ static hipError_t gemv_dispatch(const uint32_t* codes, const uint32_t* meta, int
   if (B == 1) {
     if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s);
     const bool wide = QG_B1_UI ? QG_B1_UI >= 4 : (BITS == 4 || K > 16384);
-    if (wide) return gemv_b1_t<BITS, G, false, 4, QG_B1_RPW>(codes, meta, N, K, x, y, y_bf16, s);
-    return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW>(codes, meta, N, K, x, y, y_bf16, s);
+    if (wide) return gemv_b1_t<BITS, G, false, 4, QG_B1_RPW ? QG_B1_RPW : 1>(codes, meta, N, K, x, y, y_bf16, s);
+    return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW ? QG_B1_RPW : 2>(codes, meta, N, K, x, y, y_bf16, s);
   }
   if (x_dtype != 1) return hipErrorInvalidValue;
   return gemv_mfma_t<BITS, G>(codes, meta, N, K, static_cast<const uint16_t*>(x), B, y, y_bf16, s);

@@ -94,6 +94,7 @@ def main():
     ap.add_argument("--sha", default="")
     ap.add_argument("--title", default="")
     ap.add_argument("--commands", default="", help="text block with the rocprofv3 commands")
+    ap.add_argument("--note", action="append", default=[], help="extra bullet lines for the summary")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
     lines = [f"# {a.title or a.kernel}", ""]
@@ -118,6 +119,8 @@ def main():
                   f"- traffic / algorithmic bytes: {s['traffic_bytes'] / s['alg_bytes']:.4f}"]
         if a.sha:
             lines.append(f"- kernel_source_sha: {a.sha}")
+    if a.note:
+        lines += ["", "## Notes", ""] + [f"- {n}" for n in a.note]
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))

@@ -1,0 +1,76 @@
+"""The hot-path entry points captured in a HIP graph give, on every replay,
+the same bits as eager calls (the benchmark times graph replays).  Between
+replays the program does its own eager work and synchronizes; the inputs are
+changed in place so each replay must read the current data."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, dev_bf16, say
+from workloads import gen_binlr, gen_weights, gen_x_bf16, rng_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture(fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def _check_replays(g, out, eager, xs, x_dev):
+    for i, xnew in enumerate(xs):
+        x_dev.copy_(xnew)                   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = eager()
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay {i} differs from the eager call"
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_graph_gemv_group(gpu, B):
+    say(f"graph gemv_group B={B}")
+    N, K = 1000, 4096
+    W = gen_weights(N, K, rng_for(80, B), outliers=True)
+    codes, meta = gpu.qpack_group(dev(W), 4, 64)
+    x = dev_bf16(gen_x_bf16(B, K, rng_for(81, 0)))
+    y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    g = _capture(lambda: gpu.qgemv_group(codes, meta, N, K, 4, 64, x, y=y))
+    xs = [dev_bf16(gen_x_bf16(B, K, rng_for(82, i))) for i in range(3)]
+    _check_replays(g, y, lambda: gpu.qgemv_group(codes, meta, N, K, 4, 64, x), xs, x)
+
+
+def test_graph_gemv_binlr(gpu):
+    say("graph gemv_binlr")
+    N, K, r = 700, 2048, 300
+    U, V, s1, s2 = gen_binlr(N, K, r, rng_for(83, 0))
+    ub, vb = gpu.qpack_binlr(dev(U), dev(V))
+    s1d, s2d = dev(s1.view(np.int16)), dev(s2.view(np.int16))
+    x = dev_bf16(gen_x_bf16(1, K, rng_for(84, 0)))
+    y = torch.empty((1, N), dtype=torch.float32, device=x.device)
+    ws = torch.empty(gpu.qbinlr_sizes(N, K, r, 1)[2], dtype=torch.uint8, device=x.device)
+    g = _capture(lambda: gpu.qgemv_binlr(ub, vb, s1d, s2d, N, K, r, x, y=y, ws=ws))
+    xs = [dev_bf16(gen_x_bf16(1, K, rng_for(85, i))) for i in range(3)]
+    _check_replays(g, y, lambda: gpu.qgemv_binlr(ub, vb, s1d, s2d, N, K, r, x), xs, x)
+
+
+def test_graph_prefill(gpu):
+    say("graph prefill")
+    M, N, K = 96, 300, 512
+    W = gen_weights(N, K, rng_for(86, 0), outliers=True)
+    codes, meta = gpu.qpack_group(dev(W), 4, 64)
+    w = gpu.make_qweight_group(codes, meta, N, K, 4, 64)
+    X = dev_bf16(gen_x_bf16(M, K, rng_for(87, 0)))
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    g = _capture(lambda: gpu.qgemm_prefill(w, X, Y=Y))
+    xs = [dev_bf16(gen_x_bf16(M, K, rng_for(88, i))) for i in range(3)]
+    _check_replays(g, Y, lambda: gpu.qgemm_prefill(w, X), xs, X)
