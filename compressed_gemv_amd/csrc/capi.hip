@@ -122,7 +122,7 @@ int qbinlr_sizes(int64_t N, int64_t K, int64_t r, int64_t B, size_t* ubits_bytes
     return Q_EUNSUPPORTED;
   if (ubits_bytes) *ubits_bytes = (size_t)(N * padded_words(r) * 4);
   if (vtbits_bytes) *vtbits_bytes = (size_t)(r * padded_words(K) * 4);
-  if (ws_bytes) *ws_bytes = (size_t)(B * padded_words(r) * 32 * 4);
+  if (ws_bytes) *ws_bytes = (size_t)(B * qg::binlr_ws_bytes_per_batch(r));
   return Q_OK;
 }
 
@@ -167,12 +167,9 @@ int qgemv_binlr(const void* ubits, const void* vtbits, const uint16_t* s1, const
   if (!aligned(ubits, 16) || !aligned(vtbits, 16) || !aligned(ws, 16) || !aligned(x, 4) ||
       !aligned(y, 4) || !aligned(s1, 2) || !aligned(s2, 2))
     return Q_EALIGN;
-  // each stage keeps a slice of its input vector in registers: at most
-  // 8 slices x 2 words x 64 lanes x 32 entries
-  if (K > 8 * 2 * 64 * 32 || r > 8 * 2 * 64 * 32) return Q_EUNSUPPORTED;
   return hip_status(qg::launch_gemv_binlr(
       static_cast<const uint32_t*>(ubits), static_cast<const uint32_t*>(vtbits), s1, s2, N, K, r,
-      x, x_dtype, B, y, y_dtype, static_cast<float*>(ws), stream));
+      x, x_dtype, B, y, y_dtype, ws, stream));
 }
 
 int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes) {

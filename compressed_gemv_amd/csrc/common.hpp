@@ -89,22 +89,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int B>
+template <int B, int AUX = kNT>
 __device__ __forceinline__ void buf_load_unit(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                               uint32_t (&w)[B]) {
   if constexpr (B == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
     w[0] = v[0]; w[1] = v[1];
   } else if constexpr (B == 3) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, kNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, AUX);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
   } else {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
     if constexpr (B == 5) {
-      w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 16, soff, kNT);
+      w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 16, soff, AUX);
     } else if constexpr (B == 6) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 16, soff, kNT);
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 16, soff, AUX);
       w[4] = t[0]; w[5] = t[1];
     }
   }
@@ -180,6 +180,50 @@ template <int B>
 __device__ __forceinline__ void decode_unit(const uint32_t (&w)[B], uint32_t (&pr)[16]) {
   decode_unit<B>(w, pr, kBias2);
 }
+
+// Second decode of the same unit, for kernels that dequantize with
+// v_fma_mix_f32: a field is masked into the mantissa of an fp16 with zero
+// exponent, i.e. the subnormal q*2^(p-24), with no bias to remove.  Fields
+// land at bit p <= 10 - b; a shift by S = b*floor(10/b) brings the upper
+// fields down.  Then fma(v, s*2^(24-p), o) = fl32(q*s + o) exactly, since
+// q*s has at most 17 significant bits.
+template <int B> struct UnitH {
+  static constexpr int F = 16 / B;
+  static constexpr int S = B * (10 / B);
+  static constexpr int kRegularPairs = F * B;
+  static constexpr int NCLS = (S - 1) / B + 1;     // landing bits 0, B, ..., < S
+  static constexpr int shift_of(int j) { return (B * j / S) * S; }
+  static constexpr int p_of(int j) { return B * j - shift_of(j); }
+  static constexpr PairInfo pair(int k) { return Unit<B>::pair(k); }
+  static constexpr int p_of_pair(int k) { return k < kRegularPairs ? p_of(k % F) : 0; }
+};
+
+template <int B>
+__device__ __forceinline__ void decode_unit_h(const uint32_t (&w)[B], uint32_t (&pr)[16]) {
+  using U = UnitH<B>;
+#pragma unroll
+  for (int k = 0; k < U::kRegularPairs; ++k) {
+    const int wi = k / U::F, j = k % U::F;
+    const uint32_t m = ((1u << B) - 1u) << U::p_of(j);
+    pr[k] = (w[wi] >> U::shift_of(j)) & (m | (m << 16));
+  }
+  if constexpr (B == 3 || B == 5) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < B; ++i) t |= (w[i] >> (15 - i)) & (0x00010001u << i);
+    pr[15] = t;
+  } else if constexpr (B == 6) {
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const uint32_t lo = (w[pp] >> 12) & 0x000F000Fu;
+      pr[12 + pp] = ((w[4 + pp / 2] >> (8 + 2 * (pp % 2))) & 0x00300030u) | lo;
+    }
+  }
+}
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
 
 // Codes of one unit as fp32 values q (exact), natural code order.
 template <int B>

@@ -2,273 +2,368 @@
 // VRAM...", section 1, NanoQuant formulation), read right to left:
 //   stage 1  t = V^T (s2 (.) x)       rows of VTbits, reduction over K
 //   stage 2  y = s1 (.) (U t)         rows of Ubits,  reduction over r
-// Both stages are one kernel: a +-1 row dotted with a vector v,
-//   sum_k (2 b_k - 1) v_k = 2 * sum_{b_k = 1} v_k - sum_k v_k.
-// A lane owns one 32-bit word (32 signs) per row.  Bit j of the low half and
-// bit j of the high half form a pair; one shift and one masked OR turn a
-// pair into a bf16x2 operand 128 + b*2^p (p = landing mantissa bit), so the
-// matching v is pre-scaled by 2^-p and the bias 128*v*2^-p is removed once
-// per word.  v (s2*x in stage 1, t in stage 2) is fp32 and is carried as
-// bf16 hi + lo halves (two v_dot2 per pair, 2^-16 relative residual).
+// Both stages are one kernel: 16-row tiles of +-1 rows times a vector v on
+// the matrix cores (v_mfma_f32_16x16x32_bf16), with
+//   sum_k (2 b_k - 1) v_k = 2 * sum_k b_k v_k - sum_k v_k.
+//
+// A operand (the signs): bit j and bit 16+j of a 32-bit word form a pair;
+// one masked OR into 0x4300 (bf16 128) turns it into the bf16x2
+// 128 + b*2^p, p the mantissa bit the pair lands on (words pre-shifted by 7
+// and 14 bring bits 7..15 down).  Exact in bf16.
+// B operand (the vector): v is split into bf16 hi + lo (2^-16 relative
+// residual), pre-scaled by 2^-p so every product b*2^p * v*2^-p is b*v, and
+// laid out in a table in the order the A lanes hold their bits.  Column 0 of
+// the 16 MFMA columns carries hi, column 1 lo (the others repeat them and
+// are ignored).  Then D = sum_k (128 + b_k 2^p_k)(hi_k + lo_k) 2^-p_k
+//                       = 128 C + sum_k b_k v~_k,  C = sum_k (hi_k + lo_k) 2^-p_k,
+// and the row result is 2 (D - 128 C) - V with V = sum_k v~_k.
+//
+// Table layout (4 bytes per vector entry, 2 KB per 512-entry K-step): the
+// 16-byte chunk ((s*16 + j)*2 + n)*4 + kg holds part n (0 hi, 1 lo) of the 8
+// entries e = 2*e2 + h at k = 512 s + 32 (4 kg + e2) + 16 h + j.
+//
+// Stage 1 builds its table in LDS from x and s2, one chunk of 8192 entries at
+// a time.  Its epilogue writes t already split and permuted into the stage-2
+// table in the workspace, with per-workgroup partial sums of C and V, so a
+// stage-2 workgroup only copies the table into LDS.
+//
+// Work split: a workgroup owns RT row tiles (16 RT rows) and NS waves that
+// split the 512-bit K-steps; each wave loads all of its sign words for a
+// table chunk up front, the table lands in LDS meanwhile, and the NS partial
+// sums meet in LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
-#ifndef QG_BIN_RPW
-#define QG_BIN_RPW 8   // rows per pipeline stage (each row is one 4-byte word per lane)
-#endif
-
 namespace qg {
 
-// word layout of a 32-sign word: pair j (0..15) = bits (j, 16+j)
+namespace {
+
+constexpr int kTK = 8192;                 // vector entries per LDS table chunk
+constexpr int kStepsPerChunk = kTK / 512; // 16 K-steps of 512 bits
+constexpr int kMaxNS = 16;
+
+// pair j of a word = bits (j, 16 + j); shift that brings it down, landing bit
 __device__ __forceinline__ constexpr int bin_shift(int j) { return j < 7 ? 0 : (j < 14 ? 7 : 14); }
 __device__ __forceinline__ constexpr int bin_p(int j) { return j - bin_shift(j); }
+__device__ __forceinline__ int bin_p_rt(int j) { return j < 7 ? j : (j < 14 ? j - 7 : j - 14); }
 
-// MODE 0: v = s2 * x (x bf16), output t (fp32)
-// MODE 1: v = s2 * x (x fp32), output t (fp32)
-// MODE 2: v = t (fp32), output y = s1 * dot (fp32 or bf16)
-template <int MODE, int UI, int RPW>
-__global__ __launch_bounds__(512) void bin_gemv_kernel(
+// byte offset of entry k, part n, in a table
+__device__ __forceinline__ uint32_t tab_off(int k, int n) {
+  const int kl = k & 511;
+  const int ent = ((((k >> 9) * 16 + (kl & 15)) * 2 + n) * 4) + ((kl >> 7) & 3);
+  return (uint32_t)ent * 16u + (uint32_t)(((kl >> 5) & 3) * 2 + ((kl >> 4) & 1)) * 2u;
+}
+
+struct Stage2Out {         // where stage 1 leaves the stage-2 table
+  uint16_t* tab;           // [B][steps2 * 2 KB / 2]
+  float* part;             // [B][nparts][2] partial (C, V)
+  int64_t tab_bstride;     // uint16 elements per batch row
+  int64_t part_bstride;    // floats per batch row
+};
+
+// MODE 0: v = s2 * x (x bf16) -> stage-2 table
+// MODE 1: v = s2 * x (x fp32) -> stage-2 table
+// MODE 2: v from the stage-2 table -> y = s1 * dot (fp32 or bf16)
+template <int MODE, int RT>
+__global__ __launch_bounds__(1024) void bin_mfma_kernel(
     const uint32_t* __restrict__ bits, int R, int Wn, int Lk, const void* __restrict__ vin,
     const uint16_t* __restrict__ vscale, const uint16_t* __restrict__ oscale,
-    void* __restrict__ out, int y_bf16, int S, int RS, int WSL, int TMAX, int64_t in_bstride,
-    int64_t out_bstride, int vec_ok) {
-  extern __shared__ float part[];
+    void* __restrict__ out, int y_bf16, int64_t in_bstride, int64_t out_bstride, int vec_ok,
+    Stage2Out s2o, int nparts) {
+  constexpr int SPW = 8 / RT;                       // max K-steps per wave and chunk
+  __shared__ u32x4_t tab[kStepsPerChunk * 16 * 2 * 4];   // 32 KB
+  __shared__ float red[kMaxNS][RT * 16];
+  __shared__ float sums[kMaxNS][2];
   const int lane = threadIdx.x & 63;
+  const int NS = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int sl = wave % S, rs = wave / S;
   const int b = blockIdx.y;
-  const int Wv = (Lk + 31) >> 5;   // words holding real entries
+  const int row_base = blockIdx.x * 16 * RT;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int steps = (Wn + 15) >> 4;                 // 512-bit steps per row
 
-  int widx[UI];
-#pragma unroll
-  for (int it = 0; it < UI; ++it) {
-    const int lw = it * 64 + lane;
-    const int wi = sl * WSL + lw;
-    widx[it] = ((lw < WSL) && (wi < Wv)) ? wi : -1;
-  }
-  const int nstreams = gridDim.x * RS;
-  const int stream = blockIdx.x * RS + rs;
-  uint32_t wa[RPW][UI], wb[RPW][UI];
-  // Sign words through a buffer resource: rows past R read 0 (never stored),
-  // lanes without a word have zero activations.
+  // Sign words through a buffer resource: rows past R and words past the
+  // buffer read 0; words past Lk meet zero table entries.
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(bits, (uint32_t)((size_t)R * Wn * 4));
-  uint32_t wvoff[UI];
+  uint32_t voff[RT];
 #pragma unroll
-  for (int it = 0; it < UI; ++it) wvoff[it] = (uint32_t)(sl * WSL + it * 64 + lane) * 4;
-  const uint32_t wrow = (uint32_t)Wn * 4;
-  auto load = [&](uint32_t (&w)[RPW][UI], int row0) {
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const uint32_t row = (uint32_t)(row0 + r * nstreams);
-#pragma unroll
-      for (int it = 0; it < UI; ++it) w[r][it] = buf_load_u32(brs, wvoff[it], row * wrow);
-    }
-  };
-  const int step = RPW * nstreams;
-  const int nst = stream < R ? (R - stream + step - 1) / step : 0;
+  for (int t = 0; t < RT; ++t) voff[t] = ((uint32_t)(row_base + 16 * t + r16) * (uint32_t)Wn + 4u * kg) * 4u;
 
-  // vector: clamped unconditional loads before the first weight stage
-  constexpr int XW = MODE == 0 ? 4 : 8;
-  u32x4_t vraw[UI][XW], sraw[UI][4];
-  const bool vec_tile = vec_ok && (Lk % 32 == 0);
-  if (vec_tile) {
+  f32x4_t acc[RT];
 #pragma unroll
-    for (int it = 0; it < UI; ++it) {
-      const int k0 = (widx[it] >= 0 ? widx[it] : 0) * 32;
-      const u32x4_t* src = MODE == 0
-          ? reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(vin) + in_bstride * b + k0)
-          : reinterpret_cast<const u32x4_t*>(static_cast<const float*>(vin) + in_bstride * b + k0);
-#pragma unroll
-      for (int i = 0; i < XW; ++i) vraw[it][i] = src[i];
-      if constexpr (MODE != 2) {
-        const u32x4_t* sp = reinterpret_cast<const u32x4_t*>(vscale + k0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sraw[it][i] = sp[i];
-      }
-    }
-  }
-  if (nst > 0) load(wa, stream);
-
-  uint32_t xp[UI][32];
-  float negC[UI], vsum[UI];
-#pragma unroll
-  for (int it = 0; it < UI; ++it) {
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = 0.f;
-    const int wi = widx[it];
-    if (vec_tile) {
-      const bool ok = wi >= 0;
-#pragma unroll
-      for (int i = 0; i < XW; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (MODE == 0) {
-            v[8 * i + 2 * j] = ok ? bf16_lo_to_f32(vraw[it][i][j]) : 0.f;
-            v[8 * i + 2 * j + 1] = ok ? bf16_hi_to_f32(vraw[it][i][j]) : 0.f;
-          } else {
-            v[4 * i + j] = ok ? __uint_as_float(vraw[it][i][j]) : 0.f;
-          }
-        }
-      if constexpr (MODE != 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[8 * i + 2 * j] *= f16_bits_to_f32(sraw[it][i][j] & 0xFFFFu);
-            v[8 * i + 2 * j + 1] *= f16_bits_to_f32(sraw[it][i][j] >> 16);
-          }
-      }
-    } else if (wi >= 0) {
-      const int k0 = wi * 32;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int k = k0 + i;
-        if (k < Lk) {
-          float xv;
-          if constexpr (MODE == 0) xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k]);
-          else xv = static_cast<const float*>(vin)[in_bstride * b + k];
-          if constexpr (MODE != 2) xv *= f16_bits_to_f32(vscale[k]);
-          v[i] = xv;
-        }
-      }
-    }
-    // pairs (v_j, v_16+j) pre-scaled by 2^-p (exact), split into bf16
-    // hi + lo with the hardware round-to-nearest conversion; the sums come
-    // out of v_dot2 against (1, 1) on the very operands the rows will use.
-    constexpr uint32_t kOnes = 0x3F803F80u;
-    float c = 0.f, vs = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float sc = 1.0f / (float)(1 << bin_p(j));
-      const float a = v[j] * sc, bb = v[16 + j] * sc;
-      const uint32_t hi = cvt_pk_bf16(a, bb);
-      const uint32_t lo = cvt_pk_bf16(a - bf16_lo_to_f32(hi), bb - bf16_hi_to_f32(hi));
-      xp[it][2 * j] = hi;
-      xp[it][2 * j + 1] = lo;
-      c = dot2_bf16(hi, kOnes, c);
-      c = dot2_bf16(lo, kOnes, c);
-      vs += v[j] + v[16 + j];
-    }
-    negC[it] = -128.0f * c;
-    vsum[it] = vs;
-  }
-
-  auto emit = [&](int row, float total) {
-    if constexpr (MODE == 2) {
-      const float yv = total * f16_bits_to_f32(oscale[row]);
-      if (y_bf16) static_cast<uint16_t*>(out)[out_bstride * b + row] = (uint16_t)f32_to_bf16_rne(yv);
-      else static_cast<float*>(out)[out_bstride * b + row] = yv;
-    } else {
-      static_cast<float*>(out)[out_bstride * b + row] = total;
-    }
-  };
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float csum = 0.f, vsum = 0.f;                     // this thread's share of C and V
   const uint32_t bias = opaque_bias();
-  auto compute = [&](const uint32_t (&w)[RPW][UI], int row0, int m0) {
+
+  for (int c0 = 0; c0 < steps; c0 += kStepsPerChunk) {
+    const int cs = min(kStepsPerChunk, steps - c0);
+    // this wave's steps of the chunk: c0 + wave, c0 + wave + NS, ...
+    const int my = wave < cs ? (cs - wave + NS - 1) / NS : 0;
+    u32x4_t w[SPW][RT];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      float acc = 0.f;
+    for (int i = 0; i < SPW; ++i) {
+      if (i < my) {
+        const uint32_t soff = (uint32_t)(c0 + wave + i * NS) * 64u;   // 16 words per step
 #pragma unroll
-      for (int it = 0; it < UI; ++it) {
-        float a = negC[it];
-        const uint32_t ww = w[r][it];
+        for (int t = 0; t < RT; ++t) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, voff[t] + soff, 0, kNT);
+          w[i][t] = u32x4_t{v[0], v[1], v[2], v[3]};
+        }
+      }
+    }
+    if constexpr (MODE == 2) {
+      // copy this chunk of the stage-2 table
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(s2o.tab + s2o.tab_bstride * b) + c0 * 128;
+      for (int i = threadIdx.x; i < cs * 128; i += blockDim.x) tab[i] = src[i];
+    } else {
+      // build the chunk from x and s2: a thread takes groups of 8 consecutive
+      // entries (16-byte loads), two groups' loads in flight at a time
+      const int ngr = cs * 64;
+      for (int g0 = threadIdx.x; g0 < ngr; g0 += 2 * blockDim.x) {
+        float v[2][8];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int g = g0 + q * blockDim.x;
+          const int k = (c0 * 64 + g) * 8;
+          if (vec_ok && g < ngr && k + 8 <= Lk) {
+            const u32x4_t sc = *reinterpret_cast<const u32x4_t*>(vscale + k);
+            if constexpr (MODE == 0) {
+              const u32x4_t a = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(vin) + in_bstride * b + k);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v[q][2 * e] = bf16_lo_to_f32(a[e]) * f16_bits_to_f32(sc[e] & 0xFFFFu);
+                v[q][2 * e + 1] = bf16_hi_to_f32(a[e]) * f16_bits_to_f32(sc[e] >> 16);
+              }
+            } else {
+              const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(vin) + in_bstride * b + k);
+              const u32x4_t a0 = src[0], a1 = src[1];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t xw = e < 4 ? a0[e] : a1[e - 4];
+                const uint32_t sh = (e & 1) ? (sc[e / 2] >> 16) : (sc[e / 2] & 0xFFFFu);
+                v[q][e] = __uint_as_float(xw) * f16_bits_to_f32(sh);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float xv = 0.f;
+              if (g < ngr && k + e < Lk) {
+                if constexpr (MODE == 0) {
+                  xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k + e]);
+                } else {
+                  xv = static_cast<const float*>(vin)[in_bstride * b + k + e];
+                }
+                xv *= f16_bits_to_f32(vscale[k + e]);
+              }
+              v[q][e] = xv;
+            }
+          }
+        }
+        uint16_t* t16 = reinterpret_cast<uint16_t*>(tab);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int g = g0 + q * blockDim.x;
+          if (g < ngr) {
+            const int odd = g & 1;
+            const int ep = ((g >> 2) & 3) * 2 + ((g >> 1) & 1);
+            const int ent0 = (g >> 6) * 16 * 8 + ((g >> 4) & 3);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              // pair j = 8 odd + e (kl & 15) lands on bit j, j - 7 or j - 14
+              const int p0 = odd ? (e < 6 ? e + 1 : e - 6) : e;
+              const int p1 = odd ? (e + 1 < 6 ? e + 2 : e - 5) : (e + 1 < 7 ? e + 1 : 0);
+              const float a0 = v[q][e] * __builtin_ldexpf(1.0f, -p0);     // exact
+              const float a1 = v[q][e + 1] * __builtin_ldexpf(1.0f, -p1);
+              const uint32_t hi = cvt_pk_bf16(a0, a1);
+              const float h0 = bf16_lo_to_f32(hi), h1 = bf16_hi_to_f32(hi);
+              const uint32_t lo = cvt_pk_bf16(a0 - h0, a1 - h1);
+              const float l0 = bf16_lo_to_f32(lo), l1 = bf16_hi_to_f32(lo);
+              const int j0 = 8 * odd + e;
+              t16[(ent0 + j0 * 8) * 8 + ep] = (uint16_t)(hi & 0xFFFFu);
+              t16[(ent0 + j0 * 8 + 4) * 8 + ep] = (uint16_t)(lo & 0xFFFFu);
+              t16[(ent0 + (j0 + 1) * 8) * 8 + ep] = (uint16_t)(hi >> 16);
+              t16[(ent0 + (j0 + 1) * 8 + 4) * 8 + ep] = (uint16_t)(lo >> 16);
+              const float s0 = h0 + l0, s1 = h1 + l1;
+              csum += s0 + s1;
+              vsum = __builtin_fmaf(s0, __builtin_ldexpf(1.0f, p0), vsum);
+              vsum = __builtin_fmaf(s1, __builtin_ldexpf(1.0f, p1), vsum);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int n1 = r16 & 1;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      if (i < my) {
+        const int sl = wave + i * NS;                 // step within the chunk
+        u32x4_t w7[RT], w14[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) { w7[t] = w[i][t] >> 7u; w14[t] = w[i][t] >> 14u; }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
+          const u32x4_t frag = tab[((sl * 16 + j) * 2 + n1) * 4 + kg];
           const uint32_t m = 0x00010001u << bin_p(j);
-          const uint32_t pr = ((ww >> bin_shift(j)) & m) | bias;
-          a = dot2_bf16(pr, xp[it][2 * j], a);
-          a = dot2_bf16(pr, xp[it][2 * j + 1], a);
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            const u32x4_t& src = bin_shift(j) == 0 ? w[i][t] : (bin_shift(j) == 7 ? w7[t] : w14[t]);
+            u32x4_t a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = (src[e] & m) | bias;
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                             __builtin_bit_cast(bf16x8_t, frag), acc[t], 0, 0, 0);
+          }
         }
-        acc += 2.0f * a - vsum[it];
-      }
-      const float total = wave_sum(acc);
-      const int row = row0 + r * nstreams;
-      if (row < R && lane == 0) {
-        if (S == 1) emit(row, total);
-        else part[((size_t)rs * TMAX + (m0 + r)) * S + sl] = total;
       }
     }
-  };
+    __syncthreads();   // the next chunk overwrites the table
+  }
 
-  int st = 0;
-  while (st + 2 < nst) {
-    load(wb, stream + (st + 1) * step);
-    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(wa, stream + st * step, st * RPW);
-    load(wa, stream + (st + 2) * step);
-    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(wb, stream + (st + 1) * step, (st + 1) * RPW);
-    st += 2;
+  // C and V of the whole vector (every workgroup has the same sums)
+  if constexpr (MODE == 2) {
+    const float* pp = s2o.part + s2o.part_bstride * b;
+    for (int i = threadIdx.x; i < nparts; i += blockDim.x) { csum += pp[2 * i]; vsum += pp[2 * i + 1]; }
   }
-  if (st + 1 < nst) {
-    load(wb, stream + (st + 1) * step);
-    __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(wa, stream + st * step, st * RPW);
-    compute(wb, stream + (st + 1) * step, (st + 1) * RPW);
-  } else if (st < nst) {
-    compute(wa, stream + st * step, st * RPW);
-  }
-  if (S > 1) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < RS * TMAX; idx += blockDim.x) {
-      const int rs_ = idx / TMAX, m = idx % TMAX;
-      const int row = blockIdx.x * RS + rs_ + m * nstreams;
-      if (row < R) {
-        float t = 0.f;
-        for (int j = 0; j < S; ++j) t += part[(size_t)idx * S + j];
-        emit(row, t);
+  csum = wave_sum(csum);
+  vsum = wave_sum(vsum);
+  if (lane == 0) { sums[wave][0] = csum; sums[wave][1] = vsum; }
+  // lane (n, kg) holds D[4 kg + i][n]; hi (n = 0) + lo (n = 1) -> lane n = 0
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float d = acc[t][i] + dpp_f32<0x101>(acc[t][i]);   // row_shl:1 (lane l+1)
+      if (r16 == 0) red[wave][t * 16 + 4 * kg + i] = d;
+    }
+  __syncthreads();
+  if (wave == 0) {
+    float dot = 0.f;
+    const int row = row_base + lane;
+    if (lane < 16 * RT) {
+      float C = 0.f, V = 0.f, D = 0.f;
+      for (int w2 = 0; w2 < NS; ++w2) { C += sums[w2][0]; V += sums[w2][1]; D += red[w2][lane]; }
+      dot = 2.0f * (D - 128.0f * C) - V;
+    }
+    if constexpr (MODE == 2) {
+      if (lane < 16 * RT && row < R) {
+        const float yv = dot * f16_bits_to_f32(oscale[row]);
+        if (y_bf16) static_cast<uint16_t*>(out)[out_bstride * b + row] = (uint16_t)f32_to_bf16_rne(yv);
+        else static_cast<float*>(out)[out_bstride * b + row] = yv;
+      }
+    } else {
+      // t_row -> stage-2 table entry `row`, plus this workgroup's share of
+      // the stage-2 C and V; entries past R up to the end of the table's
+      // last K-step are zero
+      float cpart = 0.f, vpart = 0.f;
+      uint16_t* t2 = s2o.tab + s2o.tab_bstride * b;
+      const int kend = (R + 511) & ~511;
+      if (lane < 16 * RT) {
+        const int p = bin_p_rt(row & 15);
+        const float a = (row < R ? dot : 0.f) * __builtin_ldexpf(1.0f, -p);
+        const uint32_t hi = cvt_pk_bf16(a, 0.f);
+        const float hf = bf16_lo_to_f32(hi);
+        const uint32_t lo = cvt_pk_bf16(a - hf, 0.f);
+        const float lf = bf16_lo_to_f32(lo);
+        if (row < kend) {
+          t2[tab_off(row, 0) / 2] = (uint16_t)(hi & 0xFFFFu);
+          t2[tab_off(row, 1) / 2] = (uint16_t)(lo & 0xFFFFu);
+        }
+        cpart = hf + lf;
+        vpart = (hf + lf) * __builtin_ldexpf(1.0f, p);
+      }
+      cpart = wave_sum(cpart);
+      vpart = wave_sum(vpart);
+      if (lane == 0) {
+        s2o.part[s2o.part_bstride * b + 2 * blockIdx.x] = cpart;
+        s2o.part[s2o.part_bstride * b + 2 * blockIdx.x + 1] = vpart;
+      }
+      if (blockIdx.x == gridDim.x - 1) {
+        for (int k = row_base + 16 * RT + lane; k < kend; k += 64) {
+          t2[tab_off(k, 0) / 2] = 0;
+          t2[tab_off(k, 1) / 2] = 0;
+        }
       }
     }
   }
 }
 
-template <int MODE>
-static hipError_t bin_gemv_t(const uint32_t* bits, int64_t R, int64_t Wn, int64_t Lk,
-                             const void* vin, const uint16_t* vscale, const uint16_t* oscale,
-                             void* out, int y_bf16, int64_t B, int64_t in_bstride,
-                             int64_t out_bstride, hipStream_t s) {
-  constexpr int UI = 2, RPW = QG_BIN_RPW;
-  constexpr int64_t kTargetWaves = 2048;
-  const int Wv = (int)((Lk + 31) / 32);
-  int S = (Wv + 64 * UI - 1) / (64 * UI);
-  if (S > 8) return hipErrorInvalidValue;
-  while (S < 4 && R * S < kTargetWaves && (Wv + 2 * S - 1) / (2 * S) >= 64) S *= 2;
-  const int RS = S <= 4 ? 4 / S : 1;
-  const int WSL = (Wv + S - 1) / S;
-  const int threads = 64 * S * RS;
-  // rows per stream: a whole number of RPW-row stages, no decoded-but-idle rows
-  const int64_t streams_target = kTargetWaves / S;
-  const int64_t stages = (R + RPW * streams_target - 1) / (RPW * streams_target);
-  const int64_t rows_per_stream = RPW * stages;
-  int64_t blocks = ((R + rows_per_stream - 1) / rows_per_stream + RS - 1) / RS;
-  if (blocks < 1) blocks = 1;
-  const int64_t nstreams = blocks * RS;
-  const int TMAX = (int)((R + nstreams - 1) / nstreams);
-  const size_t lds = S > 1 ? (size_t)RS * TMAX * S * sizeof(float) : 0;
-  if (lds > 64 * 1024) return hipErrorInvalidValue;
+// waves per workgroup: enough for ~2048 waves in all, each with at most
+// 8 / RT steps per chunk, never more waves than steps
+int64_t pick_ns(int64_t blocks, int64_t Wn, int rt) {
+  const int64_t steps = (Wn + 15) / 16;
+  const int64_t chunk_steps = steps < kStepsPerChunk ? steps : kStepsPerChunk;
+  int64_t ns = 1;
+  while (ns < kMaxNS && ns < chunk_steps && blocks * ns < 2048) ns *= 2;
+  while ((chunk_steps + ns - 1) / ns > 8 / rt && ns < kMaxNS) ns *= 2;
+  return (chunk_steps + ns - 1) / ns > 8 / rt ? -1 : ns;
+}
+
+template <int MODE, int RT>
+hipError_t bin_launch(const uint32_t* bits, int64_t R, int64_t Wn, int64_t Lk, const void* vin,
+                      const uint16_t* vscale, const uint16_t* oscale, void* out, int y_bf16,
+                      int64_t B, int64_t in_bstride, int64_t out_bstride, Stage2Out s2o,
+                      int nparts, hipStream_t s) {
+  const int64_t blocks = (R + 16 * RT - 1) / (16 * RT);
+  const int64_t ns = pick_ns(blocks, Wn, RT);
+  if (ns < 0) return hipErrorInvalidValue;
+  // 16-byte vector reads of the input vector and s2 need 16-byte aligned rows
   const size_t esz = MODE == 0 ? 2 : 4;
-  const int vec_ok = ((reinterpret_cast<uintptr_t>(vin) % 16) == 0 && ((in_bstride * esz) % 16) == 0 &&
-                      (MODE == 2 || (reinterpret_cast<uintptr_t>(vscale) % 16) == 0)) ? 1 : 0;
-  hipLaunchKernelGGL((bin_gemv_kernel<MODE, UI, RPW>), dim3((unsigned)blocks, (unsigned)B),
-                     dim3(threads), lds, s, bits, (int)R, (int)Wn, (int)Lk, vin, vscale, oscale,
-                     out, y_bf16, S, RS, WSL, TMAX, in_bstride, out_bstride, vec_ok);
+  const int vec_ok = MODE == 2 || ((reinterpret_cast<uintptr_t>(vin) % 16 == 0) && ((in_bstride * esz) % 16 == 0) &&
+                                   reinterpret_cast<uintptr_t>(vscale) % 16 == 0);
+  hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT>), dim3((unsigned)blocks, (unsigned)B), dim3((unsigned)(64 * ns)),
+                     0, s, bits, (int)R, (int)Wn, (int)Lk, vin, vscale, oscale, out, y_bf16,
+                     in_bstride, out_bstride, vec_ok, s2o, nparts);
   return hipGetLastError();
 }
 
-static int64_t pw(int64_t n) { return ((n + 31) / 32 + 3) / 4 * 4; }
+// row tiles per workgroup: 2 when there are >= 512 tiles to share the table
+// over, else 1 (short matrices need the workgroups spread over the CUs)
+int pick_rt(int64_t R) { return (R + 15) / 16 >= 512 ? 2 : 1; }
+
+template <int MODE>
+hipError_t bin_gemv_t(const uint32_t* bits, int64_t R, int64_t Wn, int64_t Lk, const void* vin,
+                      const uint16_t* vscale, const uint16_t* oscale, void* out, int y_bf16,
+                      int64_t B, int64_t in_bstride, int64_t out_bstride, Stage2Out s2o,
+                      int nparts, hipStream_t s) {
+  if (pick_rt(R) == 2)
+    return bin_launch<MODE, 2>(bits, R, Wn, Lk, vin, vscale, oscale, out, y_bf16, B, in_bstride, out_bstride,
+                               s2o, nparts, s);
+  return bin_launch<MODE, 1>(bits, R, Wn, Lk, vin, vscale, oscale, out, y_bf16, B, in_bstride, out_bstride,
+                             s2o, nparts, s);
+}
+
+int64_t pw(int64_t n) { return ((n + 31) / 32 + 3) / 4 * 4; }
+
+}  // namespace
+
+int64_t binlr_ws_bytes_per_batch(int64_t r) {
+  // stage-2 table (4 bytes per entry, whole 512-entry steps) + (C, V) partials
+  // of at most one stage-1 workgroup per 16 rows of V^T
+  const int64_t tab = (r + 511) / 512 * 2048;
+  const int64_t part = ((r + 15) / 16) * 8;
+  return (tab + part + 15) / 16 * 16;
+}
 
 hipError_t launch_gemv_binlr(const uint32_t* ubits, const uint32_t* vtbits,
                              const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
                              int64_t r, const void* x, int x_dtype, int64_t B, void* y,
-                             int y_dtype, float* t_ws, hipStream_t s) {
-  const int64_t rp = pw(r) * 32;   // workspace row stride of t
+                             int y_dtype, void* ws, hipStream_t s) {
+  const int64_t wsb = binlr_ws_bytes_per_batch(r);
+  Stage2Out o;
+  o.tab = static_cast<uint16_t*>(ws);
+  o.part = reinterpret_cast<float*>(static_cast<char*>(ws) + (r + 511) / 512 * 2048);
+  o.tab_bstride = wsb / 2;
+  o.part_bstride = wsb / 4;
+  const int nparts = (int)((r + 16 * pick_rt(r) - 1) / (16 * pick_rt(r)));
   hipError_t e;
   if (x_dtype == 1)
-    e = bin_gemv_t<0>(vtbits, r, pw(K), K, x, s2, nullptr, t_ws, 0, B, K, rp, s);
+    e = bin_gemv_t<0>(vtbits, r, pw(K), K, x, s2, nullptr, nullptr, 0, B, K, 0, o, 0, s);
   else
-    e = bin_gemv_t<1>(vtbits, r, pw(K), K, x, s2, nullptr, t_ws, 0, B, K, rp, s);
+    e = bin_gemv_t<1>(vtbits, r, pw(K), K, x, s2, nullptr, nullptr, 0, B, K, 0, o, 0, s);
   if (e != hipSuccess) return e;
-  return bin_gemv_t<2>(ubits, N, pw(r), r, t_ws, nullptr, s1, y, y_dtype == 1, B, rp, N, s);
+  return bin_gemv_t<2>(ubits, N, pw(r), r, nullptr, nullptr, s1, y, y_dtype == 1, B, 0, N, o, nparts, s);
 }
 
 }  // namespace qg

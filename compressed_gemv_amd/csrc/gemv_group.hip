@@ -17,8 +17,9 @@
 //    exact in bf16, so the only roundings are fp32 accumulations.  Long rows
 //    are split into up to 4 K-slices, one per wave of a workgroup, combined in
 //    LDS.  fp32 activations are split into bf16 hi + lo halves (two dot2).
-//  * 2 <= B <= 16 (MFMA): a wave owns a 16-row tile; each lane decodes one
-//    unit per K-step to fp32 w_hat = s*q + o, rounds to bf16 and feeds
+//  * 2 <= B <= 16 (MFMA): a wave owns RT 16-row tiles; each lane decodes
+//    one unit per tile and K-step to fp32 w_hat = s*q + o (one v_fma_mix_f32
+//    per weight from an fp16-subnormal decode), rounds to bf16 and feeds
 //    v_mfma_f32_16x16x32_bf16 with the activations (bf16) as the 16-column
 //    operand, fp32 accumulation.
 #include "common.hpp"
@@ -252,17 +253,20 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 }
 
 // --------------------------------------------------------------- B = 2..16
-// A workgroup owns RT 16-row tiles; its 4 waves split K (wave w takes unit
-// quads w, w+4, ...), so the activation fragments a wave loads are reused by
-// RT tiles.  Lane (r, kg) = (lane % 16, lane / 16) decodes unit 4*q + kg of
-// row r of every tile; the 4 lane groups therefore cover 4 consecutive units
-// (128 inputs) per MFMA quad, and the activation lane (b, kg) loads the
-// matching 8-wide slices of x[b].  Partial sums of the 4 waves meet in LDS.
-template <int BITS, int G, int RT>
-__global__ __launch_bounds__(256) void gemv_mfma_kernel(
+// A workgroup owns RT 16-row tiles; its WPB waves split K (wave w takes unit
+// quads w, w+WPB, ...), so the activation fragments a wave loads are reused
+// by RT tiles.  Lane (r, kg) = (lane % 16, lane / 16) decodes unit 4*q + kg
+// of row r of every tile; the 4 lane groups therefore cover 4 consecutive
+// units (128 inputs) per MFMA quad, and the activation lane (b, kg) loads the
+// matching 8-wide slices of x[b].  Dequantization: each code is decoded as
+// the fp16 subnormal q*2^(p-24) (common.hpp, UnitH), and one v_fma_mix_f32
+// per weight gives fl32(s*q + o), rounded to bf16 for the MFMA.  Partial
+// sums of the WPB waves meet in LDS.
+template <int BITS, int G, int RT, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
     const uint16_t* __restrict__ x, int B, void* __restrict__ yout, int y_bf16) {
-  __shared__ float red[4][RT * 4][64];
+  __shared__ float red[WPB][RT * 4][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row_base = blockIdx.x * (16 * RT);
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   // Branch-free loads through buffer resources.  Activations: a lane past B
   // reads a valid activation row (its column is never stored), a unit past K
   // gets an out-of-range offset and reads 0.  Weights: rows past N read 0
-  // and are never stored.
+  // and are never stored; a unit past K meets a zero activation.
   const int bc = bcol < B ? bcol : B - 1;
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)((size_t)B * K * 2));
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
@@ -290,36 +294,33 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * t, 0, 0);
       b.xb[t] = u32x4_t{v[0], v[1], v[2], v[3]};
     }
+    // Default cache policy: the other half of each 128-byte code line and the
+    // group constants (one dword serves up to 16 K-steps) are read again
+    // shortly after, by this or a neighbouring wave.
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const uint32_t row = (uint32_t)(row_base + 16 * t + r);
-      buf_load_unit<BITS>(crs, (row * (uint32_t)U + (uint32_t)u0) * (BITS * 4), 0u, b.w[t]);
-      b.m[t] = buf_load_u32(mrs, (row * (uint32_t)GN + (uint32_t)((u0 * 32) / G)) * 4, 0u);
+      buf_load_unit<BITS, 0>(crs, (row * (uint32_t)U + (uint32_t)u0) * (BITS * 4), 0u, b.w[t]);
+      b.m[t] = __builtin_amdgcn_raw_buffer_load_b32(mrs, (row * (uint32_t)GN + (uint32_t)((u0 * 32) / G)) * 4, 0u, 0);
     }
   };
-  using UN = Unit<BITS>;
-  const uint32_t bias = opaque_bias();
+  using UN = UnitH<BITS>;
   auto compute = [&](const Buf& b) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       uint32_t pr[16];
-      decode_unit<BITS>(b.w[t], pr, bias);
-      // a pair lane reads 128 + q*2^p: w_hat = f * (s*2^-p) + (o - 128*s*2^-p)
+      decode_unit_h<BITS>(b.w[t], pr);
       const float s = f16_bits_to_f32(b.m[t] & 0xFFFFu), o = f16_bits_to_f32(b.m[t] >> 16);
-      float sp[UN::NCLS], op[UN::NCLS];
+      float sp[UN::NCLS];
 #pragma unroll
-      for (int c = 0; c < UN::NCLS; ++c) {
-        const float pc = BITS == 2 ? (float)(1 << (2 * c)) : (BITS == 3 ? (float)(1 << (3 * c)) : 1.0f);
-        sp[c] = s / pc;
-        op[c] = __builtin_fmaf(-128.0f, sp[c], o);
-      }
+      for (int c = 0; c < UN::NCLS; ++c) sp[c] = s * (float)(1 << (24 - BITS * c));
       float wv[32];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const PairInfo pi = UN::pair(k);
-        const int c = UN::cls_of_p(pi.p);
-        wv[pi.ca] = __builtin_fmaf(bf16_lo_to_f32(pr[k]), sp[c], op[c]);
-        wv[pi.cb] = __builtin_fmaf(bf16_hi_to_f32(pr[k]), sp[c], op[c]);
+        const int c = UN::p_of_pair(k) / BITS;
+        wv[pi.ca] = __builtin_fmaf(f16_lo(pr[k]), sp[c], o);
+        wv[pi.cb] = __builtin_fmaf(f16_hi(pr[k]), sp[c], o);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -333,21 +334,21 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   };
 
   const int nq = (U + 3) >> 2;
-  const int nit = wave < nq ? (nq - wave + 3) / 4 : 0;   // quads of this wave
+  const int nit = wave < nq ? (nq - wave + WPB - 1) / WPB : 0;   // quads of this wave
   Buf b0, b1;
   if (nit > 0) load(b0, wave);
   int it = 0;
   while (it + 2 < nit) {
-    load(b1, wave + 4 * (it + 1));
+    load(b1, wave + WPB * (it + 1));
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(b0);
-    load(b0, wave + 4 * (it + 2));
+    load(b0, wave + WPB * (it + 2));
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(b1);
     it += 2;
   }
   if (it + 1 < nit) {
-    load(b1, wave + 4 * (it + 1));
+    load(b1, wave + WPB * (it + 1));
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
     compute(b0);
     compute(b1);
@@ -360,9 +361,11 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
     for (int i = 0; i < 4; ++i) red[wave][t * 4 + i][lane] = acc[t][i];
   __syncthreads();
   // lane holds D[4*kg + i][bcol] of each tile: row 16t + 4kg + i, batch bcol
-  for (int v = threadIdx.x; v < RT * 4 * 64; v += 256) {
+  for (int v = threadIdx.x; v < RT * 4 * 64; v += 64 * WPB) {
     const int ti = v / 64, ln = v % 64;
-    const float sum = (red[0][ti][ln] + red[1][ti][ln]) + (red[2][ti][ln] + red[3][ti][ln]);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) sum += red[w][ti][ln];
     const int t = ti / 4, i = ti % 4;
     const int b = ln & 15, row = row_base + 16 * t + 4 * (ln >> 4) + i;
     if (b < B && row < N) {
@@ -401,21 +404,36 @@ static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t
   return hipGetLastError();
 }
 
+template <int BITS, int G, int RT, int WPB>
+static hipError_t gemv_mfma_launch(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
+                                   const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s) {
+  const int64_t tiles = (N + 16 * RT - 1) / (16 * RT);
+  hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB>), dim3((unsigned)tiles), dim3(64 * WPB), 0, s,
+                     codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16);
+  return hipGetLastError();
+}
+
+// Tile choice, measured on MI355X at B = 2..16: row tiles per wave (reuse of
+// the activation fragments) RT = 4 for N >= 16384, 2 for N >= 4096, else 1;
+// 4 waves split K.  QG_MB_RT / QG_MB_WPB force one choice.
+#ifndef QG_MB_RT
+#define QG_MB_RT 0
+#endif
+#ifndef QG_MB_WPB
+#define QG_MB_WPB 0
+#endif
 template <int BITS, int G>
 static hipError_t gemv_mfma_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
                               const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s) {
-  // largest row-tile count that still gives >= 256 workgroups
-  if ((N + 63) / 64 >= 256) {
-    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, 4>), dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s,
-                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16);
-  } else if ((N + 31) / 32 >= 256) {
-    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, 2>), dim3((unsigned)((N + 31) / 32)), dim3(256), 0, s,
-                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16);
-  } else {
-    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, 1>), dim3((unsigned)((N + 15) / 16)), dim3(256), 0, s,
-                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16);
-  }
-  return hipGetLastError();
+#if QG_MB_RT && QG_MB_WPB
+  return gemv_mfma_launch<BITS, G, QG_MB_RT, QG_MB_WPB>(codes, meta, N, K, x, B, y, y_bf16, s);
+#else
+  const int rt = N >= 16384 ? 4 : (N >= 4096 ? 2 : 1), wpb = 4;
+#define L(R, W) if (rt == R && wpb == W) return gemv_mfma_launch<BITS, G, R, W>(codes, meta, N, K, x, B, y, y_bf16, s)
+  L(4, 4); L(2, 4); L(1, 4);
+#undef L
+  return hipErrorInvalidValue;
+#endif
 }
 
 template <int BITS, int G>

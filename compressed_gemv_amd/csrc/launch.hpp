@@ -26,10 +26,13 @@ hipError_t launch_gemv_group(const uint32_t* codes, const uint32_t* meta, int64_
                              int64_t K, int bits, int group, const void* x, int x_dtype,
                              int64_t B, void* y, int y_dtype, hipStream_t s);
 
+// Workspace bytes per batch row of qgemv_binlr: the stage-2 table and the
+// stage-1 partial sums.
+int64_t binlr_ws_bytes_per_batch(int64_t r);
 hipError_t launch_gemv_binlr(const uint32_t* ubits, const uint32_t* vtbits,
                              const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
                              int64_t r, const void* x, int x_dtype, int64_t B, void* y,
-                             int y_dtype, float* t_ws, hipStream_t s);
+                             int y_dtype, void* ws, hipStream_t s);
 
 hipError_t launch_gemm_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
                              int64_t K, int bits, int group, const uint16_t* X, int64_t M,

@@ -132,7 +132,8 @@ int qunpack_binlr(const void* ubits, const void* vtbits, int64_t N, int64_t K,
 
 /* Binary GEMV in two stages ("70B en 4GB de VRAM...", section 1: the
  * factored form read right to left): t[b] = V^T (s2 (.) x[b]) into the
- * workspace (fp32), then y[b] = s1 (.) (U t[b]).  s1, s2: fp16 bits (device).
+ * workspace (as bf16 hi + lo parts laid out for the second stage, with
+ * partial sums), then y[b] = s1 (.) (U t[b]).  s1, s2: fp16 bits (device).
  * x_dtype Q_BF16 or Q_F32, y_dtype Q_F32 or Q_BF16, 1 <= B <= 16.
  * ws: device, ws_bytes >= the qbinlr_sizes value, 16-byte aligned. */
 int qgemv_binlr(const void* ubits, const void* vtbits, const uint16_t* s1,

@@ -50,9 +50,11 @@ def test_size_queries(lib):
         c, m = cg.qgroup_sizes(8192, 8192, b, 32)
         assert c == 8192 * 8192 * b // 8 and m == 8192 * 256 * 4
     ub, vb, ws = cg.qbinlr_sizes(28672, 8192, 4096, 1)
-    assert ub == 14_680_064 and vb == 4_194_304 and ws == 4096 * 4
+    # workspace: stage-2 table (4 B per entry of t, whole 512-entry steps)
+    # + (C, V) partials of one stage-1 workgroup per 16 rows, 16-byte rounded
+    assert ub == 14_680_064 and vb == 4_194_304 and ws == 4096 * 4 + 256 * 8
     ub, vb, ws = cg.qbinlr_sizes(10, 40, 3, 2)   # padding to 4-word rows
-    assert ub == 10 * 16 and vb == 3 * 16 and ws == 2 * 128 * 4
+    assert ub == 10 * 16 and vb == 3 * 16 and ws == 2 * (2048 + 16)
     w = cg.qweight(cg.Q_FMT_BINLR, 28672, 8192, 0, 0, None, None, 4096, None, None, None, None)
     assert cg.qgemm_prefill_ws(w, 512) == 512 * 4096 * 2
     w = cg.qweight(cg.Q_FMT_GROUP, 28672, 8192, 4, 64, None, None, 0, None, None, None, None)
