@@ -201,7 +201,7 @@ int qgemm_prefill(const qweight* w, const void* X, int x_dtype, int64_t M, void*
   if (M > INT32_MAX) return Q_EUNSUPPORTED;
   if (w->format == Q_FMT_GROUP) {
     if (!w->codes || !w->meta) return Q_EINVAL;
-    if (!aligned(w->codes, 4) || !aligned(w->meta, 4)) return Q_EALIGN;
+    if (!aligned(w->codes, 16) || !aligned(w->meta, 4)) return Q_EALIGN;
     return hip_status(qg::launch_gemm_group(static_cast<const uint32_t*>(w->codes),
                                             static_cast<const uint32_t*>(w->meta), w->N, w->K,
                                             w->bits, w->group, static_cast<const uint16_t*>(X),

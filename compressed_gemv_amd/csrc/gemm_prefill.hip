@@ -2,16 +2,24 @@
 //
 // Prefill multiplies many token rows by the same weights, so unlike decode it
 // is a dense contraction (arithmetic intensity of thousands of flops per
-// weight byte) and belongs on the matrix cores.  Each workgroup owns a
-// 128 x 128 output tile and walks K in steps of 64:
+// weight byte) and belongs on the matrix cores.  A workgroup of 8 waves owns
+// a 128 x 256 (tokens x outputs) tile and walks K in steps of 64:
 //   * the X tile (bf16, optionally scaled by s2 and re-rounded) and the
 //     decoded weight tile (bf16) are staged in LDS with a padded row pitch of
-//     144 bytes so the 16-byte fragment reads of 8 consecutive rows hit
-//     distinct banks;
-//   * weight decode happens once per workgroup: group RTN unit -> fp32
-//     s*q + o -> bf16 (round to nearest even); binary word -> +-1 (exact);
-//   * 4 waves in a 2 x 2 layout each run 4 x 4 v_mfma_f32_16x16x32_bf16
-//     tiles per 32-wide k slice, fp32 accumulation.
+//     144 bytes, so the 16-byte fragment reads of 16 consecutive rows hit
+//     distinct banks; two LDS buffers and two register stages: while the
+//     matrix cores work on step i, the raw loads of step i+2 are in flight
+//     and step i+1 is decoded and stored into the other LDS buffer, one
+//     barrier per step;
+//   * every thread decodes one 32-weight unit per step, once per 128 token
+//     rows: group RTN unit -> fp16
+//     subnormal q*2^(p-24) -> v_fma_mix_f32 s*q + o -> bf16 (round to nearest
+//     even); binary word -> +-1 (exact);
+//   * each wave runs a 64 x 64 block of v_mfma_f32_32x32x16_bf16 tiles (2 x 2)
+//     per 16-wide k slice, fp32 accumulation;
+//   * workgroups are numbered so that the 8 XCDs each take a contiguous run
+//     of tiles, N fastest: the concurrent tiles of one XCD share their X rows
+//     in that XCD's L2.
 // The binary format runs two passes ("70B en 4GB de VRAM...", section 1):
 // T = bf16((X (.) s2) V) into the workspace, then Y = (T U^T) (.) s1.
 #include "common.hpp"
@@ -19,143 +27,210 @@
 
 namespace qg {
 
-constexpr int BM = 128, BN = 128, BK = 64, PITCH = BK + 8;  // bf16 elements
+constexpr int TM = 128, TN = 256, TK = 64, LP = TK + 8;  // LDS pitch in bf16 elements
 
-// weight decoders: fill 32 consecutive k of weight row n starting at unit u
+// Weight decoders.  load() fetches the raw bits of 32 consecutive k of weight
+// row n starting at unit u (zero outside the matrix); decode() turns them
+// into 16 bf16 pairs in k order.
 template <int BITS, int G>
 struct DecRTN {
   const uint32_t* codes; const uint32_t* meta; int N; int U;
-  __device__ __forceinline__ void operator()(int n, int u, uint32_t (&outp)[16]) const {
-    if (n >= N || u >= U) {
+  struct Raw { uint32_t w[BITS]; uint32_t m; };
+  __device__ __forceinline__ void load(int n, int u, Raw& r) const {
+    const int GN = U * 32 / G;
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
+    const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
+    const bool ok = n < N && u < U;
+    const uint32_t co = ok ? (uint32_t)(n * U + u) * (BITS * 4) : 0xFFFFFF00u;
+    const uint32_t mo = ok ? (uint32_t)(n * GN + (u * 32) / G) * 4 : 0xFFFFFF00u;
+    buf_load_unit<BITS, 0>(crs, co, 0u, r.w);
+    r.m = __builtin_amdgcn_raw_buffer_load_b32(mrs, mo, 0u, 0);
+  }
+  __device__ __forceinline__ void decode(const Raw& r, uint32_t (&outp)[16]) const {
+    using UN = UnitH<BITS>;
+    uint32_t pr[16];
+    decode_unit_h<BITS>(r.w, pr);
+    const float s = f16_bits_to_f32(r.m & 0xFFFFu), o = f16_bits_to_f32(r.m >> 16);
+    float sp[UN::NCLS];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) outp[i] = 0u;
-      return;
+    for (int c = 0; c < UN::NCLS; ++c) sp[c] = s * (float)(1 << (24 - BITS * c));
+    float wv[32];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const PairInfo pi = UN::pair(k);
+      const int c = UN::p_of_pair(k) / BITS;
+      wv[pi.ca] = __builtin_fmaf(f16_lo(pr[k]), sp[c], o);
+      wv[pi.cb] = __builtin_fmaf(f16_hi(pr[k]), sp[c], o);
     }
-    uint32_t w[BITS];
-    const uint32_t* p = codes + ((size_t)n * U + u) * BITS;
 #pragma unroll
-    for (int i = 0; i < BITS; ++i) w[i] = p[i];
-    const uint32_t m = meta[(size_t)n * (U * 32 / G) + (u * 32) / G];
-    const float s = f16_bits_to_f32(m & 0xFFFFu), o = f16_bits_to_f32(m >> 16);
-    float q[32];
-    unit_codes_f32<BITS>(w, q);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      outp[i] = pack_bf16x2(__builtin_fmaf(s, q[2 * i], o), __builtin_fmaf(s, q[2 * i + 1], o));
+    for (int i = 0; i < 16; ++i) outp[i] = cvt_pk_bf16(wv[2 * i], wv[2 * i + 1]);
   }
 };
 
 struct DecBIN {
   const uint32_t* bits; int N; int Wn;   // rows, words per stored row
-  __device__ __forceinline__ void operator()(int n, int u, uint32_t (&outp)[16]) const {
-    uint32_t w = 0u;
-    const bool ok = n < N && u < Wn;
-    if (ok) w = bits[(size_t)n * Wn + u];
+  struct Raw { uint32_t w; };
+  __device__ __forceinline__ void load(int n, int u, Raw& r) const {
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(bits, (uint32_t)((size_t)N * Wn * 4));
+    const uint32_t off = (n < N && u < Wn) ? (uint32_t)(n * Wn + u) * 4u : 0xFFFFFF00u;
+    r.w = __builtin_amdgcn_raw_buffer_load_b32(brs, off, 0u, 0);
+  }
+  __device__ __forceinline__ void decode(const Raw& r, uint32_t (&outp)[16]) const {
+    // bit -> sign: 1 -> +1.0 (0x3F80), 0 -> -1.0 (0xBF80); bit 2i lands on
+    // bit 15, bit 2i+1 on bit 31.  A zero word outside the matrix meets zero
+    // activations.
+    const uint32_t nw = ~r.w;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      // bit -> sign: 1 -> +1.0 (0x3F80), 0 -> -1.0 (0xBF80)
-      const uint32_t lo = ((~w >> (2 * i)) & 1u) << 15;
-      const uint32_t hi = ((~w >> (2 * i + 1)) & 1u) << 31;
-      outp[i] = ok ? (0x3F803F80u | lo | hi) : 0u;
+      const uint32_t lo = 2 * i <= 15 ? (nw << (15 - 2 * i)) : (nw >> (2 * i - 15));
+      const uint32_t hi = nw << (30 - 2 * i);
+      outp[i] = (lo & 0x00008000u) | (hi & 0x80000000u) | 0x3F803F80u;
     }
   }
 };
 
-// AMODE 0: A = X (bf16).  AMODE 1: A = bf16(X * s2[k]).
-// EPI_BF16: output bf16 instead of fp32.  oscale: per-column fp16 scale or null.
-template <typename Dec, int AMODE>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ A, int64_t lda,
+// AMODE 0: A = X (bf16).  AMODE 1: A = bf16(X * s2[k]).  KMASK: Kact % 8 != 0.
+// oscale: per-column fp16 scale or null.  nbn: tiles along N.
+template <typename Dec, int AMODE, bool KMASK>
+__global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                    int M, int Kact, Dec dec, int N,
                                                    const uint16_t* __restrict__ kscale,
                                                    const uint16_t* __restrict__ oscale,
-                                                   void* __restrict__ Y, int64_t ldy, int y_bf16) {
-  __shared__ __align__(16) uint16_t As[BM * PITCH];
-  __shared__ __align__(16) uint16_t Bs[BN * PITCH];
+                                                   void* __restrict__ Y, int64_t ldy, int y_bf16,
+                                                   int nbn) {
+  __shared__ __align__(16) uint16_t lds[2][(TM + TN) * LP];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-  f32x4_t acc[4][4];
+  const int wm = wave >> 2, wn = wave & 3;          // 2 x 4 waves, 64 x 64 each
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);   // XCD-contiguous runs
+  const int m0 = (bid / nbn) * TM, n0 = (bid % nbn) * TN;
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int ld_row = tid >> 1, ld_half = tid & 1;   // 128 rows x 2 halves of 32
-  for (int k0 = 0; k0 < Kact; k0 += BK) {
-    // ---- A tile
-    {
-      const int m = m0 + ld_row;
-      const int kb = k0 + ld_half * 32;
-      uint32_t v[16];
-      if (m < M && kb + 32 <= Kact) {
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(A + (size_t)m * lda + kb);
+  const int ar = tid >> 3, ac = (tid & 7) * 8;        // A: rows ar + 64 i (i < 2), 8 bf16 at ac
+  const int wr = tid >> 1, wu = tid & 1;              // W: row wr, unit wu of the step
+  const int nsteps = (Kact + TK - 1) / TK;
+  // Branch-free loads through buffer resources based at this tile's first
+  // row: rows past M are out of range and read 0, a chunk at or past Kact
+  // gets an out-of-range offset.  (A chunk straddling Kact occurs only when
+  // Kact % 8 != 0; KMASK then zeroes its tail after the load.)
+  const int mrows = min(TM, M - m0);
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + (size_t)m0 * lda, (uint32_t)((size_t)mrows * lda * 2));
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(kscale, (uint32_t)(AMODE == 1 ? (size_t)Kact * 2 : 0));
+  struct Stage { u32x4_t a[2]; u32x4_t sc; typename Dec::Raw w; };
+  auto gload = [&](int step, Stage& st) {
+    const int k = step * TK + ac;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4_t t = src[i];
-          v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          uint32_t lo = 0u, hi = 0u;
-          if (m < M && kb + 2 * i < Kact) lo = A[(size_t)m * lda + kb + 2 * i];
-          if (m < M && kb + 2 * i + 1 < Kact) hi = A[(size_t)m * lda + kb + 2 * i + 1];
-          v[i] = lo | (hi << 16);
-        }
-      }
-      if constexpr (AMODE == 1) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k = kb + 2 * i;
-          const float s0 = k < Kact ? f16_bits_to_f32(kscale[k]) : 0.f;
-          const float s1v = k + 1 < Kact ? f16_bits_to_f32(kscale[k + 1]) : 0.f;
-          v[i] = pack_bf16x2(bf16_lo_to_f32(v[i]) * s0, bf16_hi_to_f32(v[i]) * s1v);
-        }
-      }
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(As + ld_row * PITCH + ld_half * 32);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = k < Kact ? (uint32_t)(((size_t)(ar + 64 * i) * lda + k) * 2) : 0xFFFFFFF0u;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0);
+      st.a[i] = u32x4_t{v[0], v[1], v[2], v[3]};
     }
-    // ---- weight tile, decoded once per workgroup
-    {
-      uint32_t v[16];
-      dec(n0 + ld_row, k0 / 32 + ld_half, v);
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(Bs + ld_row * PITCH + ld_half * 32);
+    if constexpr (AMODE == 1) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(srs, k < Kact ? (uint32_t)k * 2 : 0xFFFFFFF0u, 0, 0);
+      st.sc = u32x4_t{v[0], v[1], v[2], v[3]};
+    }
+    dec.load(n0 + wr, step * (TK / 32) + wu, st.w);
+  };
+  // scale (AMODE 1), decode and store one K-step into an LDS buffer
+  auto lstore = [&](int step, Stage& st, int buf) {
+    uint16_t* As = lds[buf];
+    uint16_t* Bs = lds[buf] + TM * LP;
+    if constexpr (KMASK) {
+      const int k = step * TK + ac;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t keep = (k + 2 * e + 1 < Kact) ? 0xFFFFFFFFu : ((k + 2 * e < Kact) ? 0x0000FFFFu : 0u);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) st.a[i][e] &= keep;
+      }
+    }
+    if constexpr (AMODE == 1) {
+      // A = bf16(X * s2[k]), re-rounded to nearest even
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          st.a[i][e] = cvt_pk_bf16(bf16_lo_to_f32(st.a[i][e]) * f16_bits_to_f32(st.sc[e] & 0xFFFFu),
+                                   bf16_hi_to_f32(st.a[i][e]) * f16_bits_to_f32(st.sc[e] >> 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4_t*>(As + (ar + 64 * i) * LP + ac) = st.a[i];
+    uint32_t v[16];
+    dec.decode(st.w, v);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(Bs + wr * LP + wu * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+  };
+  // v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 and k = 8 (l / 32) .. +7
+  // of each 32 x 16 operand; it sustains near-peak rate with few chains.
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  auto mfma_step = [&](int buf) {
+    const uint16_t* As = lds[buf];
+    const uint16_t* Bs = lds[buf] + TM * LP;
+#pragma unroll
+    for (int kk = 0; kk < TK; kk += 16) {
+      bf16x8_t af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 32 + fr) * LP + kk + fk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + j * 32 + fr) * LP + kk + fk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // one half-iteration, a single basic block: issue the raw loads of step
+  // s+2, run step s from LDS buffer `cur` on the matrix cores, decode and
+  // store step s+1 (loaded one step earlier) into the other buffer, with the
+  // decode interleaved between the MFMAs.  Steps past the end load zeros and
+  // store into a buffer nobody reads.
+  auto half = [&](int step, Stage& ld, Stage& st, int cur) {
+    gload(step + 2, ld);
+    mfma_step(cur);
+    lstore(step + 1, st, cur ^ 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
     }
     __syncthreads();
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8_t af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 16 + fr) * PITCH + kk + fk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + j * 16 + fr) * PITCH + kk + fk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
+  };
+
+  Stage s0, s1;
+  gload(0, s0);
+  gload(1, s1);
+  lstore(0, s0, 0);
+  __syncthreads();
+  for (int step = 0; step < nsteps; step += 2) {
+    half(step, s0, s1, 0);            // s0 <- step + 2, s1 (step + 1) -> buffer 1
+    if (step + 1 >= nsteps) break;
+    half(step + 1, s1, s0, 1);        // s1 <- step + 3, s0 (step + 2) -> buffer 0
   }
-  // ---- epilogue: lane holds D[4*(lane/16) + e][lane % 16] of each 16x16 tile
-  const int col_l = lane & 15, row_l = (lane >> 4) * 4;
+  // ---- epilogue: lane l holds D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32] of each 32x32 tile
+  const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 64 + j * 16 + col_l;
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + col_l;
     if (n >= N) continue;
     const float sc = oscale ? f16_bits_to_f32(oscale[n]) : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * 64 + i * 16 + row_l + e;
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + row_l + (e & 3);
         if (m < M) {
           const float vout = acc[i][j][e] * sc;
           if (y_bf16) static_cast<uint16_t*>(Y)[(size_t)m * ldy + n] = (uint16_t)f32_to_bf16_rne(vout);
@@ -166,14 +241,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
   }
 }
 
+static dim3 gemm_grid(int64_t M, int64_t N, int* nbn) {
+  *nbn = (int)((N + TN - 1) / TN);
+  return dim3((unsigned)(((M + TM - 1) / TM) * *nbn));
+}
+
 template <int BITS, int G>
 static hipError_t gemm_group_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
                                const uint16_t* X, int64_t M, void* Y, int y_bf16, hipStream_t s) {
   DecRTN<BITS, G> dec{codes, meta, (int)N, (int)(K / 32)};
-  dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_kernel<DecRTN<BITS, G>, 0>), grid, dim3(256), 0, s, X, K, (int)M,
+  int nbn;
+  const dim3 grid = gemm_grid(M, N, &nbn);
+  hipLaunchKernelGGL((gemm_kernel<DecRTN<BITS, G>, 0, false>), grid, dim3(512), 0, s, X, K, (int)M,
                      (int)K, dec, (int)N, (const uint16_t*)nullptr, (const uint16_t*)nullptr, Y,
-                     N, y_bf16);
+                     N, y_bf16, nbn);
   return hipGetLastError();
 }
 
@@ -203,19 +284,26 @@ hipError_t launch_gemm_binlr(const uint32_t* ubits, const uint32_t* vtbits,
   // pass 1: T[M][rp] = bf16((X * s2) V), weight rows = VT rows (r of them)
   {
     DecBIN dec{vtbits, (int)r, (int)pwords(K)};
-    dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((r + BN - 1) / BN));
-    hipLaunchKernelGGL((gemm_kernel<DecBIN, 1>), grid, dim3(256), 0, s, X, K, (int)M, (int)K,
-                       dec, (int)r, s2, (const uint16_t*)nullptr, (void*)T_ws, rp, 1);
+    int nbn;
+    const dim3 grid = gemm_grid(M, r, &nbn);
+    hipLaunchKernelGGL((gemm_kernel<DecBIN, 1, false>), grid, dim3(512), 0, s, X, K, (int)M, (int)K,
+                       dec, (int)r, s2, (const uint16_t*)nullptr, (void*)T_ws, rp, 1, nbn);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // pass 2: Y = (T U^T) * s1
   {
     DecBIN dec{ubits, (int)N, (int)pwords(r)};
-    dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
-    hipLaunchKernelGGL((gemm_kernel<DecBIN, 0>), grid, dim3(256), 0, s, (const uint16_t*)T_ws,
-                       rp, (int)M, (int)r, dec, (int)N, (const uint16_t*)nullptr, s1, Y, N,
-                       y_dtype == 1);
+    int nbn;
+    const dim3 grid = gemm_grid(M, N, &nbn);
+    if (r % 8)
+      hipLaunchKernelGGL((gemm_kernel<DecBIN, 0, true>), grid, dim3(512), 0, s, (const uint16_t*)T_ws,
+                         rp, (int)M, (int)r, dec, (int)N, (const uint16_t*)nullptr, s1, Y, N,
+                         y_dtype == 1, nbn);
+    else
+      hipLaunchKernelGGL((gemm_kernel<DecBIN, 0, false>), grid, dim3(512), 0, s, (const uint16_t*)T_ws,
+                         rp, (int)M, (int)r, dec, (int)N, (const uint16_t*)nullptr, s1, Y, N,
+                         y_dtype == 1, nbn);
     return hipGetLastError();
   }
 }
