@@ -213,12 +213,18 @@ def qgemv_binlr(ubits, vtbits, s1, s2, N: int, K: int, r: int, x: torch.Tensor,
 
 # ------------------------------------------------------------------ prefill
 def make_qweight_group(codes, meta, N, K, bits, group) -> qweight:
-    return qweight(Q_FMT_GROUP, N, K, bits, group, codes.data_ptr(), meta.data_ptr(), 0, None, None, None, None)
+    """A qweight descriptor; it keeps references to the tensors it points into."""
+    w = qweight(Q_FMT_GROUP, N, K, bits, group, codes.data_ptr(), meta.data_ptr(), 0, None, None, None, None)
+    w._tensors = (codes, meta)
+    return w
 
 
 def make_qweight_binlr(ubits, vtbits, s1, s2, N, K, r) -> qweight:
-    return qweight(Q_FMT_BINLR, N, K, 0, 0, None, None, r, ubits.data_ptr(), vtbits.data_ptr(),
-                   s1.data_ptr(), s2.data_ptr())
+    """A qweight descriptor; it keeps references to the tensors it points into."""
+    w = qweight(Q_FMT_BINLR, N, K, 0, 0, None, None, r, ubits.data_ptr(), vtbits.data_ptr(),
+                s1.data_ptr(), s2.data_ptr())
+    w._tensors = (ubits, vtbits, s1, s2)
+    return w
 
 
 def qgemm_prefill_ws(w: qweight, M: int) -> int:

@@ -19,9 +19,9 @@
 //    LDS.  fp32 activations are split into bf16 hi + lo halves (two dot2).
 //  * 2 <= B <= 16 (MFMA): a wave owns RT 16-row tiles; each lane decodes
 //    one unit per tile and K-step to fp32 w_hat = s*q + o (one v_fma_mix_f32
-//    per weight from an fp16-subnormal decode), rounds to bf16 and feeds
-//    v_mfma_f32_16x16x32_bf16 with the activations (bf16) as the 16-column
-//    operand, fp32 accumulation.
+//    per weight from an fp16-subnormal decode), splits it into bf16 hi + lo
+//    and feeds two v_mfma_f32_16x16x32_bf16 with the activations (bf16) as
+//    the 16-column operand, fp32 accumulation.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -260,8 +260,10 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 // units (128 inputs) per MFMA quad, and the activation lane (b, kg) loads the
 // matching 8-wide slices of x[b].  Dequantization: each code is decoded as
 // the fp16 subnormal q*2^(p-24) (common.hpp, UnitH), and one v_fma_mix_f32
-// per weight gives fl32(s*q + o), rounded to bf16 for the MFMA.  Partial
-// sums of the WPB waves meet in LDS.
+// per weight gives fl32(s*q + o); the MFMA takes it as bf16 hi + lo (two
+// MFMAs, 2^-16 relative residual), so the rounding of the weight operand
+// stays far below the error budget at any K.  Partial sums of the WPB waves
+// meet in LDS.
 template <int BITS, int G, int RT, int WPB>
 __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
@@ -324,10 +326,17 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u32x4_t a;
+        // w_hat = hi + lo, both bf16 (2^-16 relative residual): two MFMAs
+        u32x4_t hi, lo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = cvt_pk_bf16(wv[8 * j + 2 * e], wv[8 * j + 2 * e + 1]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+        for (int e = 0; e < 4; ++e) {
+          const float w0 = wv[8 * j + 2 * e], w1 = wv[8 * j + 2 * e + 1];
+          hi[e] = cvt_pk_bf16(w0, w1);
+          lo[e] = cvt_pk_bf16(w0 - bf16_lo_to_f32(hi[e]), w1 - bf16_hi_to_f32(hi[e]));
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
+                                                         __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo),
                                                          __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
       }
     }

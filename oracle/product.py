@@ -45,6 +45,29 @@ def abs_denominator(W_hat: np.ndarray, X: np.ndarray) -> np.ndarray:
     return np.abs(np.asarray(X, dtype=np.float64)) @ np.abs(np.asarray(W_hat, dtype=np.float64)).T
 
 
+def binlr_abs_denominator(U, V, s1_bits, s2_bits, X) -> np.ndarray:
+    """Error denominator of the binary low-rank product.
+
+    The plain D = sum_j |W_hat_ij| |x_j| with W_hat = s1 (U V^T) s2 ("70B en
+    4GB de VRAM...", section 1).  Where a row of the sign product U V^T is
+    identically zero, D = 0 while the method, evaluated in its two factored
+    stages (t = V^T (s2 x), y = s1 U t), still adds r * K nonzero terms that
+    cancel only in exact arithmetic; such elements are measured against the
+    magnitude of those terms, |s1_i| * sum_l sum_j |U_il V_jl s2_j x_j| =
+    |s1_i| * r * sum_j |s2_j x_j|, which bounds D everywhere (|C_ij| <= r).
+    """
+    U = np.asarray(U, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    s1 = f16_to_f64(s1_bits)
+    s2 = f16_to_f64(s2_bits)
+    X = np.asarray(X, dtype=np.float64)
+    W_hat = s1[:, None] * (U @ V.T) * s2[None, :]
+    D = abs_denominator(W_hat, X)
+    r = U.shape[1]
+    D_fact = np.abs(X) @ np.abs(s2)[:, None] * r * np.abs(s1)[None, :]
+    return np.where(D > 0, D, D_fact)
+
+
 def normalized_error(Y: np.ndarray, Y_ref: np.ndarray, D: np.ndarray) -> float:
     """max |Y - Y_ref| / D over elements with D > 0; inf if an element with D == 0 is nonzero."""
     Y = np.asarray(Y, dtype=np.float64)

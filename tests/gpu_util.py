@@ -9,6 +9,14 @@ import oracle
 
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
 TOL = 2e-3
+# Prefill feeds the matrix cores bf16 tiles (unit roundoff 2^-8).  RTN: each
+# weight is rounded once, so |y - y_ref| <= 2^-8 sum|w_hat||x| plus the fp32
+# accumulation; on the configs' reductions (K >= 512) the errors concentrate
+# near 1e-4, far inside 2e-3, but a short reduction can approach 2^-8.
+PREFILL_RTN_BOUND = 2.0 ** -8 + 2.0 ** -14
+# Binary prefill rounds s2*x and t = (s2*x) V to bf16: against the factored
+# magnitude |s1| r sum|s2 x| the error is <= 2 * 2^-8 (1 + 2^-8).
+PREFILL_BINLR_FACT_BOUND = 2.0 ** -7 * (1 + 2.0 ** -8) + 2.0 ** -14
 
 
 def say(msg):

@@ -116,3 +116,28 @@ def test_sizes_formulas():
     # codes + meta byte counts agree with the packed buffers
     q = np.zeros((4, 256), np.uint8)
     assert fmt.pack_codes(q, 5).nbytes + 4 * (256 // 64) * 4 == sizes.group_bytes(4, 256, 5, 64)
+
+
+def test_binlr_denominator_degenerate_rows():
+    """A sign-product row that is identically zero (U_i orthogonal to every
+    V_j) has D = 0; the binary denominator then falls back to the factored
+    terms' magnitude |s1_i| r sum_j |s2_j x_j|, and it never undercuts D."""
+    U = np.array([[1, -1], [1, 1]], np.int8)            # row 0: (1,-1) . (1,1) = 0
+    V = np.array([[1, 1], [1, 1], [-1, -1]], np.int8)
+    s1 = np.array([0x3C00, 0x4000], np.uint16)           # fp16 1.0, 2.0
+    s2 = np.array([0x3C00, 0x3800, 0x4000], np.uint16)   # 1.0, 0.5, 2.0
+    x = np.array([[1.0, -4.0, 0.25]])
+    D = product.binlr_abs_denominator(U, V, s1, s2, x)
+    # row 0: C = 0 -> 1 * 2 * (1 + 2 + 0.5) = 7 ; row 1: C = (2, 2, -2) -> 2 * (2*1 + 2*0.5*4 + 2*2*0.25) = 14
+    assert np.array_equal(D, np.array([[7.0, 14.0]]))
+    rng = np.random.default_rng(3)
+    for r in (1, 2, 3, 8):
+        U = np.where(rng.integers(0, 2, (9, r)) == 1, 1, -1).astype(np.int8)
+        V = np.where(rng.integers(0, 2, (7, r)) == 1, 1, -1).astype(np.int8)
+        s1 = (np.abs(rng.standard_normal(9)) + 0.1).astype(np.float16).view(np.uint16)
+        s2 = (np.abs(rng.standard_normal(7)) + 0.1).astype(np.float16).view(np.uint16)
+        x = rng.standard_normal((2, 7))
+        W = product.f16_to_f64(s1)[:, None] * (U.astype(np.int64) @ V.T.astype(np.int64)) * product.f16_to_f64(s2)
+        D0 = product.abs_denominator(W, x)
+        D1 = product.binlr_abs_denominator(U, V, s1, s2, x)
+        assert np.all(D1 >= D0) and np.array_equal(D1[D0 > 0], D0[D0 > 0]) and np.all(D1 > 0)
