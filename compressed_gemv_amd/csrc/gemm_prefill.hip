@@ -176,20 +176,25 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   auto mfma_step = [&](int buf) {
     const uint16_t* As = lds[buf];
     const uint16_t* Bs = lds[buf] + TM * LP;
-#pragma unroll
-    for (int kk = 0; kk < TK; kk += 16) {
-      bf16x8_t af[2], bfr[2];
+    // fragments of k-slice s+1 are read before the MFMAs of slice s
+    bf16x8_t af[2][2], bfr[2][2];
+    auto rd = [&](int kk, bf16x8_t (&a)[2], bf16x8_t (&b)[2]) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 32 + fr) * LP + kk + fk);
+        a[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 32 + fr) * LP + kk + fk);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + j * 32 + fr) * LP + kk + fk);
+        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + j * 32 + fr) * LP + kk + fk);
+    };
+    rd(0, af[0], bfr[0]);
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      if (ks + 1 < TK / 16) rd((ks + 1) * 16, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
     }
   };
   // one half-iteration, a single basic block: issue the raw loads of step
