@@ -27,16 +27,18 @@
 
 // Tile parameters of the B = 1 kernel.  UI = units per lane held in
 // registers (a K-slice covers 2048*UI inputs), RPW = rows per pipeline
-// stage, target waves per launch.  Measured on MI355X: 4-bit codes and long
-// rows (K > 16384) run best with UI = 4, one row per stage and 1024 waves
-// (one per SIMD, deep per-wave streams); 2/3/5/6-bit with UI = 2, two rows
-// per stage and 2048 waves (more waves to cover their longer decode).
-// QG_B1_UI / QG_B1_RPW / QG_B1_WAVES force one choice.
+// stage, target waves per launch.  Measured on MI355X (repeated, interleaved
+// runs over the Llama-70B layer shapes): bf16 activations run best with
+// UI = 4, one row per stage and 1024 waves (one per SIMD, deep per-wave
+// streams), except 3-bit codes (two rows per stage) and 2-bit codes (2048
+// waves); fp32 activations (two bf16 halves per pair) use UI = 2, two rows
+// per stage, 2048 waves.  QG_B1_UI / QG_B1_RPW / QG_B1_WAVES force one
+// choice.
 #ifndef QG_B1_UI
 #define QG_B1_UI 0
 #endif
 #ifndef QG_B1_RPW
-#define QG_B1_RPW 0       // 0 = by width: 1 row per stage with UI = 4, 2 with UI = 2
+#define QG_B1_RPW 0       // 0 = by width (see above)
 #endif
 #ifndef QG_B1_WAVES
 #define QG_B1_WAVES 0
@@ -387,8 +389,8 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
 // --------------------------------------------------------------- launchers
 template <int BITS, int G, bool XF32, int UI, int RPW>
 static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
-                            const void* x, void* y, int y_bf16, hipStream_t s) {
-  const int64_t kTargetWaves = QG_B1_WAVES ? QG_B1_WAVES : (UI >= 4 ? 1024 : 2048);
+                            const void* x, void* y, int y_bf16, hipStream_t s, int64_t waves) {
+  const int64_t kTargetWaves = QG_B1_WAVES ? QG_B1_WAVES : waves;
   const int U = (int)(K / 32);
   int S = (U + 64 * UI - 1) / (64 * UI);
   if (S > 8) return hipErrorInvalidValue;
@@ -450,10 +452,12 @@ static hipError_t gemv_dispatch(const uint32_t* codes, const uint32_t* meta, int
                                 int64_t K, const void* x, int x_dtype, int64_t B, void* y,
                                 int y_bf16, hipStream_t s) {
   if (B == 1) {
-    if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s);
-    const bool wide = QG_B1_UI ? QG_B1_UI >= 4 : (BITS == 4 || K > 16384);
-    if (wide) return gemv_b1_t<BITS, G, false, 4, QG_B1_RPW ? QG_B1_RPW : 1>(codes, meta, N, K, x, y, y_bf16, s);
-    return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW ? QG_B1_RPW : 2>(codes, meta, N, K, x, y, y_bf16, s);
+    if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s, 2048);
+    constexpr int kRpw = QG_B1_RPW ? QG_B1_RPW : (BITS == 3 ? 2 : 1);
+    const int64_t waves = BITS == 2 ? 2048 : 1024;
+    if (QG_B1_UI == 2)
+      return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW ? QG_B1_RPW : 2>(codes, meta, N, K, x, y, y_bf16, s, 2048);
+    return gemv_b1_t<BITS, G, false, 4, kRpw>(codes, meta, N, K, x, y, y_bf16, s, waves);
   }
   if (x_dtype != 1) return hipErrorInvalidValue;
   return gemv_mfma_t<BITS, G>(codes, meta, N, K, static_cast<const uint16_t*>(x), B, y, y_bf16, s);
