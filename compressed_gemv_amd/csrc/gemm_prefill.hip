@@ -27,7 +27,6 @@
 
 namespace qg {
 
-constexpr int TM = 128, TN = 256, TK = 64, LP = TK + 8;  // LDS pitch in bf16 elements
 
 // Weight decoders.  load() fetches the raw bits of 32 consecutive k of weight
 // row n starting at unit u (zero outside the matrix); decode() turns them
@@ -89,33 +88,50 @@ struct DecBIN {
   }
 };
 
+// Tile configurations: block tile TM x TN, WM x WN waves, each wave
+// (TM/WM) x (TN/WN) on 32x32x16 MFMAs; VPM VALU instructions are interleaved
+// after each MFMA of a step.
+// TK is the K step (a multiple of 32); LDS rows are TK + 8 bf16 apart.
+struct TileSmall { static constexpr int TM = 128, TN = 256, TK = 64, WM = 2, WN = 4, VPM = 6; };   // 8 waves, 64 x 64
+#ifndef QG_BIG_TK
+#define QG_BIG_TK 64
+#endif
+#ifndef QG_BIG_VPM
+#define QG_BIG_VPM 3
+#endif
+struct TileBig   { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 2, WN = 2, VPM = QG_BIG_VPM; };   // 4 waves, 128 x 128
+
 // AMODE 0: A = X (bf16).  AMODE 1: A = bf16(X * s2[k]).  KMASK: Kact % 8 != 0.
 // oscale: per-column fp16 scale or null.  nbn: tiles along N.
-template <typename Dec, int AMODE, bool KMASK>
-__global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ A, int64_t lda,
-                                                   int M, int Kact, Dec dec, int N,
-                                                   const uint16_t* __restrict__ kscale,
-                                                   const uint16_t* __restrict__ oscale,
-                                                   void* __restrict__ Y, int64_t ldy, int y_bf16,
-                                                   int nbn) {
+template <typename Dec, int AMODE, bool KMASK, typename Cfg>
+__global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int M, int Kact, Dec dec, int N,
+    const uint16_t* __restrict__ kscale, const uint16_t* __restrict__ oscale,
+    void* __restrict__ Y, int64_t ldy, int y_bf16, int nbn) {
+  constexpr int TM = Cfg::TM, TN = Cfg::TN, TK = Cfg::TK, LP = TK + 8, UPR = TK / 32;
+  constexpr int NT = 64 * Cfg::WM * Cfg::WN;         // threads
+  constexpr int FI = TM / Cfg::WM / 32, FJ = TN / Cfg::WN / 32;   // 32x32 tiles per wave
+  constexpr int AC = TM * (TK / 8) / NT;              // 16-byte X chunks per thread and step
+  constexpr int WU = TN * UPR / NT;                   // weight units per thread and step
+  static_assert(AC >= 1 && WU >= 1 && NT % (TK / 8) == 0, "tile configuration");
   __shared__ __align__(16) uint16_t lds[2][(TM + TN) * LP];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;          // 2 x 4 waves, 64 x 64 each
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   int bid = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);   // XCD-contiguous runs
   const int m0 = (bid / nbn) * TM, n0 = (bid % nbn) * TN;
-  f32x16_t acc[2][2];
+  f32x16_t acc[FI][FJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int ar = tid >> 3, ac = (tid & 7) * 8;        // A: rows ar + 64 i (i < 2), 8 bf16 at ac
-  const int wr = tid >> 1, wu = tid & 1;              // W: row wr, unit wu of the step
+  constexpr int AROWS = NT / (TK / 8);                // X rows covered per chunk round
+  const int ar = tid / (TK / 8), ac = (tid % (TK / 8)) * 8;   // X: rows ar + AROWS i, 8 bf16 at ac
   const int nsteps = (Kact + TK - 1) / TK;
   // Branch-free loads through buffer resources based at this tile's first
   // row: rows past M are out of range and read 0, a chunk at or past Kact
@@ -124,12 +140,12 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   const int mrows = min(TM, M - m0);
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + (size_t)m0 * lda, (uint32_t)((size_t)mrows * lda * 2));
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(kscale, (uint32_t)(AMODE == 1 ? (size_t)Kact * 2 : 0));
-  struct Stage { u32x4_t a[2]; u32x4_t sc; typename Dec::Raw w; };
+  struct Stage { u32x4_t a[AC]; u32x4_t sc; typename Dec::Raw w[WU]; };
   auto gload = [&](int step, Stage& st) {
     const int k = step * TK + ac;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t off = k < Kact ? (uint32_t)(((size_t)(ar + 64 * i) * lda + k) * 2) : 0xFFFFFFF0u;
+    for (int i = 0; i < AC; ++i) {
+      const uint32_t off = k < Kact ? (uint32_t)(((size_t)(ar + AROWS * i) * lda + k) * 2) : 0xFFFFFFF0u;
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0);
       st.a[i] = u32x4_t{v[0], v[1], v[2], v[3]};
     }
@@ -137,7 +153,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(srs, k < Kact ? (uint32_t)k * 2 : 0xFFFFFFF0u, 0, 0);
       st.sc = u32x4_t{v[0], v[1], v[2], v[3]};
     }
-    dec.load(n0 + wr, step * (TK / 32) + wu, st.w);
+#pragma unroll
+    for (int j = 0; j < WU; ++j) {
+      const int idx = tid + NT * j;                   // (row, unit) = (idx / UPR, idx % UPR)
+      dec.load(n0 + idx / UPR, step * UPR + idx % UPR, st.w[j]);
+    }
   };
   // scale (AMODE 1), decode and store one K-step into an LDS buffer
   auto lstore = [&](int step, Stage& st, int buf) {
@@ -149,51 +169,56 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
       for (int e = 0; e < 4; ++e) {
         const uint32_t keep = (k + 2 * e + 1 < Kact) ? 0xFFFFFFFFu : ((k + 2 * e < Kact) ? 0x0000FFFFu : 0u);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) st.a[i][e] &= keep;
+        for (int i = 0; i < AC; ++i) st.a[i][e] &= keep;
       }
     }
     if constexpr (AMODE == 1) {
       // A = bf16(X * s2[k]), re-rounded to nearest even
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < AC; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           st.a[i][e] = cvt_pk_bf16(bf16_lo_to_f32(st.a[i][e]) * f16_bits_to_f32(st.sc[e] & 0xFFFFu),
                                    bf16_hi_to_f32(st.a[i][e]) * f16_bits_to_f32(st.sc[e] >> 16));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4_t*>(As + (ar + 64 * i) * LP + ac) = st.a[i];
-    uint32_t v[16];
-    dec.decode(st.w, v);
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(Bs + wr * LP + wu * 32);
+    for (int i = 0; i < AC; ++i)
+      *reinterpret_cast<u32x4_t*>(As + (ar + AROWS * i) * LP + ac) = st.a[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    for (int j = 0; j < WU; ++j) {
+      const int idx = tid + NT * j;
+      uint32_t v[16];
+      dec.decode(st.w[j], v);
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(Bs + (idx / UPR) * LP + (idx % UPR) * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    }
   };
   // v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 and k = 8 (l / 32) .. +7
   // of each 32 x 16 operand; it sustains near-peak rate with few chains.
   const int fr = lane & 31, fk = (lane >> 5) * 8;
+  constexpr int WTM = TM / Cfg::WM, WTN = TN / Cfg::WN;
   auto mfma_step = [&](int buf) {
     const uint16_t* As = lds[buf];
     const uint16_t* Bs = lds[buf] + TM * LP;
     // fragments of k-slice s+1 are read before the MFMAs of slice s
-    bf16x8_t af[2][2], bfr[2][2];
-    auto rd = [&](int kk, bf16x8_t (&a)[2], bf16x8_t (&b)[2]) {
+    bf16x8_t af[2][FI], bfr[2][FJ];
+    auto rd = [&](int kk, bf16x8_t (&a)[FI], bf16x8_t (&b)[FJ]) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 32 + fr) * LP + kk + fk);
+      for (int i = 0; i < FI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WTM + i * 32 + fr) * LP + kk + fk);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + j * 32 + fr) * LP + kk + fk);
+      for (int j = 0; j < FJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WTN + j * 32 + fr) * LP + kk + fk);
     };
     rd(0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
       if (ks + 1 < TK / 16) rd((ks + 1) * 16, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
     }
   };
@@ -207,9 +232,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
     mfma_step(cur);
     lstore(step + 1, st, cur ^ 1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+    for (int i = 0; i < FI * FJ * (TK / 16); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, Cfg::VPM, 0);   // VALU
     }
     __syncthreads();
   };
@@ -219,23 +244,25 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   gload(1, s1);
   lstore(0, s0, 0);
   __syncthreads();
+  // Whole pairs of steps, so the loop has one exit: with an odd step count
+  // the last half-step runs on a buffer of zeros (everything loaded past the
+  // end is zero), which leaves the sums unchanged.
   for (int step = 0; step < nsteps; step += 2) {
     half(step, s0, s1, 0);            // s0 <- step + 2, s1 (step + 1) -> buffer 1
-    if (step + 1 >= nsteps) break;
     half(step + 1, s1, s0, 1);        // s1 <- step + 3, s0 (step + 2) -> buffer 0
   }
   // ---- epilogue: lane l holds D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32] of each 32x32 tile
   const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + col_l;
+  for (int j = 0; j < FJ; ++j) {
+    const int n = n0 + wn * WTN + j * 32 + col_l;
     if (n >= N) continue;
     const float sc = oscale ? f16_bits_to_f32(oscale[n]) : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < FI; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + row_l + (e & 3);
+        const int m = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + row_l + (e & 3);
         if (m < M) {
           const float vout = acc[i][j][e] * sc;
           if (y_bf16) static_cast<uint16_t*>(Y)[(size_t)m * ldy + n] = (uint16_t)f32_to_bf16_rne(vout);
@@ -246,21 +273,51 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   }
 }
 
-static dim3 gemm_grid(int64_t M, int64_t N, int* nbn) {
-  *nbn = (int)((N + TN - 1) / TN);
-  return dim3((unsigned)(((M + TM - 1) / TM) * *nbn));
+template <typename Dec, int AMODE, bool KMASK, typename Cfg>
+static hipError_t gemm_launch(const uint16_t* A, int64_t lda, int64_t M, int64_t Kact, Dec dec, int64_t N,
+                              const uint16_t* kscale, const uint16_t* oscale, void* Y, int64_t ldy,
+                              int y_bf16, hipStream_t s) {
+  const int nbn = (int)((N + Cfg::TN - 1) / Cfg::TN);
+  const dim3 grid((unsigned)(((M + Cfg::TM - 1) / Cfg::TM) * nbn));
+  hipLaunchKernelGGL((gemm_kernel<Dec, AMODE, KMASK, Cfg>), grid, dim3(64 * Cfg::WM * Cfg::WN), 0, s, A, lda,
+                     (int)M, (int)Kact, dec, (int)N, kscale, oscale, Y, ldy, y_bf16, nbn);
+  return hipGetLastError();
+}
+
+// Either tile runs one workgroup per CU, and a 256 x 256 tile takes about
+// 7/4 the time of a 128 x 256 one (fewer LDS reads and barriers per MFMA),
+// so the choice compares whole rounds of workgroups over the CUs: the big
+// tile wins once it has enough tiles to fill the GPU, the small one when
+// its extra parallelism saves a round (short M, or the narrow first pass of
+// the binary path).
+#ifndef QG_GEMM_TILE
+#define QG_GEMM_TILE 0    // 0 = by cost, 1 = small, 2 = big
+#endif
+static bool use_big_tile(int64_t M, int64_t N) {
+  if (QG_GEMM_TILE) return QG_GEMM_TILE == 2;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t nbig = ((M + TileBig::TM - 1) / TileBig::TM) * ((N + TileBig::TN - 1) / TileBig::TN);
+  const int64_t nsmall = ((M + TileSmall::TM - 1) / TileSmall::TM) * ((N + TileSmall::TN - 1) / TileSmall::TN);
+  return 7 * ((nbig + cus - 1) / cus) <= 4 * ((nsmall + cus - 1) / cus);
+}
+
+template <typename Dec, int AMODE, bool KMASK>
+static hipError_t gemm_run(const uint16_t* A, int64_t lda, int64_t M, int64_t Kact, Dec dec, int64_t N,
+                           const uint16_t* kscale, const uint16_t* oscale, void* Y, int64_t ldy,
+                           int y_bf16, hipStream_t s) {
+  if (use_big_tile(M, N))
+    return gemm_launch<Dec, AMODE, KMASK, TileBig>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16, s);
+  return gemm_launch<Dec, AMODE, KMASK, TileSmall>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16, s);
 }
 
 template <int BITS, int G>
 static hipError_t gemm_group_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
                                const uint16_t* X, int64_t M, void* Y, int y_bf16, hipStream_t s) {
   DecRTN<BITS, G> dec{codes, meta, (int)N, (int)(K / 32)};
-  int nbn;
-  const dim3 grid = gemm_grid(M, N, &nbn);
-  hipLaunchKernelGGL((gemm_kernel<DecRTN<BITS, G>, 0, false>), grid, dim3(512), 0, s, X, K, (int)M,
-                     (int)K, dec, (int)N, (const uint16_t*)nullptr, (const uint16_t*)nullptr, Y,
-                     N, y_bf16, nbn);
-  return hipGetLastError();
+  return gemm_run<DecRTN<BITS, G>, 0, false>(X, K, M, K, dec, N, nullptr, nullptr, Y, N, y_bf16, s);
 }
 
 hipError_t launch_gemm_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
@@ -289,28 +346,13 @@ hipError_t launch_gemm_binlr(const uint32_t* ubits, const uint32_t* vtbits,
   // pass 1: T[M][rp] = bf16((X * s2) V), weight rows = VT rows (r of them)
   {
     DecBIN dec{vtbits, (int)r, (int)pwords(K)};
-    int nbn;
-    const dim3 grid = gemm_grid(M, r, &nbn);
-    hipLaunchKernelGGL((gemm_kernel<DecBIN, 1, false>), grid, dim3(512), 0, s, X, K, (int)M, (int)K,
-                       dec, (int)r, s2, (const uint16_t*)nullptr, (void*)T_ws, rp, 1, nbn);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = gemm_run<DecBIN, 1, false>(X, K, M, K, dec, r, s2, nullptr, T_ws, rp, 1, s);
     if (e != hipSuccess) return e;
   }
   // pass 2: Y = (T U^T) * s1
-  {
-    DecBIN dec{ubits, (int)N, (int)pwords(r)};
-    int nbn;
-    const dim3 grid = gemm_grid(M, N, &nbn);
-    if (r % 8)
-      hipLaunchKernelGGL((gemm_kernel<DecBIN, 0, true>), grid, dim3(512), 0, s, (const uint16_t*)T_ws,
-                         rp, (int)M, (int)r, dec, (int)N, (const uint16_t*)nullptr, s1, Y, N,
-                         y_dtype == 1, nbn);
-    else
-      hipLaunchKernelGGL((gemm_kernel<DecBIN, 0, false>), grid, dim3(512), 0, s, (const uint16_t*)T_ws,
-                         rp, (int)M, (int)r, dec, (int)N, (const uint16_t*)nullptr, s1, Y, N,
-                         y_dtype == 1, nbn);
-    return hipGetLastError();
-  }
+  DecBIN dec{ubits, (int)N, (int)pwords(r)};
+  if (r % 8) return gemm_run<DecBIN, 0, true>(T_ws, rp, M, r, dec, N, nullptr, s1, Y, N, y_dtype == 1, s);
+  return gemm_run<DecBIN, 0, false>(T_ws, rp, M, r, dec, N, nullptr, s1, Y, N, y_dtype == 1, s);
 }
 
 }  // namespace qg

@@ -24,7 +24,7 @@ def _group(gpu, N, K, bits, group, B, xkind, seed, y_dtype=torch.float32, tol=2e
         xv, xd = oracle.product.bf16_to_f64(xb), dev_bf16(xb)
     y = gpu.qgemv_group(dev(words.view(np.uint8).reshape(-1)), dev(meta.view(np.int32).reshape(-1)),
                         N, K, bits, group, xd, y_dtype=y_dtype)
-    # a bf16 output adds one rounding of y (2^-9 relative)
+    # a bf16 output adds one rounding of y (2^-8 relative)
     return check_err(host(y), oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv), tol)
 
 

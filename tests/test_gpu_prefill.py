@@ -98,3 +98,41 @@ def test_full_binlr(gpu):
     Xv = oracle.product.bf16_to_f64(X[rows])
     err = check_err(Ys, oracle.product.matmul_ref(W, Xv), oracle.product.abs_denominator(W, Xv))
     say(f"  err={err:.3e}")
+
+
+def test_big_tile_rtn_ragged(gpu):
+    """With 256 CUs this shape takes the 256 x 256 tile (496 tiles, two
+    rounds, against four rounds of 128 x 256 tiles), with ragged M and N and
+    an odd number of 64-wide K steps."""
+    M, N, K = 4000, 7900, 4032
+    say(f"prefill big-tile RTN M={M} N={N} K={K}")
+    W = gen_weights(N, K, rng_for(76, 0), outliers=True)
+    codes, meta = gpu.qpack_group(dev(W), 3, 32)
+    X = gen_x_bf16(M, K, rng_for(77, 0))
+    Y = host(gpu.qgemm_prefill(gpu.make_qweight_group(codes, meta, N, K, 3, 32), dev_bf16(X)))
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(9).choice(M, 12, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, N - 1], np.random.default_rng(10).choice(N, 40, replace=False)]))
+    _, _, _, _, _, W_hat = group_reference(W[cols], 3, 32)
+    Xv = oracle.product.bf16_to_f64(X[rows])
+    err = check_err(Y[np.ix_(rows, cols)], oracle.product.matmul_ref(W_hat, Xv),
+                    oracle.product.abs_denominator(W_hat, Xv))
+    say(f"  err={err:.3e}")
+
+
+def test_big_tile_binlr_ragged(gpu):
+    """The second pass (M x N) takes the 256 x 256 tile with its masked K
+    tail (r % 8 != 0); the first (M x r) takes the 128 x 256 one."""
+    M, N, K, r = 4000, 7900, 3000, 1001
+    say(f"prefill big-tile binary M={M} N={N} K={K} r={r}")
+    U, V, s1, s2 = gen_binlr(N, K, r, rng_for(78, 0))
+    ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
+    X = gen_x_bf16(M, K, rng_for(79, 0))
+    Y = host(gpu.qgemm_prefill(gpu.make_qweight_binlr(ubd, vbd, dev(s1.view(np.int16)), dev(s2.view(np.int16)),
+                                                      N, K, r), dev_bf16(X)))
+    rows = np.unique(np.concatenate([[0, 256, M - 1], np.random.default_rng(11).choice(M, 10, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 256, N - 1], np.random.default_rng(12).choice(N, 40, replace=False)]))
+    W = oracle.binlr.reconstruct(U[cols], V, s1[cols], s2)
+    Xv = oracle.product.bf16_to_f64(X[rows])
+    err = check_err(Y[np.ix_(rows, cols)], oracle.product.matmul_ref(W, Xv),
+                    oracle.product.binlr_abs_denominator(U[cols], V, s1[cols], s2, Xv))
+    say(f"  err={err:.3e}")
