@@ -113,6 +113,14 @@ def test_gemv_batched(gpu, bits, B):
 
 
 @pytest.mark.parametrize("bits", WIDTHS)
+@pytest.mark.parametrize("B", [3, 16])
+def test_gemv_batched_other_group(gpu, bits, B):
+    """The group size not covered above (groups of 64 hold two units each)."""
+    say(f"gemv B={B} b={bits} other group")
+    _gemv_case(gpu, bits, 64 if bits != 4 else 32, 45, 1216, B, "bf16", bits * 10 + B + 1)
+
+
+@pytest.mark.parametrize("bits", WIDTHS)
 @pytest.mark.parametrize("B", [1, 2, 16])
 def test_gemv_integer_case_exact(gpu, bits, B):
     """Integer weights with both ends in every group (s = 1, o = 0, q = w) and
