@@ -16,6 +16,9 @@ Sources (web pages, cited by title and section):
     "Compresión por bloques": blocks of 32 or 64 weights share one scale and
     one offset; "Asignación de bits por capa": 5-6 bits for attention,
     down to 2 bits for MLP.
+  * "Métodos de cuantización de LLM...", opening and LLM.int8() paragraph:
+    about 0.1 % of the hidden dimensions hold values up to 20x larger; they
+    run in FP16 while the rest runs at low precision, results added.
   * "AirLLM corre un modelo 70B en una GPU de 4GB", "Por qué es lento":
     time per token ~ bytes moved / bandwidth (the roofline the metric uses).
 
@@ -28,8 +31,9 @@ Modules:
   binlr    +-1 factor bit packing and explicit reconstruction of W
   product  explicit W-hat, fp64 products, the normalized error metric
   sizes    byte counts and bits per weight
+  outlier  outlier channels kept aside in fp16, the rest group RTN
 
 Parity status: every function here is pinned by tests under tests/ marked
 "not gpu" (bounds, brute force, closed forms, special cases, page figures).
 """
-from . import rtn, fmt, binlr, product, sizes  # noqa: F401
+from . import rtn, fmt, binlr, product, sizes, outlier  # noqa: F401
