@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "QError", "load", "lib_path", "q_abi_version", "q_format_version", "q_status_str",
     "qgroup_sizes", "qpack_group", "qunpack_group", "qgemv_group",
+    "qgroup_outlier_ws", "qpack_group_outlier", "qgemv_group_outlier",
     "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr",
     "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
 ]
@@ -47,6 +48,7 @@ class qweight(ctypes.Structure):
         ("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p),
         ("r", ctypes.c_int64), ("ubits", ctypes.c_void_p), ("vtbits", ctypes.c_void_p),
         ("s1", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+        ("side", ctypes.c_void_p), ("oidx", ctypes.c_void_p), ("n_out", ctypes.c_int64),
     ]
 
 
@@ -68,6 +70,9 @@ def load() -> ctypes.CDLL:
         "qpack_group": (I32, [P, I64, I64, I32, I32, P, P, P]),
         "qunpack_group": (I32, [P, P, I64, I64, I32, I32, P, P, P]),
         "qgemv_group": (I32, [P, P, I64, I64, I32, I32, P, I32, I64, P, I32, P]),
+        "qgroup_outlier_ws": (I32, [I64, I64, SZ]),
+        "qpack_group_outlier": (I32, [P, I64, I64, I32, I32, I64, P, P, P, P, P, ctypes.c_size_t, P]),
+        "qgemv_group_outlier": (I32, [P, P, P, P, I64, I64, I64, I32, I32, P, I32, I64, P, I32, P]),
         "qbinlr_sizes": (I32, [I64, I64, I64, I64, SZ, SZ, SZ]),
         "qpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
         "qunpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
@@ -165,6 +170,42 @@ def qgemv_group(codes, meta, N: int, K: int, bits: int, group: int, x: torch.Ten
     return y
 
 
+# ------------------------------------------------ group RTN + outlier columns
+def qgroup_outlier_ws(K: int, n_out: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().qgroup_outlier_ws(K, n_out, ctypes.byref(n)), "qgroup_outlier_ws")
+    return n.value
+
+
+def qpack_group_outlier(W: torch.Tensor, bits: int, group: int, n_out: int, stream=None):
+    """(codes, meta, side uint16[N][n_out] fp16 bits, idx int32[n_out]) for fp32 W[N][K]."""
+    _need_cuda(W)
+    N, K = W.shape
+    cb, mb = qgroup_sizes(N, K, bits, group)
+    codes = torch.empty(cb, dtype=torch.uint8, device=W.device)
+    meta = torch.empty(mb // 4, dtype=torch.int32, device=W.device)
+    side = torch.empty((N, n_out), dtype=torch.int16, device=W.device)
+    idx = torch.empty(n_out, dtype=torch.int32, device=W.device)
+    ws = torch.empty(qgroup_outlier_ws(K, n_out), dtype=torch.uint8, device=W.device)
+    _check(load().qpack_group_outlier(_ptr(W), N, K, bits, group, n_out, _ptr(codes), _ptr(meta),
+                                      _ptr(side), _ptr(idx), _ptr(ws), ws.numel(), _stream(stream)),
+           "qpack_group_outlier")
+    return codes, meta, side, idx
+
+
+def qgemv_group_outlier(codes, meta, side, idx, N: int, K: int, bits: int, group: int, x: torch.Tensor,
+                        y: Optional[torch.Tensor] = None, y_dtype=torch.float32, stream=None):
+    """y[B][N] = x W_rest_hat^T + x[:, idx] side^T."""
+    _need_cuda(codes, meta, side, idx, x, y)
+    B = x.shape[0] if x.dim() == 2 else 1
+    if y is None:
+        y = torch.empty((B, N), dtype=y_dtype, device=x.device)
+    _check(load().qgemv_group_outlier(_ptr(codes), _ptr(meta), _ptr(side), _ptr(idx), idx.numel(), N, K, bits,
+                                      group, _ptr(x), _dtype_code(x), B, _ptr(y), _dtype_code(y),
+                                      _stream(stream)), "qgemv_group_outlier")
+    return y
+
+
 # ---------------------------------------------------------------- binary LR
 def qbinlr_sizes(N: int, K: int, r: int, B: int = 1):
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
@@ -212,10 +253,13 @@ def qgemv_binlr(ubits, vtbits, s1, s2, N: int, K: int, r: int, x: torch.Tensor,
 
 
 # ------------------------------------------------------------------ prefill
-def make_qweight_group(codes, meta, N, K, bits, group) -> qweight:
-    """A qweight descriptor; it keeps references to the tensors it points into."""
-    w = qweight(Q_FMT_GROUP, N, K, bits, group, codes.data_ptr(), meta.data_ptr(), 0, None, None, None, None)
-    w._tensors = (codes, meta)
+def make_qweight_group(codes, meta, N, K, bits, group, side=None, idx=None) -> qweight:
+    """A qweight descriptor (optionally with outlier side columns); it keeps
+    references to the tensors it points into."""
+    n_out = 0 if idx is None else idx.numel()
+    w = qweight(Q_FMT_GROUP, N, K, bits, group, codes.data_ptr(), meta.data_ptr(), 0, None, None, None, None,
+                side.data_ptr() if n_out else None, idx.data_ptr() if n_out else None, n_out)
+    w._tensors = (codes, meta, side, idx)
     return w
 
 

@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxOutliers = 64;     // outlier side columns per matrix
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -113,6 +114,64 @@ int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K, int b
                                           x, x_dtype, B, y, y_dtype, stream));
 }
 
+int outlier_args_ok(int64_t K, int64_t n_out) {
+  return (n_out >= 0 && n_out <= kMaxOutliers && n_out <= K) ? Q_OK : Q_EINVAL;
+}
+
+int qgroup_outlier_ws(int64_t K, int64_t n_out, size_t* ws_bytes) {
+  if (!ws_bytes || K < 1 || K > kMaxDim) return Q_EINVAL;
+  const int st = outlier_args_ok(K, n_out);
+  if (st != Q_OK) return st;
+  *ws_bytes = qg::pack_group_outlier_ws_bytes(K);
+  return Q_OK;
+}
+
+int qpack_group_outlier(const float* W, int64_t N, int64_t K, int bits, int group, int64_t n_out,
+                        void* codes, void* meta, uint16_t* side, int32_t* idx, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int st = group_args_ok(N, K, bits, group);
+  if (st != Q_OK) return st;
+  if ((st = outlier_args_ok(K, n_out)) != Q_OK) return st;
+  if (!W || !codes || !meta || (n_out > 0 && (!side || !idx))) return Q_EINVAL;
+  if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(meta, 16) || !aligned(side, 2) || !aligned(idx, 4))
+    return Q_EALIGN;
+  if (!ws || ws_bytes < qg::pack_group_outlier_ws_bytes(K)) return Q_EWORKSPACE;
+  if (!aligned(ws, 16)) return Q_EALIGN;
+  hipError_t e;
+  int* status = qg::pack_status_ptr(&e);
+  if (!status) return Q_EHIP;
+  if ((e = qg::launch_zero_status(status, stream)) != hipSuccess) return Q_EHIP;
+  e = qg::launch_pack_group_outlier(W, N, K, bits, group, (int)n_out, static_cast<uint32_t*>(codes),
+                                    static_cast<uint32_t*>(meta), side, idx, ws, status, stream);
+  if (e != hipSuccess) return Q_EHIP;
+  int host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return Q_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return Q_EHIP;
+  return host ? Q_ERANGE : Q_OK;
+}
+
+int qgemv_group_outlier(const void* codes, const void* meta, const uint16_t* side, const int32_t* idx,
+                        int64_t n_out, int64_t N, int64_t K, int bits, int group, const void* x,
+                        int x_dtype, int64_t B, void* y, int y_dtype, hipStream_t stream) {
+  int st = group_args_ok(N, K, bits, group);
+  if (st != Q_OK) return st;
+  if ((st = outlier_args_ok(K, n_out)) != Q_OK) return st;
+  if (n_out > 0 && (!side || !idx)) return Q_EINVAL;
+  if (!aligned(side, 2) || !aligned(idx, 4)) return Q_EALIGN;
+  if (!codes || !meta || !x || !y) return Q_EINVAL;
+  if (B < 1 || B > 16) return Q_EINVAL;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return Q_EINVAL;
+  if (!aligned(codes, 16) || !aligned(meta, 16) || !aligned(x, 16) || !aligned(y, 4))
+    return Q_EALIGN;
+  if (B == 1 && K > gemv_b1_max_k(x_dtype)) return Q_EUNSUPPORTED;
+  if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
+  if (N > INT32_MAX || K > INT32_MAX || N * n_out > INT32_MAX) return Q_EUNSUPPORTED;
+  return hip_status(qg::launch_gemv_group(static_cast<const uint32_t*>(codes),
+                                          static_cast<const uint32_t*>(meta), N, K, bits, group,
+                                          x, x_dtype, B, y, y_dtype, stream, side, idx, (int)n_out));
+}
+
 int qbinlr_sizes(int64_t N, int64_t K, int64_t r, int64_t B, size_t* ubits_bytes,
                  size_t* vtbits_bytes, size_t* ws_bytes) {
   if (N < 1 || K < 1 || r < 1 || N > kMaxDim || K > kMaxDim || r > kMaxDim) return Q_EINVAL;
@@ -201,11 +260,14 @@ int qgemm_prefill(const qweight* w, const void* X, int x_dtype, int64_t M, void*
   if (M > INT32_MAX) return Q_EUNSUPPORTED;
   if (w->format == Q_FMT_GROUP) {
     if (!w->codes || !w->meta) return Q_EINVAL;
-    if (!aligned(w->codes, 16) || !aligned(w->meta, 4)) return Q_EALIGN;
+    if (outlier_args_ok(w->K, w->n_out) != Q_OK || (w->n_out > 0 && (!w->side || !w->oidx))) return Q_EINVAL;
+    if (!aligned(w->codes, 16) || !aligned(w->meta, 4) || !aligned(w->side, 2) || !aligned(w->oidx, 4))
+      return Q_EALIGN;
+    if (w->N * w->n_out > INT32_MAX) return Q_EUNSUPPORTED;
     return hip_status(qg::launch_gemm_group(static_cast<const uint32_t*>(w->codes),
                                             static_cast<const uint32_t*>(w->meta), w->N, w->K,
                                             w->bits, w->group, static_cast<const uint16_t*>(X),
-                                            M, Y, y_dtype, stream));
+                                            M, Y, y_dtype, stream, w->side, w->oidx, (int)w->n_out));
   }
   if (!w->ubits || !w->vtbits || !w->s1 || !w->s2) return Q_EINVAL;
   if (w->K % 8) return Q_EUNSUPPORTED;  // 16-byte row loads of X

@@ -103,11 +103,15 @@ struct TileBig   { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM =
 
 // AMODE 0: A = X (bf16).  AMODE 1: A = bf16(X * s2[k]).  KMASK: Kact % 8 != 0.
 // oscale: per-column fp16 scale or null.  nbn: tiles along N.
+// side/oidx/n_out: outlier side columns (fp16 side[N][n_out] at input
+// channels oidx[], n_out <= 64; 0 = none), added as sum_j A[m][oidx_j] *
+// side[n][j] in the epilogue, before the output's single rounding.
 template <typename Dec, int AMODE, bool KMASK, typename Cfg>
 __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int M, int Kact, Dec dec, int N,
     const uint16_t* __restrict__ kscale, const uint16_t* __restrict__ oscale,
-    void* __restrict__ Y, int64_t ldy, int y_bf16, int nbn) {
+    void* __restrict__ Y, int64_t ldy, int y_bf16, int nbn,
+    const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN, TK = Cfg::TK, LP = TK + 8, UPR = TK / 32;
   constexpr int NT = 64 * Cfg::WM * Cfg::WN;         // threads
   constexpr int FI = TM / Cfg::WM / 32, FJ = TN / Cfg::WN / 32;   // 32x32 tiles per wave
@@ -251,6 +255,17 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
     half(step, s0, s1, 0);            // s0 <- step + 2, s1 (step + 1) -> buffer 1
     half(step + 1, s1, s0, 1);        // s1 <- step + 3, s0 (step + 2) -> buffer 0
   }
+  // ---- outlier columns: the main loop is done with LDS (its last step
+  // ended at a barrier), so stage A[m0 + r][oidx[j]] there as fp32
+  float* xo = reinterpret_cast<float*>(&lds[0][0]);
+  static_assert(sizeof(lds) >= TM * 64 * sizeof(float), "LDS holds the outlier activations");
+  if (n_out > 0) {
+    for (int t = tid; t < TM * n_out; t += NT) {
+      const int r = t / n_out, m = m0 + r;
+      xo[t] = m < M ? bf16_bits_to_f32(A[(size_t)m * lda + oidx[t % n_out]]) : 0.f;
+    }
+    __syncthreads();
+  }
   // ---- epilogue: lane l holds D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32] of each 32x32 tile
   const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
@@ -264,7 +279,9 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + row_l + (e & 3);
         if (m < M) {
-          const float vout = acc[i][j][e] * sc;
+          float vout = acc[i][j][e] * sc;
+          for (int q = 0; q < n_out; ++q)
+            vout = __builtin_fmaf(xo[(m - m0) * n_out + q], f16_bits_to_f32(side[(size_t)n * n_out + q]), vout);
           if (y_bf16) static_cast<uint16_t*>(Y)[(size_t)m * ldy + n] = (uint16_t)f32_to_bf16_rne(vout);
           else static_cast<float*>(Y)[(size_t)m * ldy + n] = vout;
         }
@@ -273,14 +290,16 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   }
 }
 
+struct SideCols { const uint16_t* vals; const int32_t* idx; int n; };   // outlier columns (n = 0: none)
+
 template <typename Dec, int AMODE, bool KMASK, typename Cfg>
 static hipError_t gemm_launch(const uint16_t* A, int64_t lda, int64_t M, int64_t Kact, Dec dec, int64_t N,
                               const uint16_t* kscale, const uint16_t* oscale, void* Y, int64_t ldy,
-                              int y_bf16, hipStream_t s) {
+                              int y_bf16, hipStream_t s, SideCols sc) {
   const int nbn = (int)((N + Cfg::TN - 1) / Cfg::TN);
   const dim3 grid((unsigned)(((M + Cfg::TM - 1) / Cfg::TM) * nbn));
   hipLaunchKernelGGL((gemm_kernel<Dec, AMODE, KMASK, Cfg>), grid, dim3(64 * Cfg::WM * Cfg::WN), 0, s, A, lda,
-                     (int)M, (int)Kact, dec, (int)N, kscale, oscale, Y, ldy, y_bf16, nbn);
+                     (int)M, (int)Kact, dec, (int)N, kscale, oscale, Y, ldy, y_bf16, nbn, sc.vals, sc.idx, sc.n);
   return hipGetLastError();
 }
 
@@ -307,24 +326,26 @@ static bool use_big_tile(int64_t M, int64_t N) {
 template <typename Dec, int AMODE, bool KMASK>
 static hipError_t gemm_run(const uint16_t* A, int64_t lda, int64_t M, int64_t Kact, Dec dec, int64_t N,
                            const uint16_t* kscale, const uint16_t* oscale, void* Y, int64_t ldy,
-                           int y_bf16, hipStream_t s) {
+                           int y_bf16, hipStream_t s, SideCols sc = SideCols{nullptr, nullptr, 0}) {
   if (use_big_tile(M, N))
-    return gemm_launch<Dec, AMODE, KMASK, TileBig>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16, s);
-  return gemm_launch<Dec, AMODE, KMASK, TileSmall>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16, s);
+    return gemm_launch<Dec, AMODE, KMASK, TileBig>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16, s, sc);
+  return gemm_launch<Dec, AMODE, KMASK, TileSmall>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16, s, sc);
 }
 
 template <int BITS, int G>
 static hipError_t gemm_group_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
-                               const uint16_t* X, int64_t M, void* Y, int y_bf16, hipStream_t s) {
+                               const uint16_t* X, int64_t M, void* Y, int y_bf16, hipStream_t s, SideCols sc) {
   DecRTN<BITS, G> dec{codes, meta, (int)N, (int)(K / 32)};
-  return gemm_run<DecRTN<BITS, G>, 0, false>(X, K, M, K, dec, N, nullptr, nullptr, Y, N, y_bf16, s);
+  return gemm_run<DecRTN<BITS, G>, 0, false>(X, K, M, K, dec, N, nullptr, nullptr, Y, N, y_bf16, s, sc);
 }
 
 hipError_t launch_gemm_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
                              int64_t K, int bits, int group, const uint16_t* X, int64_t M,
-                             void* Y, int y_dtype, hipStream_t s) {
+                             void* Y, int y_dtype, hipStream_t s, const uint16_t* side,
+                             const int32_t* oidx, int n_out) {
   const int yb = y_dtype == 1;
-#define CALL(b, g) gemm_group_t<b, g>(codes, meta, N, K, X, M, Y, yb, s)
+  const SideCols sc{side, oidx, n_out};
+#define CALL(b, g) gemm_group_t<b, g>(codes, meta, N, K, X, M, Y, yb, s, sc)
   switch (bits * 100 + group) {
     case 232: return CALL(2, 32); case 264: return CALL(2, 64);
     case 332: return CALL(3, 32); case 364: return CALL(3, 64);

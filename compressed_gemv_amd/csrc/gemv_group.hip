@@ -47,11 +47,14 @@
 namespace qg {
 
 // ------------------------------------------------------------------ B = 1
-template <int BITS, int G, bool XF32, int UI, int RPW>
+// OUT: outlier side columns (fp16 side[N][n_out] at input channels oidx[],
+// n_out <= 64): lane j < n_out of K-slice 0 adds side[row][j] * x[oidx[j]]
+// to its share of the row before the wave reduction.
+template <int BITS, int G, bool XF32, int UI, int RPW, bool OUT>
 __global__ __launch_bounds__(512) void gemv_b1_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
     const void* __restrict__ xin, void* __restrict__ yout, int y_bf16, int S, int RS, int USL,
-    int TMAX) {
+    int TMAX, const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out) {
   extern __shared__ float part[];
   constexpr int XS = XF32 ? 2 : 1;
   const int lane = threadIdx.x & 63;
@@ -75,6 +78,7 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   // The first chunk is requested before the activations are prepared.
   uint32_t wa[RPW][UI][BITS], ma[RPW][UI];
   uint32_t wb[RPW][UI][BITS], mb[RPW][UI];
+  uint32_t sva[RPW], svb[RPW];               // side value of each row (OUT)
   // Weight loads go through buffer resources (row offset in soffset, the
   // lane's unit offset in voffset).  A lane without a unit reads whatever
   // lies at its offset (or 0 past the end): its activation pairs are zero.
@@ -90,7 +94,9 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
     mvoff[it] = (uint32_t)((u * 32) / G) * 4;
   }
   const uint32_t crow = (uint32_t)U * BITS * 4, mrow = (uint32_t)GN * 4;
-  auto load = [&](uint32_t (&w)[RPW][UI][BITS], uint32_t (&m)[RPW][UI], int row0) {
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(side, OUT ? (uint32_t)((size_t)N * n_out * 2) : 0u);
+  const uint32_t svoff = (OUT && sl == 0 && lane < n_out) ? (uint32_t)lane * 2u : 0xFFFFFF00u;
+  auto load = [&](uint32_t (&w)[RPW][UI][BITS], uint32_t (&m)[RPW][UI], uint32_t (&sv)[RPW], int row0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const uint32_t row = (uint32_t)(row0 + r * nstreams);
@@ -99,6 +105,8 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
         buf_load_unit<BITS>(crs, cvoff[it], row * crow, w[r][it]);
         m[r][it] = buf_load_u32(mrs, mvoff[it], row * mrow);
       }
+      if constexpr (OUT)
+        sv[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, svoff, row * (uint32_t)n_out * 2u, 0);
     }
   };
   // activations first (in-order vmcnt: waiting for them must not wait for
@@ -115,7 +123,15 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   }
   const int step = RPW * nstreams;
   const int nst = stream < N ? (N - stream + step - 1) / step : 0;   // stages of this stream
-  if (nst > 0) load(wa, ma, stream);
+  if (nst > 0) load(wa, ma, sva, stream);
+  // activation of this lane's outlier channel (OUT, K-slice 0)
+  float xo = 0.f;
+  if constexpr (OUT) {
+    if (sl == 0 && lane < n_out) {
+      const int k = oidx[lane];
+      xo = XF32 ? static_cast<const float*>(xin)[k] : bf16_bits_to_f32(static_cast<const uint16_t*>(xin)[k]);
+    }
+  }
 
   // Activation prep.  Pair k of a unit holds x[ca] (low bf16) and x[cb]
   // (high bf16), unscaled; codes that land on mantissa bit p are summed in
@@ -179,10 +195,12 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   }
 
   const uint32_t bias = opaque_bias();
-  auto compute = [&](const uint32_t (&w)[RPW][UI][BITS], const uint32_t (&m)[RPW][UI], int row0, int m0) {
+  auto compute = [&](const uint32_t (&w)[RPW][UI][BITS], const uint32_t (&m)[RPW][UI], const uint32_t (&sv)[RPW],
+                     int row0, int m0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       float acc_row = 0.f;
+      if constexpr (OUT) acc_row = f16_bits_to_f32(sv[r] & 0xFFFFu) * xo;
 #pragma unroll
       for (int it = 0; it < UI; ++it) {
         uint32_t pr[16];
@@ -223,21 +241,21 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   // exactly that stage's loads and the next stage stays in flight.
   int st = 0;
   while (st + 2 < nst) {
-    load(wb, mb, stream + (st + 1) * step);
+    load(wb, mb, svb, stream + (st + 1) * step);
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(wa, ma, stream + st * step, st * RPW);
-    load(wa, ma, stream + (st + 2) * step);
+    compute(wa, ma, sva, stream + st * step, st * RPW);
+    load(wa, ma, sva, stream + (st + 2) * step);
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(wb, mb, stream + (st + 1) * step, (st + 1) * RPW);
+    compute(wb, mb, svb, stream + (st + 1) * step, (st + 1) * RPW);
     st += 2;
   }
   if (st + 1 < nst) {
-    load(wb, mb, stream + (st + 1) * step);
+    load(wb, mb, svb, stream + (st + 1) * step);
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(wa, ma, stream + st * step, st * RPW);
-    compute(wb, mb, stream + (st + 1) * step, (st + 1) * RPW);
+    compute(wa, ma, sva, stream + st * step, st * RPW);
+    compute(wb, mb, svb, stream + (st + 1) * step, (st + 1) * RPW);
   } else if (st < nst) {
-    compute(wa, ma, stream + st * step, st * RPW);
+    compute(wa, ma, sva, stream + st * step, st * RPW);
   }
   if (S > 1) {
     __syncthreads();
@@ -266,11 +284,20 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 // MFMAs, 2^-16 relative residual), so the rounding of the weight operand
 // stays far below the error budget at any K.  Partial sums of the WPB waves
 // meet in LDS.
-template <int BITS, int G, int RT, int WPB>
+// OUT: outlier side columns as in the B = 1 kernel, added to each output
+// in the final reduction (the activations of the outlier channels are
+// staged in LDS first).
+template <int BITS, int G, int RT, int WPB, bool OUT>
 __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
-    const uint16_t* __restrict__ x, int B, void* __restrict__ yout, int y_bf16) {
+    const uint16_t* __restrict__ x, int B, void* __restrict__ yout, int y_bf16,
+    const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out) {
   __shared__ float red[WPB][RT * 4][64];
+  __shared__ float xo[OUT ? 16 * 64 : 1];
+  if constexpr (OUT) {
+    for (int t = threadIdx.x; t < B * n_out; t += 64 * WPB)
+      xo[t] = bf16_bits_to_f32(x[(size_t)(t / n_out) * K + oidx[t % n_out]]);
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row_base = blockIdx.x * (16 * RT);
@@ -380,6 +407,9 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     const int t = ti / 4, i = ti % 4;
     const int b = ln & 15, row = row_base + 16 * t + 4 * (ln >> 4) + i;
     if (b < B && row < N) {
+      if constexpr (OUT)
+        for (int j = 0; j < n_out; ++j)
+          sum = __builtin_fmaf(f16_bits_to_f32(side[(size_t)row * n_out + j]), xo[b * n_out + j], sum);
       if (y_bf16) static_cast<uint16_t*>(yout)[(size_t)b * N + row] = (uint16_t)f32_to_bf16_rne(sum);
       else static_cast<float*>(yout)[(size_t)b * N + row] = sum;
     }
@@ -387,9 +417,11 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
 }
 
 // --------------------------------------------------------------- launchers
+struct Side { const uint16_t* vals; const int32_t* idx; int n; };   // outlier columns (n = 0: none)
+
 template <int BITS, int G, bool XF32, int UI, int RPW>
 static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
-                            const void* x, void* y, int y_bf16, hipStream_t s, int64_t waves) {
+                            const void* x, void* y, int y_bf16, hipStream_t s, int64_t waves, Side sd) {
   const int64_t kTargetWaves = QG_B1_WAVES ? QG_B1_WAVES : waves;
   const int U = (int)(K / 32);
   int S = (U + 64 * UI - 1) / (64 * UI);
@@ -409,18 +441,27 @@ static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t
   const int TMAX = (int)((N + nstreams - 1) / nstreams);
   const size_t lds = S > 1 ? (size_t)RS * TMAX * S * sizeof(float) : 0;
   if (lds > 64 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemv_b1_kernel<BITS, G, XF32, UI, RPW>), dim3((unsigned)blocks),
-                     dim3(threads), lds, s, codes, meta, (int)N, (int)K, x, y, y_bf16, S, RS, USL,
-                     TMAX);
+  if (sd.n > 0)
+    hipLaunchKernelGGL((gemv_b1_kernel<BITS, G, XF32, UI, RPW, true>), dim3((unsigned)blocks),
+                       dim3(threads), lds, s, codes, meta, (int)N, (int)K, x, y, y_bf16, S, RS, USL,
+                       TMAX, sd.vals, sd.idx, sd.n);
+  else
+    hipLaunchKernelGGL((gemv_b1_kernel<BITS, G, XF32, UI, RPW, false>), dim3((unsigned)blocks),
+                       dim3(threads), lds, s, codes, meta, (int)N, (int)K, x, y, y_bf16, S, RS, USL,
+                       TMAX, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 
 template <int BITS, int G, int RT, int WPB>
 static hipError_t gemv_mfma_launch(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
-                                   const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s) {
+                                   const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s, Side sd) {
   const int64_t tiles = (N + 16 * RT - 1) / (16 * RT);
-  hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB>), dim3((unsigned)tiles), dim3(64 * WPB), 0, s,
-                     codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16);
+  if (sd.n > 0)
+    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, true>), dim3((unsigned)tiles), dim3(64 * WPB), 0, s,
+                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16, sd.vals, sd.idx, sd.n);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, false>), dim3((unsigned)tiles), dim3(64 * WPB), 0, s,
+                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -435,12 +476,12 @@ static hipError_t gemv_mfma_launch(const uint32_t* codes, const uint32_t* meta, 
 #endif
 template <int BITS, int G>
 static hipError_t gemv_mfma_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
-                              const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s) {
+                              const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s, Side sd) {
 #if QG_MB_RT && QG_MB_WPB
-  return gemv_mfma_launch<BITS, G, QG_MB_RT, QG_MB_WPB>(codes, meta, N, K, x, B, y, y_bf16, s);
+  return gemv_mfma_launch<BITS, G, QG_MB_RT, QG_MB_WPB>(codes, meta, N, K, x, B, y, y_bf16, s, sd);
 #else
   const int rt = N >= 16384 ? 4 : (N >= 4096 ? 2 : 1), wpb = 4;
-#define L(R, W) if (rt == R && wpb == W) return gemv_mfma_launch<BITS, G, R, W>(codes, meta, N, K, x, B, y, y_bf16, s)
+#define L(R, W) if (rt == R && wpb == W) return gemv_mfma_launch<BITS, G, R, W>(codes, meta, N, K, x, B, y, y_bf16, s, sd)
   L(4, 4); L(2, 4); L(1, 4);
 #undef L
   return hipErrorInvalidValue;
@@ -450,24 +491,26 @@ static hipError_t gemv_mfma_t(const uint32_t* codes, const uint32_t* meta, int64
 template <int BITS, int G>
 static hipError_t gemv_dispatch(const uint32_t* codes, const uint32_t* meta, int64_t N,
                                 int64_t K, const void* x, int x_dtype, int64_t B, void* y,
-                                int y_bf16, hipStream_t s) {
+                                int y_bf16, hipStream_t s, Side sd) {
   if (B == 1) {
-    if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s, 2048);
+    if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s, 2048, sd);
     constexpr int kRpw = QG_B1_RPW ? QG_B1_RPW : (BITS == 3 ? 2 : 1);
     const int64_t waves = BITS == 2 ? 2048 : 1024;
     if (QG_B1_UI == 2)
-      return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW ? QG_B1_RPW : 2>(codes, meta, N, K, x, y, y_bf16, s, 2048);
-    return gemv_b1_t<BITS, G, false, 4, kRpw>(codes, meta, N, K, x, y, y_bf16, s, waves);
+      return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW ? QG_B1_RPW : 2>(codes, meta, N, K, x, y, y_bf16, s, 2048, sd);
+    return gemv_b1_t<BITS, G, false, 4, kRpw>(codes, meta, N, K, x, y, y_bf16, s, waves, sd);
   }
   if (x_dtype != 1) return hipErrorInvalidValue;
-  return gemv_mfma_t<BITS, G>(codes, meta, N, K, static_cast<const uint16_t*>(x), B, y, y_bf16, s);
+  return gemv_mfma_t<BITS, G>(codes, meta, N, K, static_cast<const uint16_t*>(x), B, y, y_bf16, s, sd);
 }
 
 hipError_t launch_gemv_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
                              int64_t K, int bits, int group, const void* x, int x_dtype,
-                             int64_t B, void* y, int y_dtype, hipStream_t s) {
+                             int64_t B, void* y, int y_dtype, hipStream_t s, const uint16_t* side,
+                             const int32_t* oidx, int n_out) {
   const int yb = y_dtype == 1;
-#define CALL(b, g) gemv_dispatch<b, g>(codes, meta, N, K, x, x_dtype, B, y, yb, s)
+  const Side sd{side, oidx, n_out};
+#define CALL(b, g) gemv_dispatch<b, g>(codes, meta, N, K, x, x_dtype, B, y, yb, s, sd)
   switch (bits * 100 + group) {
     case 232: return CALL(2, 32); case 264: return CALL(2, 64);
     case 332: return CALL(3, 32); case 364: return CALL(3, 64);

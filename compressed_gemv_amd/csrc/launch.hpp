@@ -22,9 +22,16 @@ hipError_t launch_unpack_binlr(const uint32_t* ubits, const uint32_t* vtbits, in
                                int64_t K, int64_t r, int8_t* U, int8_t* V, hipStream_t s);
 hipError_t launch_zero_status(int* status, hipStream_t s);
 
+// Outlier side columns (side[N][n_out] fp16 bits at input channels oidx[];
+// n_out = 0: none) are optional for the group GEMV and GEMM.
 hipError_t launch_gemv_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
                              int64_t K, int bits, int group, const void* x, int x_dtype,
-                             int64_t B, void* y, int y_dtype, hipStream_t s);
+                             int64_t B, void* y, int y_dtype, hipStream_t s,
+                             const uint16_t* side = nullptr, const int32_t* oidx = nullptr, int n_out = 0);
+hipError_t launch_pack_group_outlier(const float* W, int64_t N, int64_t K, int bits, int group, int n_out,
+                                     uint32_t* codes, uint32_t* meta, uint16_t* side, int32_t* idx,
+                                     void* ws, int* status, hipStream_t s);
+size_t pack_group_outlier_ws_bytes(int64_t K);
 
 // Workspace bytes per batch row of qgemv_binlr: the stage-2 table and the
 // stage-1 partial sums.
@@ -36,7 +43,8 @@ hipError_t launch_gemv_binlr(const uint32_t* ubits, const uint32_t* vtbits,
 
 hipError_t launch_gemm_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
                              int64_t K, int bits, int group, const uint16_t* X, int64_t M,
-                             void* Y, int y_dtype, hipStream_t s);
+                             void* Y, int y_dtype, hipStream_t s,
+                             const uint16_t* side = nullptr, const int32_t* oidx = nullptr, int n_out = 0);
 hipError_t launch_gemm_binlr(const uint32_t* ubits, const uint32_t* vtbits,
                              const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
                              int64_t r, const uint16_t* X, int64_t M, void* Y, int y_dtype,

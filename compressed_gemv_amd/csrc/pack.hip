@@ -107,10 +107,13 @@ __device__ __forceinline__ void place_code(uint32_t (&w)[B], int c, uint32_t q) 
   }
 }
 
+// zmask (optional): bit k set -> input channel k is encoded as 0 (the
+// outlier channels of the mixed decomposition).
 template <int B, int G>
 __global__ __launch_bounds__(256) void pack_group_kernel(const float* __restrict__ W, int64_t N,
                                                         int64_t K, uint32_t* __restrict__ codes,
-                                                        uint32_t* __restrict__ meta, int* status) {
+                                                        uint32_t* __restrict__ meta, int* status,
+                                                        const uint32_t* __restrict__ zmask) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t Gn = K / G;
   if (gid >= N * Gn) return;
@@ -123,6 +126,15 @@ __global__ __launch_bounds__(256) void pack_group_kernel(const float* __restrict
   for (int i = 0; i < G / 4; ++i) {
     const float4 t = reinterpret_cast<const float4*>(src)[i];
     v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+  if (zmask) {
+#pragma unroll
+    for (int uu = 0; uu < G / 32; ++uu) {
+      const uint32_t zw = zmask[(j * G) / 32 + uu];
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if ((zw >> c) & 1u) v[uu * 32 + c] = 0.f;
+    }
   }
   bool bad = false;
   float mn = v[0], mx = v[0];
@@ -202,11 +214,11 @@ __global__ __launch_bounds__(256) void unpack_group_kernel(const uint32_t* __res
 
 template <int B, int G>
 static hipError_t pack_group_t(const float* W, int64_t N, int64_t K, uint32_t* codes,
-                               uint32_t* meta, int* status, hipStream_t s) {
+                               uint32_t* meta, int* status, const uint32_t* zmask, hipStream_t s) {
   const int64_t groups = N * (K / G);
   const int64_t blocks = (groups + 255) / 256;
   hipLaunchKernelGGL((pack_group_kernel<B, G>), dim3((unsigned)blocks), dim3(256), 0, s, W, N,
-                     K, codes, meta, status);
+                     K, codes, meta, status, zmask);
   return hipGetLastError();
 }
 
@@ -232,9 +244,186 @@ static hipError_t unpack_group_t(const uint32_t* codes, const uint32_t* meta, in
 
 hipError_t launch_pack_group(const float* W, int64_t N, int64_t K, int bits, int group,
                              uint32_t* codes, uint32_t* meta, int* status, hipStream_t s) {
-#define CALL(b, g) pack_group_t<b, g>(W, N, K, codes, meta, status, s)
+#define CALL(b, g) pack_group_t<b, g>(W, N, K, codes, meta, status, nullptr, s)
   QG_DISPATCH_BG(bits, group, CALL)
 #undef CALL
+}
+
+// ------------------------------------------------------ outlier channels
+// Mixed decomposition ("Métodos de cuantización de LLM...", opening and
+// LLM.int8() paragraph): the n_out input channels with the largest
+// max_n |W[n][k]| (ties to the lower k) are encoded as 0 by the group RTN and
+// kept as fp16 columns side[n][j] = fp16(W[n][idx_j] - w_rest[n][idx_j]).
+
+// fp64 -> fp16 bits, rounded to nearest even, one rounding; +-0 keep their
+// sign.  Non-finite input or a result beyond the fp16 range is flagged.
+__device__ uint32_t f16_rne_bits(double v, bool* bad) {
+  const uint32_t sign = signbit(v) ? 0x8000u : 0u;
+  const double a = fabs(v);
+  if (!(a <= 1.7976931348623157e308)) { *bad = true; return sign | 0x7C00u; }   // NaN, inf
+  if (a == 0.0) return sign;
+  int e = 0;
+  (void)frexp(a, &e);
+  const int E = e - 1;                                  // a in [2^E, 2^(E+1))
+  if (E > 15) { *bad = true; return sign | 0x7C00u; }
+  const int qexp = (E >= -14) ? (E - 10) : -24;         // weight of the last fp16 bit
+  const double t = ldexp(a, -qexp);                     // exact
+  double k = floor(t);
+  const double frac = t - k;                            // exact
+  if (frac > 0.5 || (frac == 0.5 && fmod(k, 2.0) == 1.0)) k += 1.0;
+  const uint32_t ki = (uint32_t)k;
+  const uint32_t m = (E >= -14) ? ((uint32_t)(E + 15) << 10) + (ki - 1024u) : ki;   // carries into the exponent
+  if (m >= 0x7C00u) { *bad = true; return sign | 0x7C00u; }
+  return sign | m;
+}
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// score[k] = max over rows of |W[n][k]| as fp32 bits (monotonic for |w|; a
+// NaN sorts above +inf).  Block (x, y): 256 columns x `rows` rows.
+__global__ __launch_bounds__(256) void colmax_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                     int rows, uint32_t* __restrict__ score) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  const int64_t n0 = (int64_t)blockIdx.y * rows;
+  const int64_t n1 = n0 + rows < N ? n0 + rows : N;
+  uint32_t m = 0u;
+  for (int64_t n = n0; n < n1; ++n) {
+    const uint32_t b = __float_as_uint(W[n * K + k]) & 0x7FFFFFFFu;
+    m = b > m ? b : m;
+  }
+  atomicMax(&score[k], m);
+}
+
+// One workgroup: n_out rounds of a block-wide argmax over (score, -k); a
+// taken channel is marked 0xFFFFFFFF.  idx[] is written in increasing k and
+// zmask (K bits) marks the chosen channels.  A non-finite chosen score flags
+// the status word.
+__global__ __launch_bounds__(1024) void select_outliers_kernel(uint32_t* __restrict__ score, int64_t K,
+                                                               int n_out, int32_t* __restrict__ idx,
+                                                               uint32_t* __restrict__ zmask,
+                                                               int* status) {
+  __shared__ unsigned long long best[1024];
+  __shared__ int32_t sel[64];
+  const int tid = threadIdx.x;
+  for (int r = 0; r < n_out; ++r) {
+    unsigned long long b = 0ull;
+    for (int64_t k = tid; k < K; k += 1024) {
+      const uint32_t sc = score[k];
+      if (sc != 0xFFFFFFFFu) {
+        const unsigned long long key = ((unsigned long long)sc << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)k);
+        b = key > b ? key : b;
+      }
+    }
+    best[tid] = b;
+    __syncthreads();
+    for (int w = 512; w > 0; w >>= 1) {
+      if (tid < w && best[tid + w] > best[tid]) best[tid] = best[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) {
+      const unsigned long long key = best[0];
+      const uint32_t k = 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull);
+      if ((uint32_t)(key >> 32) >= 0x7F800000u) atomicOr(status, 1);
+      sel[r] = (int32_t)k;
+      score[k] = 0xFFFFFFFFu;
+    }
+    __syncthreads();
+  }
+  for (int64_t i = tid; i < (K + 31) / 32; i += 1024) zmask[i] = 0u;
+  if (tid == 0) {
+    for (int a = 1; a < n_out; ++a) {          // insertion sort, n_out <= 64
+      const int32_t v = sel[a];
+      int b2 = a - 1;
+      while (b2 >= 0 && sel[b2] > v) { sel[b2 + 1] = sel[b2]; --b2; }
+      sel[b2 + 1] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < n_out) {
+    idx[tid] = sel[tid];
+    atomicOr(&zmask[sel[tid] >> 5], 1u << (sel[tid] & 31));
+  }
+}
+
+// Code c of a unit (b words at w) in format v1.
+template <int B>
+__device__ __forceinline__ uint32_t unit_code_at(const uint32_t* w, int c) {
+  constexpr int F = 16 / B;
+  constexpr uint32_t L = (1u << B) - 1u;
+  if (c < 2 * F * B) {
+    const int wi = c / (2 * F), h = (c % (2 * F)) / F, j = c % F;
+    return (w[wi] >> (16 * h + B * j)) & L;
+  }
+  if constexpr (B == 3 || B == 5) {
+    const int h = c - 30;
+    uint32_t q = 0u;
+#pragma unroll
+    for (int i = 0; i < B; ++i) q |= ((w[i] >> (16 * h + 15)) & 1u) << i;
+    return q;
+  } else if constexpr (B == 6) {
+    const int h = (c - 24) / 4, p = (c - 24) % 4;
+    return ((w[p] >> (16 * h + 12)) & 0xFu) | (((w[4 + p / 2] >> (16 * h + 12 + 2 * (p % 2))) & 3u) << 4);
+  }
+  return 0u;
+}
+
+// side[n][j] = fp16(W[n][k] - (s*q + o)) at k = idx[j], fp64 arithmetic.
+template <int B, int G>
+__global__ __launch_bounds__(256) void outlier_side_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                           const uint32_t* __restrict__ codes,
+                                                           const uint32_t* __restrict__ meta,
+                                                           const int32_t* __restrict__ idx, int n_out,
+                                                           uint16_t* __restrict__ side, int* status) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= N * n_out) return;
+  const int64_t n = t / n_out;
+  const int k = idx[t % n_out];
+  const uint32_t q = unit_code_at<B>(codes + (n * (K / 32) + k / 32) * B, k % 32);
+  const uint32_t m = meta[n * (K / G) + k / G];
+  const double wr = f16_bits_to_f64(m & 0xFFFFu) * (double)q + f16_bits_to_f64(m >> 16);   // exact
+  bool bad = false;
+  const uint32_t h = f16_rne_bits((double)W[n * K + k] - wr, &bad);
+  if (bad) atomicOr(status, 1);
+  side[t] = (uint16_t)h;
+}
+
+template <int B, int G>
+static hipError_t pack_outlier_t(const float* W, int64_t N, int64_t K, int n_out, uint32_t* codes,
+                                 uint32_t* meta, uint16_t* side, int32_t* idx, uint32_t* score,
+                                 uint32_t* zmask, int* status, hipStream_t s) {
+  const unsigned kb = (unsigned)((K + 255) / 256);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(kb), dim3(256), 0, s, score, K, 0u);
+  const int rows = 256;
+  hipLaunchKernelGGL(colmax_kernel, dim3(kb, (unsigned)((N + rows - 1) / rows)), dim3(256), 0, s, W, N, K,
+                     rows, score);
+  hipLaunchKernelGGL(select_outliers_kernel, dim3(1), dim3(1024), 0, s, score, K, n_out, idx, zmask, status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = pack_group_t<B, G>(W, N, K, codes, meta, status, zmask, s);
+  if (e != hipSuccess) return e;
+  const int64_t t = N * n_out;
+  if (t > 0)
+    hipLaunchKernelGGL((outlier_side_kernel<B, G>), dim3((unsigned)((t + 255) / 256)), dim3(256), 0, s, W, N, K,
+                       codes, meta, idx, n_out, side, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_group_outlier(const float* W, int64_t N, int64_t K, int bits, int group, int n_out,
+                                     uint32_t* codes, uint32_t* meta, uint16_t* side, int32_t* idx,
+                                     void* ws, int* status, hipStream_t s) {
+  uint32_t* score = static_cast<uint32_t*>(ws);
+  uint32_t* zmask = score + ((K + 3) / 4) * 4;
+#define CALL(b, g) pack_outlier_t<b, g>(W, N, K, n_out, codes, meta, side, idx, score, zmask, status, s)
+  QG_DISPATCH_BG(bits, group, CALL)
+#undef CALL
+}
+
+size_t pack_group_outlier_ws_bytes(int64_t K) {
+  return (size_t)(((K + 3) / 4) * 4 + ((K + 31) / 32 + 3) / 4 * 4) * 4;
 }
 
 hipError_t launch_unpack_group(const uint32_t* codes, const uint32_t* meta, int64_t N,

@@ -71,7 +71,7 @@ enum {
 enum { Q_F32 = 0, Q_BF16 = 1, Q_F16 = 2 };
 enum { Q_FMT_GROUP = 1, Q_FMT_BINLR = 2 };
 
-#define Q_ABI_VERSION 1
+#define Q_ABI_VERSION 2
 #define Q_FORMAT_VERSION 1
 
 int q_abi_version(void);
@@ -114,6 +114,38 @@ int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K,
                 int bits, int group, const void* x, int x_dtype, int64_t B,
                 void* y, int y_dtype, hipStream_t stream);
 
+/* ------------------------------------------- group RTN with outlier columns
+ * Mixed decomposition ("Métodos de cuantización de LLM...", opening and
+ * LLM.int8() paragraph: about 0.1 % of the hidden dimensions carry values up
+ * to 20x larger; they run in FP16, the rest at low precision, and the two
+ * results are added).  The n_out input channels with the largest
+ * max_n |W[n][k]| (ties to the lower k) are the outliers, 0 <= n_out <= 64.
+ * They are encoded as 0 by the group RTN above (codes and meta as usual),
+ * and kept as fp16 columns side[n][j] = fp16(W[n][idx_j] - w_rest[n][idx_j]),
+ * the true column minus what the codes reconstruct there (fp64, one
+ * rounding to nearest even), so y = W_rest_hat x + side x[idx].
+ *   side  [N][n_out] fp16 bits (uint16), row-major.
+ *   idx   [n_out] int32, increasing.
+ *
+ * Workspace bytes of qpack_group_outlier (host only). */
+int qgroup_outlier_ws(int64_t K, int64_t n_out, size_t* ws_bytes);
+
+/* Choose the outlier channels, pack the rest as qpack_group does, and
+ * write side and idx.  ws: device, >= the qgroup_outlier_ws value, 16-byte
+ * aligned; side 2-byte and idx 4-byte aligned.  Synchronizes `stream`;
+ * Q_ERANGE on a non-finite weight, an fp16 overflow of a group constant or
+ * of a side value. */
+int qpack_group_outlier(const float* W, int64_t N, int64_t K, int bits, int group, int64_t n_out,
+                        void* codes, void* meta, uint16_t* side, int32_t* idx, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* qgemv_group plus the outlier term: y[b][n] = sum_k (s*q + o) x[b][k] +
+ * sum_j side[n][j] x[b][idx[j]], fp32 accumulation; same arguments and
+ * limits as qgemv_group (n_out = 0 is qgemv_group).  Asynchronous. */
+int qgemv_group_outlier(const void* codes, const void* meta, const uint16_t* side, const int32_t* idx,
+                        int64_t n_out, int64_t N, int64_t K, int bits, int group, const void* x,
+                        int x_dtype, int64_t B, void* y, int y_dtype, hipStream_t stream);
+
 /* ------------------------------------------------------------- binary LR
  * Sizes of Ubits, VTbits and of the qgemv_binlr workspace for batch B
  * (host only).  r >= 1, N >= 1, K >= 1, 1 <= B <= 16. */
@@ -153,12 +185,17 @@ typedef struct qweight {
   const void* vtbits;
   const uint16_t* s1;
   const uint16_t* s2;
+  const uint16_t* side;       /* Q_FMT_GROUP outlier columns [N][n_out] fp16, or NULL */
+  const int32_t* oidx;        /* their input channels [n_out] */
+  int64_t n_out;              /* 0..64; 0 = none */
 } qweight;
 
 /* Workspace bytes qgemm_prefill needs for M token rows (host only). */
 int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes);
 
 /* Prefill GEMM Y[M][N] = X[M][K] W_hat^T with X bf16 (x_dtype Q_BF16).
+ * Group RTN with n_out > 0 adds X[:, oidx] side^T before the output
+ * rounding.
  * Weight tiles are decoded to bf16 in LDS and fed to MFMA with fp32
  * accumulation.  Group RTN: one pass.  Binary: T = (X (.) s2) V into the
  * workspace as bf16, then Y = (T U^T) (.) s1 ("70B en 4GB de VRAM...",

@@ -47,8 +47,16 @@ def outlier_channels(W: np.ndarray, n_out: int) -> np.ndarray:
 def encode(W: np.ndarray, bits: int, group: int, n_out: int):
     """(q, s, o, side, idx): group RTN of W with the outlier columns zeroed,
     and the fp16 residual columns side[N][n_out] (float16)."""
-    W = np.asarray(W, dtype=np.float32)
     idx = outlier_channels(W, n_out)
+    return encode_with(W, bits, group, idx) + (idx,)
+
+
+def encode_with(W: np.ndarray, bits: int, group: int, idx: np.ndarray):
+    """(q, s, o, side) for a given channel list idx.  Every step after the
+    channel choice is row-local, so a subset of W's rows gives those rows'
+    codes, constants and side values."""
+    W = np.asarray(W, dtype=np.float32)
+    idx = np.asarray(idx, dtype=np.int64)
     W_rest = W.copy()
     W_rest[:, idx] = 0.0
     q, s, o = rtn.quantize(W_rest, bits, group)
@@ -58,7 +66,7 @@ def encode(W: np.ndarray, bits: int, group: int, n_out: int):
         side = diff.astype(np.float16)
     if not np.all(np.isfinite(side)):
         raise rtn.RangeError("outlier residual leaves the fp16 range")
-    return q, s, o, side, idx
+    return q, s, o, side
 
 
 def reconstruct(q: np.ndarray, s: np.ndarray, o: np.ndarray, group: int,

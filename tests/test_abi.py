@@ -29,13 +29,13 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_versions_and_status_strings(lib):
-    assert cg.q_abi_version() == 1
+    assert cg.q_abi_version() == 2
     assert cg.q_format_version() == 1
     for st in (0, -1, -2, -3, -4, -5, -6):
         s = cg.q_status_str(st)
@@ -97,6 +97,26 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemv_binlr(good, good, good, good, 64, 128, 16, good, cg.Q_BF16, 1, good, cg.Q_F32,
                            P(0), 1 << 20, s) == cg.Q_EWORKSPACE
     assert lib.qpack_binlr(good, good, 64, 128, 0, good, good, s) == cg.Q_EINVAL
+    # outlier columns: count limits, workspace, alignment
+    assert cg.qgroup_outlier_ws(8192, 8) == (8192 + 256) * 4
+    assert cg.qgroup_outlier_ws(100, 3) == (100 + 4) * 4
+    n = ctypes.c_size_t()
+    assert lib.qgroup_outlier_ws(128, 65, ctypes.byref(n)) == cg.Q_EINVAL
+    assert lib.qgroup_outlier_ws(32, 33, ctypes.byref(n)) == cg.Q_EINVAL
+    assert lib.qpack_group_outlier(good, 64, 128, 4, 32, 4, good, good, good, good, good, 16, s) == cg.Q_EWORKSPACE
+    assert lib.qpack_group_outlier(good, 64, 128, 4, 32, 4, good, good, P(0x10001), good, good, 1 << 20,
+                                   s) == cg.Q_EALIGN
+    assert lib.qpack_group_outlier(good, 64, 128, 4, 32, 4, good, good, P(0), good, good, 1 << 20,
+                                   s) == cg.Q_EINVAL
+    assert lib.qgemv_group_outlier(good, good, good, good, 65, 64, 128, 4, 32, good, cg.Q_BF16, 1, good,
+                                   cg.Q_F32, s) == cg.Q_EINVAL
+    assert lib.qgemv_group_outlier(good, good, P(0), good, 2, 64, 128, 4, 32, good, cg.Q_BF16, 1, good,
+                                   cg.Q_F32, s) == cg.Q_EINVAL
+    assert lib.qgemv_group_outlier(good, good, good, P(0x10002), 2, 64, 128, 4, 32, good, cg.Q_BF16, 1, good,
+                                   cg.Q_F32, s) == cg.Q_EALIGN
+    wo = cg.qweight(cg.Q_FMT_GROUP, 64, 128, 4, 32, 0x10000, 0x10000, 0, None, None, None, None, 0x10000,
+                    0x10000, 65)
+    assert lib.qgemm_prefill(ctypes.byref(wo), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
     # prefill
     w = cg.qweight(cg.Q_FMT_GROUP, 64, 128, 4, 32, 0x10000, 0x10000, 0, None, None, None, None)
     assert lib.qgemm_prefill(ctypes.byref(w), good, cg.Q_F32, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EUNSUPPORTED

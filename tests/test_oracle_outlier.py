@@ -126,6 +126,18 @@ def test_isolating_outliers_restores_the_grid(bits, group, seed):
     assert err_out < err_rtn, (err_out, err_rtn)
 
 
+def test_encode_with_is_row_local():
+    """Rows encoded on their own, with the channel list of the whole matrix,
+    give exactly the whole matrix's rows."""
+    W = _planted(40, 256, [7, 200], rng_for(314, 0))
+    q, s, o, side, idx = outlier.encode(W, 3, 32, 2)
+    rows = [0, 5, 39]
+    q2, s2, o2, side2 = outlier.encode_with(W[rows], 3, 32, idx)
+    assert np.array_equal(q2, q[rows]) and np.array_equal(s2.view(np.uint16), s[rows].view(np.uint16))
+    assert np.array_equal(o2.view(np.uint16), o[rows].view(np.uint16))
+    assert np.array_equal(side2.view(np.uint16), side[rows].view(np.uint16))
+
+
 def test_residual_range_error():
     W = np.zeros((2, 64), np.float32)
     W[0, 7] = 1e6          # survives as a channel score, but fp16 cannot hold it
