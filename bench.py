@@ -284,6 +284,29 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
             "per_matrix": per,
         }
         log(label, rows[f"layer_set_{label}_B1"]["GB/s"], "GB/s")
+    # the headline shape with its outlier channels kept aside in fp16 (0.1 %
+    # of K = 8 channels); bytes = codes + meta + side columns
+    def outlier_row(W, bits, group, n_out, B):
+        N, K = W.shape
+        codes, meta, side, idx = cg.qpack_group_outlier(to_dev(W), bits, group, n_out)
+        nbytes = codes.numel() + meta.numel() * 4 + side.numel() * 2
+        pool = pool_of((codes, meta, side), nbytes)
+        x = bf16(layer_x(K, B))
+        y = torch.empty((B, N), dtype=torch.float32, device=dev)
+
+        def f(i):
+            c, m, sd = pool[i % len(pool)]
+            cg.qgemv_group_outlier(c, m, sd, idx, N, K, bits, group, x, y=y)
+        wall, ev = time_launches(f, steps, warm, period=len(pool))
+        gbs = nbytes * steps / ev / 1e9
+        del pool
+        torch.cuda.empty_cache()
+        return {"us": round(ev / steps * 1e6, 3), "GB/s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / 8000.0, 2), "bytes": nbytes, "n_out": n_out}
+
+    for B in (1, 16):
+        rows[f"gemv_4b_g64_gate_outlier8_B{B}"] = outlier_row(W_gate, 4, 64, 8, B)
+        log(f"outlier B{B}:", rows[f"gemv_4b_g64_gate_outlier8_B{B}"])
     # mixed widths at batch 8 (MLP shape)
     for bits in (3, 2):
         rows[f"gemv_{bits}b_g32_gate_B8"] = gemv_row("gate", W_gate, bits, 32, 8)

@@ -110,7 +110,12 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
     }
   };
   // activations first (in-order vmcnt: waiting for them must not wait for
-  // the weight stream), then the first weight stage, then the prep.
+  // the weight stream), then the first weight stage, then the prep.  With
+  // outlier columns the channel index comes before everything else, so its
+  // wait covers nothing but itself, and the dependent activation load is
+  // issued before the weight stream.
+  int kout = 0;
+  if constexpr (OUT) kout = oidx[lane < n_out ? lane : n_out - 1];   // branch-free (n_out >= 1)
   constexpr int XW = XF32 ? 8 : 4;   // 16-byte loads per unit of activations
   u32x4_t xraw[UI][XW];
 #pragma unroll
@@ -124,13 +129,13 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   const int step = RPW * nstreams;
   const int nst = stream < N ? (N - stream + step - 1) / step : 0;   // stages of this stream
   if (nst > 0) load(wa, ma, sva, stream);
-  // activation of this lane's outlier channel (OUT, K-slice 0)
+  // activation of this lane's outlier channel (OUT, K-slice 0; 0 elsewhere),
+  // requested after the first weight stage: its wait is for the index only
   float xo = 0.f;
   if constexpr (OUT) {
-    if (sl == 0 && lane < n_out) {
-      const int k = oidx[lane];
-      xo = XF32 ? static_cast<const float*>(xin)[k] : bf16_bits_to_f32(static_cast<const uint16_t*>(xin)[k]);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    xo = XF32 ? static_cast<const float*>(xin)[kout] : bf16_bits_to_f32(static_cast<const uint16_t*>(xin)[kout]);
+    if (!(sl == 0 && lane < n_out)) xo = 0.f;
   }
 
   // Activation prep.  Pair k of a unit holds x[ca] (low bf16) and x[cb]
