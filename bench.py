@@ -284,6 +284,37 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
             "per_matrix": per,
         }
         log(label, rows[f"layer_set_{label}_B1"]["GB/s"], "GB/s")
+    # the 4-bit layer set with q/k/v in one launch and gate/up in one launch
+    def grouped_row(specs, bits, group):
+        """specs: [(name, W)] sharing K; one grouped launch per step."""
+        K = specs[0][1].shape[1]
+        packed = [cg.qpack_group(to_dev(W), bits, group) + (W.shape[0],) for _, W in specs]
+        nbytes = sum(c.numel() + m.numel() * 4 for c, m, _ in packed)
+        pool = pool_of(tuple(t for c, m, _ in packed for t in (c, m)), nbytes)
+        x = bf16(layer_x(K, 1))
+        ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for _, _, n in packed]
+
+        def f(i):
+            p = pool[i % len(pool)]
+            cg.qgemv_group_multi([(p[2 * j], p[2 * j + 1], packed[j][2]) for j in range(len(packed))], K, bits,
+                                 group, x, ys=ys)
+        wall, ev = time_launches(f, steps, warm, period=len(pool))
+        del pool
+        torch.cuda.empty_cache()
+        return {"us": round(ev / steps * 1e6, 3), "GB/s": round(nbytes * steps / ev / 1e9, 1), "bytes": nbytes}
+
+    g_qkv = grouped_row([(n, layer_weights(n)) for n in ("q", "k", "v")], 4, 64)
+    g_gu = grouped_row([("gate", W_gate), ("up", W_gate)], 4, 64)
+    per = rows["layer_set_4b_g64_B1"]["per_matrix"]
+    t_layer = g_qkv["us"] + per["o"]["us"] + g_gu["us"] + per["down"]["us"]
+    layer_b = g_qkv["bytes"] + per["o"]["bytes"] + g_gu["bytes"] + per["down"]["bytes"]
+    rows["layer_set_4b_g64_B1_grouped"] = {
+        "sum_kernel_us_per_layer": round(t_layer, 2),
+        "GB/s": round(layer_b / (t_layer * 1e-6) / 1e9, 1),
+        "tok_s_equivalent_80_layers": round(1.0 / (N_LAYERS * t_layer * 1e-6), 1),
+        "launches": {"qkv": g_qkv, "o": per["o"], "gate_up": g_gu, "down": per["down"]},
+    }
+    log("grouped layer set:", rows["layer_set_4b_g64_B1_grouped"]["GB/s"], "GB/s")
     # the headline shape with its outlier channels kept aside in fp16 (0.1 %
     # of K = 8 channels); bytes = codes + meta + side columns
     def outlier_row(W, bits, group, n_out, B):

@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "QError", "load", "lib_path", "q_abi_version", "q_format_version", "q_status_str",
     "qgroup_sizes", "qpack_group", "qunpack_group", "qgemv_group",
-    "qgroup_outlier_ws", "qpack_group_outlier", "qgemv_group_outlier",
+    "qgroup_outlier_ws", "qpack_group_outlier", "qgemv_group_outlier", "qgemv_group_multi",
     "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr",
     "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
 ]
@@ -52,6 +52,11 @@ class qweight(ctypes.Structure):
     ]
 
 
+class qgroup_mat(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("y", ctypes.c_void_p)]
+
+
 def load() -> ctypes.CDLL:
     """Load libqgemv.so from the package directory (raises if it is missing)."""
     global _LIB
@@ -71,6 +76,7 @@ def load() -> ctypes.CDLL:
         "qunpack_group": (I32, [P, P, I64, I64, I32, I32, P, P, P]),
         "qgemv_group": (I32, [P, P, I64, I64, I32, I32, P, I32, I64, P, I32, P]),
         "qgroup_outlier_ws": (I32, [I64, I64, SZ]),
+        "qgemv_group_multi": (I32, [ctypes.POINTER(qgroup_mat), I32, I64, I32, I32, P, I32, I64, I32, P]),
         "qpack_group_outlier": (I32, [P, I64, I64, I32, I32, I64, P, P, P, P, P, ctypes.c_size_t, P]),
         "qgemv_group_outlier": (I32, [P, P, P, P, I64, I64, I64, I32, I32, P, I32, I64, P, I32, P]),
         "qbinlr_sizes": (I32, [I64, I64, I64, I64, SZ, SZ, SZ]),
@@ -168,6 +174,23 @@ def qgemv_group(codes, meta, N: int, K: int, bits: int, group: int, x: torch.Ten
     _check(load().qgemv_group(_ptr(codes), _ptr(meta), N, K, bits, group, _ptr(x), _dtype_code(x), B,
                               _ptr(y), _dtype_code(y), _stream(stream)), "qgemv_group")
     return y
+
+
+def qgemv_group_multi(mats, K: int, bits: int, group: int, x: torch.Tensor, ys=None,
+                      y_dtype=torch.float32, stream=None):
+    """[y_i] for mats = [(codes_i, meta_i, N_i)] sharing x, K, bits, group; one
+    launch for batch 1."""
+    B = x.shape[0] if x.dim() == 2 else 1
+    if ys is None:
+        ys = [torch.empty((B, n), dtype=y_dtype, device=x.device) for (_, _, n) in mats]
+    for (c, m, _), y in zip(mats, ys):
+        _need_cuda(c, m, y)
+    _need_cuda(x)
+    arr = (qgroup_mat * len(mats))(*[qgroup_mat(c.data_ptr(), m.data_ptr(), n, y.data_ptr())
+                                     for (c, m, n), y in zip(mats, ys)])
+    _check(load().qgemv_group_multi(arr, len(mats), K, bits, group, _ptr(x), _dtype_code(x), B,
+                                    _dtype_code(ys[0]), _stream(stream)), "qgemv_group_multi")
+    return ys
 
 
 # ------------------------------------------------ group RTN + outlier columns

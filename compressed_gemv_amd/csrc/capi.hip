@@ -114,6 +114,48 @@ int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K, int b
                                           x, x_dtype, B, y, y_dtype, stream));
 }
 
+int qgemv_group_multi(const qgroup_mat* mats, int count, int64_t K, int bits, int group,
+                      const void* x, int x_dtype, int64_t B, int y_dtype, hipStream_t stream) {
+  if (!mats || count < 1 || count > 4 || !x) return Q_EINVAL;
+  if (B < 1 || B > 16) return Q_EINVAL;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return Q_EINVAL;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const int st = group_args_ok(mats[i].N, K, bits, group);
+    if (st != Q_OK) return st;
+    if (!mats[i].codes || !mats[i].meta || !mats[i].y) return Q_EINVAL;
+    if (!aligned(mats[i].codes, 16) || !aligned(mats[i].meta, 16) || !aligned(mats[i].y, 4)) return Q_EALIGN;
+    total += mats[i].N;
+  }
+  if (!aligned(x, 16)) return Q_EALIGN;
+  if (B == 1 && K > gemv_b1_max_k(x_dtype)) return Q_EUNSUPPORTED;
+  if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
+  if (total > INT32_MAX || K > INT32_MAX) return Q_EUNSUPPORTED;
+  if (B > 1) {
+    for (int i = 0; i < count; ++i) {
+      const hipError_t e = qg::launch_gemv_group(static_cast<const uint32_t*>(mats[i].codes),
+                                                 static_cast<const uint32_t*>(mats[i].meta), mats[i].N, K, bits,
+                                                 group, x, x_dtype, B, mats[i].y, y_dtype, stream);
+      if (e != hipSuccess) return Q_EHIP;
+    }
+    return Q_OK;
+  }
+  qg::MultiSegs ms{};
+  int start = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (i < count) {
+      ms.codes[i] = mats[i].codes; ms.meta[i] = mats[i].meta; ms.y[i] = mats[i].y;
+      ms.nrows[i] = mats[i].N; ms.start[i] = start;
+      start += (int)mats[i].N;
+    } else {
+      ms.codes[i] = mats[0].codes; ms.meta[i] = mats[0].meta; ms.y[i] = mats[0].y;
+      ms.nrows[i] = 0; ms.start[i] = INT32_MAX;
+    }
+  }
+  ms.nseg = count;
+  return hip_status(qg::launch_gemv_group_multi(ms, K, bits, group, x, x_dtype, mats[0].y, y_dtype, stream));
+}
+
 int outlier_args_ok(int64_t K, int64_t n_out) {
   return (n_out >= 0 && n_out <= kMaxOutliers && n_out <= K) ? Q_OK : Q_EINVAL;
 }

@@ -50,11 +50,17 @@ namespace qg {
 // OUT: outlier side columns (fp16 side[N][n_out] at input channels oidx[],
 // n_out <= 64): lane j < n_out of K-slice 0 adds side[row][j] * x[oidx[j]]
 // to its share of the row before the wave reduction.
-template <int BITS, int G, bool XF32, int UI, int RPW, bool OUT>
+// MULTI: up to four matrices with the same K, width and group size, sharing
+// x, in one launch (a layer's q/k/v or gate/up): launch row g belongs to
+// matrix m with segs.start[m] <= g < segs.start[m + 1] (unused starts are
+// INT_MAX) and is its row g - segs.start[m]; every row is wave-uniform, so
+// the matrix's buffer resources and output are picked with scalar selects.
+template <int BITS, int G, bool XF32, int UI, int RPW, bool OUT, bool MULTI>
 __global__ __launch_bounds__(512) void gemv_b1_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
     const void* __restrict__ xin, void* __restrict__ yout, int y_bf16, int S, int RS, int USL,
-    int TMAX, const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out) {
+    int TMAX, const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out,
+    MultiSegs segs) {
   extern __shared__ float part[];
   constexpr int XS = XF32 ? 2 : 1;
   const int lane = threadIdx.x & 63;
@@ -86,6 +92,33 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   // the next stage stays in flight while the current one is decoded.
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
+  __amdgpu_buffer_rsrc_t mcrs[4], mmrs[4];
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t rows = segs.nrows[i];
+      mcrs[i] = make_rsrc(segs.codes[i], (uint32_t)((size_t)rows * U * BITS * 4));
+      mmrs[i] = make_rsrc(segs.meta[i], (uint32_t)((size_t)rows * GN * 4));
+    }
+  }
+  auto seg_of = [&](uint32_t row) -> int {   // wave-uniform
+    return (row >= (uint32_t)segs.start[1]) + (row >= (uint32_t)segs.start[2]) + (row >= (uint32_t)segs.start[3]);
+  };
+  auto pick = [](int i, const __amdgpu_buffer_rsrc_t (&a)[4]) {
+    return i == 0 ? a[0] : (i == 1 ? a[1] : (i == 2 ? a[2] : a[3]));
+  };
+  // the output element of launch row `row`
+  auto store = [&](int row, float v) {
+    void* yb = yout;
+    int lr = row;
+    if constexpr (MULTI) {
+      const int mi = seg_of((uint32_t)row);
+      lr = row - segs.start[mi];
+      yb = mi == 0 ? segs.y[0] : (mi == 1 ? segs.y[1] : (mi == 2 ? segs.y[2] : segs.y[3]));
+    }
+    if (y_bf16) static_cast<uint16_t*>(yb)[lr] = (uint16_t)f32_to_bf16_rne(v);
+    else static_cast<float*>(yb)[lr] = v;
+  };
   uint32_t cvoff[UI], mvoff[UI];
 #pragma unroll
   for (int it = 0; it < UI; ++it) {
@@ -100,10 +133,21 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const uint32_t row = (uint32_t)(row0 + r * nstreams);
+      if constexpr (MULTI) {
+        const int mi = seg_of(row);
+        const uint32_t lr = row - (uint32_t)segs.start[mi];
+        const __amdgpu_buffer_rsrc_t c = pick(mi, mcrs), mm = pick(mi, mmrs);
 #pragma unroll
-      for (int it = 0; it < UI; ++it) {
-        buf_load_unit<BITS>(crs, cvoff[it], row * crow, w[r][it]);
-        m[r][it] = buf_load_u32(mrs, mvoff[it], row * mrow);
+        for (int it = 0; it < UI; ++it) {
+          buf_load_unit<BITS>(c, cvoff[it], lr * crow, w[r][it]);
+          m[r][it] = buf_load_u32(mm, mvoff[it], lr * mrow);
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < UI; ++it) {
+          buf_load_unit<BITS>(crs, cvoff[it], row * crow, w[r][it]);
+          m[r][it] = buf_load_u32(mrs, mvoff[it], row * mrow);
+        }
       }
       if constexpr (OUT)
         sv[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, svoff, row * (uint32_t)n_out * 2u, 0);
@@ -232,8 +276,7 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
       const int row = row0 + r * nstreams;
       if (row < N && lane == 0) {
         if (S == 1) {
-          if (y_bf16) static_cast<uint16_t*>(yout)[row] = (uint16_t)f32_to_bf16_rne(total);
-          else static_cast<float*>(yout)[row] = total;
+          store(row, total);
         } else {
           part[((size_t)rs * TMAX + (m0 + r)) * S + sl] = total;
         }
@@ -270,8 +313,7 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
       if (row < N) {
         float t = 0.f;
         for (int j = 0; j < S; ++j) t += part[(size_t)idx * S + j];
-        if (y_bf16) static_cast<uint16_t*>(yout)[row] = (uint16_t)f32_to_bf16_rne(t);
-        else static_cast<float*>(yout)[row] = t;
+        store(row, t);
       }
     }
   }
@@ -426,7 +468,8 @@ struct Side { const uint16_t* vals; const int32_t* idx; int n; };   // outlier c
 
 template <int BITS, int G, bool XF32, int UI, int RPW>
 static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
-                            const void* x, void* y, int y_bf16, hipStream_t s, int64_t waves, Side sd) {
+                            const void* x, void* y, int y_bf16, hipStream_t s, int64_t waves, Side sd,
+                            const MultiSegs* ms = nullptr) {
   const int64_t kTargetWaves = QG_B1_WAVES ? QG_B1_WAVES : waves;
   const int U = (int)(K / 32);
   int S = (U + 64 * UI - 1) / (64 * UI);
@@ -446,14 +489,19 @@ static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t
   const int TMAX = (int)((N + nstreams - 1) / nstreams);
   const size_t lds = S > 1 ? (size_t)RS * TMAX * S * sizeof(float) : 0;
   if (lds > 64 * 1024) return hipErrorInvalidValue;
-  if (sd.n > 0)
-    hipLaunchKernelGGL((gemv_b1_kernel<BITS, G, XF32, UI, RPW, true>), dim3((unsigned)blocks),
+  MultiSegs none{};
+  if (ms)
+    hipLaunchKernelGGL((gemv_b1_kernel<BITS, G, XF32, UI, RPW, false, true>), dim3((unsigned)blocks),
                        dim3(threads), lds, s, codes, meta, (int)N, (int)K, x, y, y_bf16, S, RS, USL,
-                       TMAX, sd.vals, sd.idx, sd.n);
+                       TMAX, nullptr, nullptr, 0, *ms);
+  else if (sd.n > 0)
+    hipLaunchKernelGGL((gemv_b1_kernel<BITS, G, XF32, UI, RPW, true, false>), dim3((unsigned)blocks),
+                       dim3(threads), lds, s, codes, meta, (int)N, (int)K, x, y, y_bf16, S, RS, USL,
+                       TMAX, sd.vals, sd.idx, sd.n, none);
   else
-    hipLaunchKernelGGL((gemv_b1_kernel<BITS, G, XF32, UI, RPW, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((gemv_b1_kernel<BITS, G, XF32, UI, RPW, false, false>), dim3((unsigned)blocks),
                        dim3(threads), lds, s, codes, meta, (int)N, (int)K, x, y, y_bf16, S, RS, USL,
-                       TMAX, nullptr, nullptr, 0);
+                       TMAX, nullptr, nullptr, 0, none);
   return hipGetLastError();
 }
 
@@ -496,15 +544,17 @@ static hipError_t gemv_mfma_t(const uint32_t* codes, const uint32_t* meta, int64
 template <int BITS, int G>
 static hipError_t gemv_dispatch(const uint32_t* codes, const uint32_t* meta, int64_t N,
                                 int64_t K, const void* x, int x_dtype, int64_t B, void* y,
-                                int y_bf16, hipStream_t s, Side sd) {
+                                int y_bf16, hipStream_t s, Side sd, const MultiSegs* ms = nullptr) {
   if (B == 1) {
-    if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s, 2048, sd);
+    if (x_dtype == 0) return gemv_b1_t<BITS, G, true, 2, 2>(codes, meta, N, K, x, y, y_bf16, s, 2048, sd, ms);
     constexpr int kRpw = QG_B1_RPW ? QG_B1_RPW : (BITS == 3 ? 2 : 1);
     const int64_t waves = BITS == 2 ? 2048 : 1024;
     if (QG_B1_UI == 2)
-      return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW ? QG_B1_RPW : 2>(codes, meta, N, K, x, y, y_bf16, s, 2048, sd);
-    return gemv_b1_t<BITS, G, false, 4, kRpw>(codes, meta, N, K, x, y, y_bf16, s, waves, sd);
+      return gemv_b1_t<BITS, G, false, 2, QG_B1_RPW ? QG_B1_RPW : 2>(codes, meta, N, K, x, y, y_bf16, s, 2048,
+                                                                       sd, ms);
+    return gemv_b1_t<BITS, G, false, 4, kRpw>(codes, meta, N, K, x, y, y_bf16, s, waves, sd, ms);
   }
+  if (ms) return hipErrorInvalidValue;   // the grouped launch is for batch 1
   if (x_dtype != 1) return hipErrorInvalidValue;
   return gemv_mfma_t<BITS, G>(codes, meta, N, K, static_cast<const uint16_t*>(x), B, y, y_bf16, s, sd);
 }
@@ -516,6 +566,26 @@ hipError_t launch_gemv_group(const uint32_t* codes, const uint32_t* meta, int64_
   const int yb = y_dtype == 1;
   const Side sd{side, oidx, n_out};
 #define CALL(b, g) gemv_dispatch<b, g>(codes, meta, N, K, x, x_dtype, B, y, yb, s, sd)
+  switch (bits * 100 + group) {
+    case 232: return CALL(2, 32); case 264: return CALL(2, 64);
+    case 332: return CALL(3, 32); case 364: return CALL(3, 64);
+    case 432: return CALL(4, 32); case 464: return CALL(4, 64);
+    case 532: return CALL(5, 32); case 564: return CALL(5, 64);
+    case 632: return CALL(6, 32); case 664: return CALL(6, 64);
+    default: return hipErrorInvalidValue;
+  }
+#undef CALL
+}
+
+hipError_t launch_gemv_group_multi(const MultiSegs& ms, int64_t K, int bits, int group, const void* x,
+                                   int x_dtype, void* y0, int y_dtype, hipStream_t s) {
+  const int yb = y_dtype == 1;
+  int64_t N = 0;
+  for (int i = 0; i < ms.nseg; ++i) N += ms.nrows[i];
+  const Side none{nullptr, nullptr, 0};
+  const uint32_t* c0 = static_cast<const uint32_t*>(ms.codes[0]);
+  const uint32_t* m0 = static_cast<const uint32_t*>(ms.meta[0]);
+#define CALL(b, g) gemv_dispatch<b, g>(c0, m0, N, K, x, x_dtype, 1, y0, yb, s, none, &ms)
   switch (bits * 100 + group) {
     case 232: return CALL(2, 32); case 264: return CALL(2, 64);
     case 332: return CALL(3, 32); case 364: return CALL(3, 64);

@@ -7,6 +7,20 @@
 
 namespace qg {
 
+// Up to four group-RTN matrices with one K, width and group size that share
+// x, multiplied in one launch; start[i] is the first launch row of matrix i
+// (INT_MAX for i >= nseg).
+struct MultiSegs {
+  const void* codes[4];
+  const void* meta[4];
+  void* y[4];
+  int64_t nrows[4];
+  int start[4];
+  int nseg;
+};
+hipError_t launch_gemv_group_multi(const MultiSegs& ms, int64_t K, int bits, int group, const void* x,
+                                   int x_dtype, void* y0, int y_dtype, hipStream_t s);
+
 // status word shared by the packers (per device)
 int* pack_status_ptr(hipError_t* err);
 

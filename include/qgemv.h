@@ -114,6 +114,21 @@ int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K,
                 int bits, int group, const void* x, int x_dtype, int64_t B,
                 void* y, int y_dtype, hipStream_t stream);
 
+/* Several group-RTN matrices that share K, bits, group and the input x
+ * (a decoder layer's q, k, v or its gate and up projections), multiplied in
+ * one launch for B = 1 (one launch per matrix for B > 1): y_i = x W_i^T for
+ * each entry of mats (a HOST array of 1..4 entries; each codes/meta/y as in
+ * qgemv_group, y_i [B][N_i]).  Same limits and dtypes as qgemv_group; the
+ * sum of the N_i is below 2^31.  Asynchronous. */
+typedef struct qgroup_mat {
+  const void* codes;
+  const void* meta;
+  int64_t N;
+  void* y;
+} qgroup_mat;
+int qgemv_group_multi(const qgroup_mat* mats, int count, int64_t K, int bits, int group,
+                      const void* x, int x_dtype, int64_t B, int y_dtype, hipStream_t stream);
+
 /* ------------------------------------------- group RTN with outlier columns
  * Mixed decomposition ("Métodos de cuantización de LLM...", opening and
  * LLM.int8() paragraph: about 0.1 % of the hidden dimensions carry values up

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -97,6 +97,16 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemv_binlr(good, good, good, good, 64, 128, 16, good, cg.Q_BF16, 1, good, cg.Q_F32,
                            P(0), 1 << 20, s) == cg.Q_EWORKSPACE
     assert lib.qpack_binlr(good, good, 64, 128, 0, good, good, s) == cg.Q_EINVAL
+    # grouped GEMV: count and per-matrix checks
+    mats = (cg.qgroup_mat * 5)(*[cg.qgroup_mat(0x10000, 0x10000, 64, 0x10000) for _ in range(5)])
+    assert lib.qgemv_group_multi(mats, 5, 128, 4, 32, good, cg.Q_BF16, 1, cg.Q_F32, s) == cg.Q_EINVAL
+    assert lib.qgemv_group_multi(mats, 0, 128, 4, 32, good, cg.Q_BF16, 1, cg.Q_F32, s) == cg.Q_EINVAL
+    mats[1].codes = 0x10004
+    assert lib.qgemv_group_multi(mats, 2, 128, 4, 32, good, cg.Q_BF16, 1, cg.Q_F32, s) == cg.Q_EALIGN
+    mats[1].codes = 0x10000
+    mats[2].N = 0
+    assert lib.qgemv_group_multi(mats, 3, 128, 4, 32, good, cg.Q_BF16, 1, cg.Q_F32, s) == cg.Q_EINVAL
+    assert lib.qgemv_group_multi(mats, 2, 100, 4, 32, good, cg.Q_BF16, 1, cg.Q_F32, s) == cg.Q_EINVAL
     # outlier columns: count limits, workspace, alignment
     assert cg.qgroup_outlier_ws(8192, 8) == (8192 + 256) * 4
     assert cg.qgroup_outlier_ws(100, 3) == (100 + 4) * 4
