@@ -328,12 +328,18 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         def f(i):
             c, m, sd = pool[i % len(pool)]
             cg.qgemv_group_outlier(c, m, sd, idx, N, K, bits, group, x, y=y)
+
+        def f_plain(i):   # the same codes without the side term, timed just before
+            c, m, _ = pool[i % len(pool)]
+            cg.qgemv_group(c, m, N, K, bits, group, x, y=y)
+        _, ev_plain = time_launches(f_plain, steps, warm, period=len(pool))
         wall, ev = time_launches(f, steps, warm, period=len(pool))
         gbs = nbytes * steps / ev / 1e9
         del pool
         torch.cuda.empty_cache()
         return {"us": round(ev / steps * 1e6, 3), "GB/s": round(gbs, 1),
-                "pct_hbm_peak": round(100 * gbs / 8000.0, 2), "bytes": nbytes, "n_out": n_out}
+                "pct_hbm_peak": round(100 * gbs / 8000.0, 2), "bytes": nbytes, "n_out": n_out,
+                "plain_gemv_us_same_pool": round(ev_plain / steps * 1e6, 3)}
 
     for B in (1, 16):
         rows[f"gemv_4b_g64_gate_outlier8_B{B}"] = outlier_row(W_gate, 4, 64, 8, B)
