@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqgemv.so")
 ARCH = os.environ.get("QGEMV_ARCH", "gfx950")
 
-SOURCES = ["capi.hip", "pack.hip", "gemv_group.hip", "gemv_binlr.hip", "gemm_prefill.hip"]
+SOURCES = ["capi.hip", "pack.hip", "gemv_group.hip", "gemv_binlr.hip", "gemm_prefill.hip", "gemm_prefill_outlier.hip"]
 
 CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

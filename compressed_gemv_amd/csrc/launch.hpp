@@ -59,6 +59,9 @@ hipError_t launch_gemm_group(const uint32_t* codes, const uint32_t* meta, int64_
                              int64_t K, int bits, int group, const uint16_t* X, int64_t M,
                              void* Y, int y_dtype, hipStream_t s,
                              const uint16_t* side = nullptr, const int32_t* oidx = nullptr, int n_out = 0);
+hipError_t launch_gemm_group_outlier(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
+                                     int bits, int group, const uint16_t* X, int64_t M, void* Y, int y_dtype,
+                                     hipStream_t s, const uint16_t* side, const int32_t* oidx, int n_out);
 hipError_t launch_gemm_binlr(const uint32_t* ubits, const uint32_t* vtbits,
                              const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
                              int64_t r, const uint16_t* X, int64_t M, void* Y, int y_dtype,

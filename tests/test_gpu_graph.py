@@ -74,3 +74,40 @@ def test_graph_prefill(gpu):
     g = _capture(lambda: gpu.qgemm_prefill(w, X, Y=Y))
     xs = [dev_bf16(gen_x_bf16(M, K, rng_for(88, i))) for i in range(3)]
     _check_replays(g, Y, lambda: gpu.qgemm_prefill(w, X), xs, X)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_graph_gemv_outlier(gpu, B):
+    say(f"graph gemv_group_outlier B={B}")
+    N, K = 600, 2048
+    W = gen_weights(N, K, rng_for(89, B), outliers=True)
+    codes, meta, side, idx = gpu.qpack_group_outlier(dev(W), 4, 64, 4)
+    x = dev_bf16(gen_x_bf16(B, K, rng_for(90, 0)))
+    y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    g = _capture(lambda: gpu.qgemv_group_outlier(codes, meta, side, idx, N, K, 4, 64, x, y=y))
+    xs = [dev_bf16(gen_x_bf16(B, K, rng_for(91, i))) for i in range(3)]
+    _check_replays(g, y, lambda: gpu.qgemv_group_outlier(codes, meta, side, idx, N, K, 4, 64, x), xs, x)
+
+
+def test_graph_gemv_multi(gpu):
+    say("graph gemv_group_multi")
+    K = 2048
+    mats = []
+    for i, N in enumerate([500, 64, 64]):
+        c, m = gpu.qpack_group(dev(gen_weights(N, K, rng_for(92, i), outliers=True)), 3, 32)
+        mats.append((c, m, N))
+    x = dev_bf16(gen_x_bf16(1, K, rng_for(93, 0)))
+    ys = [torch.empty((1, n), dtype=torch.float32, device=x.device) for _, _, n in mats]
+    out = torch.empty(sum(n for _, _, n in mats), dtype=torch.float32, device=x.device)
+
+    def run(dst):
+        gpu.qgemv_group_multi(mats, K, 3, 32, x, ys=ys)
+        torch.cat([y.reshape(-1) for y in ys], out=dst)
+    g = _capture(lambda: run(out))
+    xs = [dev_bf16(gen_x_bf16(1, K, rng_for(94, i))) for i in range(3)]
+
+    def eager():
+        ref = torch.empty_like(out)
+        run(ref)
+        return ref
+    _check_replays(g, out, eager, xs, x)
