@@ -19,6 +19,9 @@ Sources (web pages, cited by title and section):
   * "Métodos de cuantización de LLM...", opening and LLM.int8() paragraph:
     about 0.1 % of the hidden dimensions hold values up to 20x larger; they
     run in FP16 while the rest runs at low precision, results added.
+  * "TurboQuant: cuantizar modelos grandes...", introduction and
+    "Compresión por bloques": block compression with a shared dictionary,
+    a compressed codebook per group.
   * "AirLLM corre un modelo 70B en una GPU de 4GB", "Por qué es lento":
     time per token ~ bytes moved / bandwidth (the roofline the metric uses).
 
@@ -32,8 +35,9 @@ Modules:
   product  explicit W-hat, fp64 products, the normalized error metric
   sizes    byte counts and bits per weight
   outlier  outlier channels kept aside in fp16, the rest group RTN
+  codebook group codes read through a per-group book of a shared dictionary
 
 Parity status: every function here is pinned by tests under tests/ marked
 "not gpu" (bounds, brute force, closed forms, special cases, page figures).
 """
-from . import rtn, fmt, binlr, product, sizes, outlier  # noqa: F401
+from . import rtn, fmt, binlr, product, sizes, outlier, codebook  # noqa: F401
