@@ -19,6 +19,7 @@ __all__ = [
     "QError", "load", "lib_path", "q_abi_version", "q_format_version", "q_status_str",
     "qgroup_sizes", "qpack_group", "qunpack_group", "qgemv_group",
     "qgroup_outlier_ws", "qpack_group_outlier", "qgemv_group_outlier", "qgemv_group_multi",
+    "qcodebook_default", "qpack_group_cb", "qgemv_group_cb",
     "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr",
     "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
 ]
@@ -79,6 +80,9 @@ def load() -> ctypes.CDLL:
         "qgemv_group_multi": (I32, [ctypes.POINTER(qgroup_mat), I32, I64, I32, I32, P, I32, I64, I32, P]),
         "qpack_group_outlier": (I32, [P, I64, I64, I32, I32, I64, P, P, P, P, P, ctypes.c_size_t, P]),
         "qgemv_group_outlier": (I32, [P, P, P, P, I64, I64, I64, I32, I32, P, I32, I64, P, I32, P]),
+        "qcodebook_default": (I32, [I32, P, ctypes.POINTER(ctypes.c_int)]),
+        "qpack_group_cb": (I32, [P, I64, I64, I32, I32, P, I32, P, P, P, P]),
+        "qgemv_group_cb": (I32, [P, P, P, P, I32, I64, I64, I32, I32, P, I32, I64, P, I32, P]),
         "qbinlr_sizes": (I32, [I64, I64, I64, I64, SZ, SZ, SZ]),
         "qpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
         "qunpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
@@ -226,6 +230,43 @@ def qgemv_group_outlier(codes, meta, side, idx, N: int, K: int, bits: int, group
     _check(load().qgemv_group_outlier(_ptr(codes), _ptr(meta), _ptr(side), _ptr(idx), idx.numel(), N, K, bits,
                                       group, _ptr(x), _dtype_code(x), B, _ptr(y), _dtype_code(y),
                                       _stream(stream)), "qgemv_group_outlier")
+    return y
+
+
+# ------------------------------------------------- group codes with codebooks
+def qcodebook_default(bits: int) -> torch.Tensor:
+    """The library's default dictionary for b-bit codes: uint8 [8][2^b] (host)."""
+    L = 1 << bits
+    out = torch.zeros((8, L), dtype=torch.uint8)
+    n = ctypes.c_int()
+    _check(load().qcodebook_default(bits, ctypes.c_void_p(out.data_ptr()), ctypes.byref(n)), "qcodebook_default")
+    return out[: n.value]
+
+
+def qpack_group_cb(W: torch.Tensor, bits: int, group: int, books: torch.Tensor, stream=None):
+    """(codes, meta, book_ids uint8[N][K/g]) for fp32 W[N][K] with the
+    dictionary books (uint8 [D][2^b], on the device)."""
+    _need_cuda(W, books)
+    N, K = W.shape
+    cb, mb = qgroup_sizes(N, K, bits, group)
+    codes = torch.empty(cb, dtype=torch.uint8, device=W.device)
+    meta = torch.empty(mb // 4, dtype=torch.int32, device=W.device)
+    ids = torch.empty((N, K // group), dtype=torch.uint8, device=W.device)
+    _check(load().qpack_group_cb(_ptr(W), N, K, bits, group, _ptr(books), books.shape[0], _ptr(codes),
+                                 _ptr(meta), _ptr(ids), _stream(stream)), "qpack_group_cb")
+    return codes, meta, ids
+
+
+def qgemv_group_cb(codes, meta, book_ids, books, N: int, K: int, bits: int, group: int, x: torch.Tensor,
+                   y: Optional[torch.Tensor] = None, y_dtype=torch.float32, stream=None):
+    """y[B][N] = x W_hat^T with w_hat = s * books[id][q] / 2^(7-b) + o."""
+    _need_cuda(codes, meta, book_ids, books, x, y)
+    B = x.shape[0] if x.dim() == 2 else 1
+    if y is None:
+        y = torch.empty((B, N), dtype=y_dtype, device=x.device)
+    _check(load().qgemv_group_cb(_ptr(codes), _ptr(meta), _ptr(book_ids), _ptr(books), books.shape[0], N, K,
+                                 bits, group, _ptr(x), _dtype_code(x), B, _ptr(y), _dtype_code(y),
+                                 _stream(stream)), "qgemv_group_cb")
     return y
 
 

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqgemv.so")
 ARCH = os.environ.get("QGEMV_ARCH", "gfx950")
 
-SOURCES = ["capi.hip", "pack.hip", "gemv_group.hip", "gemv_binlr.hip", "gemm_prefill.hip", "gemm_prefill_outlier.hip"]
+SOURCES = ["capi.hip", "pack.hip", "gemv_group.hip", "gemv_binlr.hip", "gemm_prefill.hip", "gemm_prefill_outlier.hip",
+           "gemv_codebook.hip"]
 
 CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

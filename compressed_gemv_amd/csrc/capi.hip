@@ -6,6 +6,7 @@
 
 #include "launch.hpp"
 
+#include <math.h>
 #include <stdint.h>
 
 namespace {
@@ -35,6 +36,14 @@ int dtype_ok(int d) { return d == Q_F32 || d == Q_BF16; }
 // 64 lanes x UI units x 32 inputs (UI = 4 for bf16 rows longer than 16384,
 // 2 for fp32 activations).
 int64_t gemv_b1_max_k(int x_dtype) { return x_dtype == Q_F32 ? 8 * 64 * 2 * 32 : 8 * 64 * 4 * 32; }
+
+// codebooks: 2..4-bit codes, 1..16 books
+int cb_args_ok(int64_t N, int64_t K, int bits, int group, const uint8_t* books, int n_books) {
+  const int st = group_args_ok(N, K, bits, group);
+  if (st != Q_OK) return st;
+  if (bits > 4 || !books || n_books < 1 || n_books > 16) return Q_EINVAL;
+  return Q_OK;
+}
 
 }  // namespace
 
@@ -212,6 +221,69 @@ int qgemv_group_outlier(const void* codes, const void* meta, const uint16_t* sid
   return hip_status(qg::launch_gemv_group(static_cast<const uint32_t*>(codes),
                                           static_cast<const uint32_t*>(meta), N, K, bits, group,
                                           x, x_dtype, B, y, y_dtype, stream, side, idx, (int)n_out));
+}
+
+int qcodebook_default(int bits, uint8_t* books, int* n_books) {
+  if (bits < 2 || bits > 4 || !books) return Q_EINVAL;
+  // 8 monotone warps of the uniform grid c = j (j = 0..L-1, L = 2^bits):
+  // uniform; centre-dense m(1 + sign(t)|t|^g), t = 2j/(L-1) - 1,
+  // m = (L-1)/2, g = 1.5, 2, 3; minimum-dense (L-1) a^g, a = j/(L-1),
+  // g = 1.5, 2.5; and their mirrors (L-1)(1 - (1-a)^g).  Entry =
+  // c * 2^(7-bits) rounded to nearest, ties to even.
+  const int L = 1 << bits;
+  const double top = (double)(L - 1), m = top / 2.0, unit = (double)(1 << (7 - bits));
+  const double gc[3] = {1.5, 2.0, 3.0}, gs[2] = {1.5, 2.5};
+  for (int j = 0; j < L; ++j) {
+    const double t = 2.0 * j / top - 1.0, a = j / top;
+    double c[8];
+    c[0] = j;
+    for (int i = 0; i < 3; ++i) c[1 + i] = m * (1.0 + (t < 0 ? -1.0 : 1.0) * pow(fabs(t), gc[i]));
+    for (int i = 0; i < 2; ++i) {
+      c[4 + i] = top * pow(a, gs[i]);
+      c[6 + i] = top * (1.0 - pow(1.0 - a, gs[i]));
+    }
+    for (int d = 0; d < 8; ++d) books[d * L + j] = (uint8_t)nearbyint(c[d] * unit);
+  }
+  if (n_books) *n_books = 8;
+  return Q_OK;
+}
+
+int qpack_group_cb(const float* W, int64_t N, int64_t K, int bits, int group, const uint8_t* books, int n_books,
+                   void* codes, void* meta, uint8_t* book_ids, hipStream_t stream) {
+  const int st = cb_args_ok(N, K, bits, group, books, n_books);
+  if (st != Q_OK) return st;
+  if (!W || !codes || !meta || !book_ids) return Q_EINVAL;
+  if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(meta, 16)) return Q_EALIGN;
+  hipError_t e;
+  int* status = qg::pack_status_ptr(&e);
+  if (!status) return Q_EHIP;
+  if ((e = qg::launch_zero_status(status, stream)) != hipSuccess) return Q_EHIP;
+  e = qg::launch_pack_group_cb(W, N, K, bits, group, books, n_books, static_cast<uint32_t*>(codes),
+                               static_cast<uint32_t*>(meta), book_ids, status, stream);
+  if (e != hipSuccess) return Q_EHIP;
+  int host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return Q_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return Q_EHIP;
+  return (host & 2) ? Q_EINVAL : (host ? Q_ERANGE : Q_OK);
+}
+
+int qgemv_group_cb(const void* codes, const void* meta, const uint8_t* book_ids, const uint8_t* books,
+                   int n_books, int64_t N, int64_t K, int bits, int group, const void* x, int x_dtype,
+                   int64_t B, void* y, int y_dtype, hipStream_t stream) {
+  const int st = cb_args_ok(N, K, bits, group, books, n_books);
+  if (st != Q_OK) return st;
+  if (!codes || !meta || !book_ids || !x || !y) return Q_EINVAL;
+  if (B < 1 || B > 16) return Q_EINVAL;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return Q_EINVAL;
+  if (!aligned(codes, 16) || !aligned(meta, 16) || !aligned(x, 16) || !aligned(y, 4))
+    return Q_EALIGN;
+  if (B == 1 && K > gemv_b1_max_k(x_dtype)) return Q_EUNSUPPORTED;
+  if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
+  if (N > INT32_MAX || K > INT32_MAX) return Q_EUNSUPPORTED;
+  return hip_status(qg::launch_gemv_group_cb(static_cast<const uint32_t*>(codes),
+                                             static_cast<const uint32_t*>(meta), book_ids, books, n_books,
+                                             N, K, bits, group, x, x_dtype, B, y, y_dtype, stream));
 }
 
 int qbinlr_sizes(int64_t N, int64_t K, int64_t r, int64_t B, size_t* ubits_bytes,

@@ -46,6 +46,12 @@ hipError_t launch_pack_group_outlier(const float* W, int64_t N, int64_t K, int b
                                      uint32_t* codes, uint32_t* meta, uint16_t* side, int32_t* idx,
                                      void* ws, int* status, hipStream_t s);
 size_t pack_group_outlier_ws_bytes(int64_t K);
+hipError_t launch_pack_group_cb(const float* W, int64_t N, int64_t K, int bits, int group, const uint8_t* books,
+                                int n_books, uint32_t* codes, uint32_t* meta, uint8_t* book_ids, int* status,
+                                hipStream_t s);
+hipError_t launch_gemv_group_cb(const uint32_t* codes, const uint32_t* meta, const uint8_t* book_ids,
+                                const uint8_t* books, int n_books, int64_t N, int64_t K, int bits, int group,
+                                const void* x, int x_dtype, int64_t B, void* y, int y_dtype, hipStream_t s);
 
 // Workspace bytes per batch row of qgemv_binlr: the stage-2 table and the
 // stage-1 partial sums.

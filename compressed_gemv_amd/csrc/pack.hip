@@ -107,6 +107,32 @@ __device__ __forceinline__ void place_code(uint32_t (&w)[B], int c, uint32_t q) 
   }
 }
 
+// Group constants of the RTN grid with L = 2^b - 1 steps: o = largest fp16
+// <= min, s = smallest fp16 >= (max - o)/L in fp64 (fp16 bits).  A
+// non-finite weight or a constant outside the fp16 range sets *bad and
+// returns zero constants.
+template <int G>
+__device__ __forceinline__ void group_constants(const float (&v)[G], uint32_t L, uint32_t* obits,
+                                                uint32_t* sbits, bool* bad) {
+  bool b = false;
+  float mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const uint32_t bits = __float_as_uint(v[i]);
+    if ((bits & 0x7F800000u) == 0x7F800000u) b = true;
+    mn = v[i] < mn ? v[i] : mn;
+    mx = v[i] > mx ? v[i] : mx;
+  }
+  uint32_t ob = 0, sb = 0;
+  if (!b) {
+    ob = f16_round_down_bits((double)mn, &b);
+    const double o = f16_bits_to_f64(ob);
+    sb = f16_round_up_bits(((double)mx - o) / (double)L, &b);
+  }
+  if (b) { ob = 0; sb = 0; }
+  *obits = ob; *sbits = sb; *bad = b;
+}
+
 // zmask (optional): bit k set -> input channel k is encoded as 0 (the
 // outlier channels of the mixed decomposition).
 template <int B, int G>
@@ -137,22 +163,9 @@ __global__ __launch_bounds__(256) void pack_group_kernel(const float* __restrict
     }
   }
   bool bad = false;
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    const uint32_t bits = __float_as_uint(v[i]);
-    if ((bits & 0x7F800000u) == 0x7F800000u) bad = true;
-    mn = v[i] < mn ? v[i] : mn;
-    mx = v[i] > mx ? v[i] : mx;
-  }
   uint32_t obits = 0, sbits = 0;
-  if (!bad) {
-    obits = f16_round_down_bits((double)mn, &bad);
-    const double o = f16_bits_to_f64(obits);
-    const double vs = ((double)mx - o) / (double)L;
-    sbits = f16_round_up_bits(vs, &bad);
-  }
-  if (bad) { atomicOr(status, 1); obits = 0; sbits = 0; }
+  group_constants<G>(v, L, &obits, &sbits, &bad);
+  if (bad) atomicOr(status, 1);
   meta[gid] = sbits | (obits << 16);
   const double o = f16_bits_to_f64(obits);
   const double s = f16_bits_to_f64(sbits);
@@ -246,6 +259,113 @@ hipError_t launch_pack_group(const float* W, int64_t N, int64_t K, int bits, int
                              uint32_t* codes, uint32_t* meta, int* status, hipStream_t s) {
 #define CALL(b, g) pack_group_t<b, g>(W, N, K, codes, meta, status, nullptr, s)
   QG_DISPATCH_BG(bits, group, CALL)
+#undef CALL
+}
+
+// -------------------------------------------------- per-group codebooks
+// Codes read through per-group books ("TurboQuant: cuantizar modelos
+// grandes...", introduction and "Compresión por bloques": block compression
+// with a shared dictionary, a compressed codebook per group).  One thread per
+// group: the RTN constants s, o; u = (w - o)/s in fp64; for every book of
+// the dictionary (levels c = e/2^(7-b), staged in LDS as fp64) each weight's
+// nearest level (ties to the even index, then the lower) and the book's
+// squared error summed in increasing k; the least-error book (ties to the
+// lower index) and its codes.  s == 0: book 0, codes 0.
+template <int B, int G>
+__global__ __launch_bounds__(256) void pack_group_cb_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                           const uint8_t* __restrict__ books, int nb,
+                                                           uint32_t* __restrict__ codes, uint32_t* __restrict__ meta,
+                                                           uint8_t* __restrict__ book_ids, int* status) {
+  constexpr int NL = 1 << B;
+  __shared__ double lv[16 * NL];
+  for (int t = threadIdx.x; t < nb * NL; t += blockDim.x) {
+    if (books[t] > 127) atomicOr(status, 2);   // level above the 7-bit grid
+    lv[t] = ldexp((double)books[t], B - 7);
+  }
+  __syncthreads();
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t Gn = K / G;
+  if (gid >= N * Gn) return;
+  const int64_t n = gid / Gn, j = gid % Gn;
+  const float* src = W + n * K + j * G;
+  float v[G];
+#pragma unroll
+  for (int i = 0; i < G / 4; ++i) {
+    const float4 t = reinterpret_cast<const float4*>(src)[i];
+    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+  bool bad = false;
+  uint32_t obits = 0, sbits = 0;
+  group_constants<G>(v, (uint32_t)(NL - 1), &obits, &sbits, &bad);
+  if (bad) atomicOr(status, 1);
+  meta[gid] = sbits | (obits << 16);
+  const double o = f16_bits_to_f64(obits);
+  const double s = f16_bits_to_f64(sbits);
+  double u[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) u[i] = s != 0.0 ? ((double)v[i] - o) / s : 0.0;
+  // nearest level of book d for u; distance in *dist
+  auto nearest = [&](int d, double x, double* dist) {
+    int bj = 0;
+    double bd = fabs(x - lv[d * NL]);
+    for (int jj = 1; jj < NL; ++jj) {
+      const double a = fabs(x - lv[d * NL + jj]);
+      if (a < bd || (a == bd && (bj & 1) && !(jj & 1))) { bd = a; bj = jj; }
+    }
+    *dist = bd;
+    return bj;
+  };
+  int best = 0;
+  if (s != 0.0) {
+    double best_err = 0.0;
+    for (int d = 0; d < nb; ++d) {
+      double err = 0.0;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        double a;
+        (void)nearest(d, u[i], &a);
+        err = err + a * a;
+      }
+      if (d == 0 || err < best_err) { best_err = err; best = d; }
+    }
+  }
+  book_ids[gid] = (uint8_t)best;
+#pragma unroll
+  for (int uu = 0; uu < G / 32; ++uu) {
+    uint32_t w[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) w[i] = 0u;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      double a;
+      const uint32_t q = s != 0.0 ? (uint32_t)nearest(best, u[uu * 32 + c], &a) : 0u;
+      place_code<B>(w, c, q);
+    }
+    uint32_t* dst = codes + ((n * (K / 32)) + j * (G / 32) + uu) * B;
+#pragma unroll
+    for (int i = 0; i < B; ++i) dst[i] = w[i];
+  }
+}
+
+template <int B, int G>
+static hipError_t pack_group_cb_t(const float* W, int64_t N, int64_t K, const uint8_t* books, int nb,
+                                  uint32_t* codes, uint32_t* meta, uint8_t* book_ids, int* status, hipStream_t s) {
+  const int64_t blocks = (N * (K / G) + 255) / 256;
+  hipLaunchKernelGGL((pack_group_cb_kernel<B, G>), dim3((unsigned)blocks), dim3(256), 0, s, W, N, K, books, nb,
+                     codes, meta, book_ids, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_group_cb(const float* W, int64_t N, int64_t K, int bits, int group, const uint8_t* books,
+                                int n_books, uint32_t* codes, uint32_t* meta, uint8_t* book_ids, int* status,
+                                hipStream_t s) {
+#define CALL(b, g) pack_group_cb_t<b, g>(W, N, K, books, n_books, codes, meta, book_ids, status, s)
+  switch (bits * 100 + group) {
+    case 232: return CALL(2, 32); case 264: return CALL(2, 64);
+    case 332: return CALL(3, 32); case 364: return CALL(3, 64);
+    case 432: return CALL(4, 32); case 464: return CALL(4, 64);
+    default: return hipErrorInvalidValue;
+  }
 #undef CALL
 }
 

@@ -161,6 +161,40 @@ int qgemv_group_outlier(const void* codes, const void* meta, const uint16_t* sid
                         int64_t n_out, int64_t N, int64_t K, int bits, int group, const void* x,
                         int x_dtype, int64_t B, void* y, int y_dtype, hipStream_t stream);
 
+/* ------------------------------------------ group codes with codebooks
+ * Per-group codebooks from a shared dictionary ("TurboQuant: cuantizar
+ * modelos grandes para que quepan en local", introduction and "Compresión
+ * por bloques": block compression with a shared dictionary; blocks of 32 or
+ * 64 weights keep a scale and an offset and a compressed codebook per
+ * group).  A dictionary holds n_books (1..16) books of 2^bits byte entries
+ * e <= 127, bits = 2, 3 or 4, books[d][j] at byte d*2^bits + j.  Each group
+ * stores s and o of the group RTN above and the index of one book in
+ * book_ids[N][K/group] (bytes, row-major); code q stands for the level
+ * e[q] / 2^(7-bits) in code units, w_hat = s * e[q] / 2^(7-bits) + o.  codes
+ * and meta have the format-1 layout and sizes of qgroup_sizes.
+ *
+ * Default dictionary (host only): 8 books of 2^bits entries written to
+ * books (8 * 2^bits bytes): the uniform grid e_j = j * 2^(7-bits) (book 0;
+ * a dictionary of that book alone is qpack_group), three books denser near
+ * the middle of the group's range, two denser near its minimum and their
+ * two mirrors.  *n_books = 8 when n_books is not NULL. */
+int qcodebook_default(int bits, uint8_t* books, int* n_books);
+/* Encode W[N][K] (fp32, device): per group the RTN constants s, o,
+ * u = (w - o)/s in fp64, for every book each weight's nearest level (ties
+ * to the even, then the lower index) and the squared error summed in
+ * increasing k in fp64; the least-error book (ties to the lower index) and
+ * its codes.  books: device.  W, codes, meta 16-byte aligned.  Synchronizes
+ * `stream`; Q_ERANGE as qpack_group, Q_EINVAL if a book entry exceeds 127
+ * (outputs then undefined). */
+int qpack_group_cb(const float* W, int64_t N, int64_t K, int bits, int group, const uint8_t* books,
+                   int n_books, void* codes, void* meta, uint8_t* book_ids, hipStream_t stream);
+/* Decode GEMV y[b][n] = sum_k (s * e[book][q] / 2^(7-bits) + o) x[b][k],
+ * fp32 accumulation; same arguments, limits and dtypes as qgemv_group plus
+ * book_ids and books (device, entries <= 127 as qpack_group_cb checks).
+ * Asynchronous. */
+int qgemv_group_cb(const void* codes, const void* meta, const uint8_t* book_ids, const uint8_t* books,
+                   int n_books, int64_t N, int64_t K, int bits, int group, const void* x, int x_dtype,
+                   int64_t B, void* y, int y_dtype, hipStream_t stream);
 /* ------------------------------------------------------------- binary LR
  * Sizes of Ubits, VTbits and of the qgemv_binlr workspace for batch B
  * (host only).  r >= 1, N >= 1, K >= 1, 1 <= B <= 16. */

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import compressed_gemv_amd as cg
@@ -29,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -134,3 +135,31 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemm_prefill(ctypes.byref(w), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
     wb = cg.qweight(cg.Q_FMT_BINLR, 64, 128, 0, 0, None, None, 16, 0x10000, 0x10000, 0x10000, 0x10000)
     assert lib.qgemm_prefill(ctypes.byref(wb), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EWORKSPACE
+    # codebooks: widths 2..4, 1..16 books, books and ids present
+    assert lib.qpack_group_cb(good, 64, 128, 5, 32, good, 8, good, good, good, s) == cg.Q_EINVAL
+    assert lib.qpack_group_cb(good, 64, 128, 4, 32, good, 0, good, good, good, s) == cg.Q_EINVAL
+    assert lib.qpack_group_cb(good, 64, 128, 4, 32, good, 17, good, good, good, s) == cg.Q_EINVAL
+    assert lib.qpack_group_cb(good, 64, 128, 4, 32, P(0), 8, good, good, good, s) == cg.Q_EINVAL
+    assert lib.qpack_group_cb(good, 64, 128, 4, 32, good, 8, good, good, P(0), s) == cg.Q_EINVAL
+    assert lib.qpack_group_cb(good, 64, 128, 4, 32, good, 8, odd, good, good, s) == cg.Q_EALIGN
+    assert lib.qgemv_group_cb(good, good, P(0), good, 8, 64, 128, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32,
+                              s) == cg.Q_EINVAL
+    assert lib.qgemv_group_cb(good, good, good, good, 8, 64, 128, 6, 32, good, cg.Q_BF16, 1, good, cg.Q_F32,
+                              s) == cg.Q_EINVAL
+    assert lib.qgemv_group_cb(good, odd, good, good, 8, 64, 128, 2, 32, good, cg.Q_BF16, 1, good, cg.Q_F32,
+                              s) == cg.Q_EALIGN
+    assert lib.qgemv_group_cb(good, good, good, good, 8, 64, 128, 3, 64, good, cg.Q_F32, 4, good, cg.Q_F32,
+                              s) == cg.Q_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_default_codebooks_match_the_oracle(lib, bits):
+    """The library's default dictionary is the one the oracle defines."""
+    from oracle import codebook
+    assert np.array_equal(cg.qcodebook_default(bits).numpy(), codebook.default_dictionary(bits))
+
+
+def test_default_codebooks_reject_widths(lib):
+    buf = (ctypes.c_uint8 * 256)()
+    assert lib.qcodebook_default(5, buf, None) == cg.Q_EINVAL
+    assert lib.qcodebook_default(4, None, None) == cg.Q_EINVAL
