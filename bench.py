@@ -38,7 +38,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-KERNEL_SOURCES = ["compressed_gemv_amd/csrc/gemv_group.hip", "compressed_gemv_amd/csrc/common.hpp"]
+KERNEL_SOURCES = ["compressed_gemv_amd/csrc/gemv_kernels.hpp", "compressed_gemv_amd/csrc/gemv_group.hip",
+                  "compressed_gemv_amd/csrc/common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_b1_gate_8192x28672_4b_g64.md")
 
 
@@ -344,6 +345,36 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
     for B in (1, 16):
         rows[f"gemv_4b_g64_gate_outlier8_B{B}"] = outlier_row(W_gate, 4, 64, 8, B)
         log(f"outlier B{B}:", rows[f"gemv_4b_g64_gate_outlier8_B{B}"])
+    # the headline shape with per-group codebooks (default 8-book dictionary);
+    # bytes = codes + meta + one book id per group
+    def codebook_row(W, bits, group, B):
+        N, K = W.shape
+        books = cg.qcodebook_default(bits).to(dev)
+        codes, meta, ids = cg.qpack_group_cb(to_dev(W), bits, group, books)
+        nbytes = codes.numel() + meta.numel() * 4 + ids.numel()
+        pool = pool_of((codes, meta, ids), nbytes)
+        x = bf16(layer_x(K, B))
+        y = torch.empty((B, N), dtype=torch.float32, device=dev)
+
+        def f(i):
+            c, m, k = pool[i % len(pool)]
+            cg.qgemv_group_cb(c, m, k, books, N, K, bits, group, x, y=y)
+
+        def f_plain(i):   # the same codes read as plain RTN codes, timed just before
+            c, m, _ = pool[i % len(pool)]
+            cg.qgemv_group(c, m, N, K, bits, group, x, y=y)
+        _, ev_plain = time_launches(f_plain, steps, warm, period=len(pool))
+        wall, ev = time_launches(f, steps, warm, period=len(pool))
+        gbs = nbytes * steps / ev / 1e9
+        del pool
+        torch.cuda.empty_cache()
+        return {"us": round(ev / steps * 1e6, 3), "GB/s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / 8000.0, 2), "bytes": nbytes, "books": int(books.shape[0]),
+                "plain_gemv_us_same_pool": round(ev_plain / steps * 1e6, 3)}
+
+    for bits, B in [(4, 1), (4, 16), (2, 1)]:
+        rows[f"gemv_{bits}b_g64_gate_codebook_B{B}"] = codebook_row(W_gate, bits, 64, B)
+        log(f"codebook {bits}b B{B}:", rows[f"gemv_{bits}b_g64_gate_codebook_B{B}"])
     # mixed widths at batch 8 (MLP shape)
     for bits in (3, 2):
         rows[f"gemv_{bits}b_g32_gate_B8"] = gemv_row("gate", W_gate, bits, 32, 8)
@@ -383,10 +414,14 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
     ub, vb = cg.qpack_binlr(to_dev(U), to_dev(V))
     s1d, s2d = to_dev(s1.view(np.int16)), to_dev(s2.view(np.int16))
     wb = cg.make_qweight_binlr(ub, vb, s1d, s2d, N, K, 4096)
+    books = cg.qcodebook_default(4).to(dev)
+    cc, mc, kc = cg.qpack_group_cb(to_dev(W_gate), 4, 64, books)
+    wcb = cg.make_qweight_group(cc, mc, N, K, 4, 64, book_ids=kc, books=books)
     for M in (512, 4096):
         X = bf16(layer_x(K, M, config=5))
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        for label, w, flops in [("rtn_4b_g64", wq, 2.0 * M * N * K), ("binlr_r4096", wb, 2.0 * M * 4096 * (K + N))]:
+        for label, w, flops in [("rtn_4b_g64", wq, 2.0 * M * N * K), ("binlr_r4096", wb, 2.0 * M * 4096 * (K + N)),
+                                ("codebook_4b_g64", wcb, 2.0 * M * N * K)]:
             ws = None
             need = cg.qgemm_prefill_ws(w, M)
             if need:

@@ -50,6 +50,7 @@ class qweight(ctypes.Structure):
         ("r", ctypes.c_int64), ("ubits", ctypes.c_void_p), ("vtbits", ctypes.c_void_p),
         ("s1", ctypes.c_void_p), ("s2", ctypes.c_void_p),
         ("side", ctypes.c_void_p), ("oidx", ctypes.c_void_p), ("n_out", ctypes.c_int64),
+        ("book_ids", ctypes.c_void_p), ("books", ctypes.c_void_p), ("n_books", ctypes.c_int),
     ]
 
 
@@ -317,13 +318,17 @@ def qgemv_binlr(ubits, vtbits, s1, s2, N: int, K: int, r: int, x: torch.Tensor,
 
 
 # ------------------------------------------------------------------ prefill
-def make_qweight_group(codes, meta, N, K, bits, group, side=None, idx=None) -> qweight:
-    """A qweight descriptor (optionally with outlier side columns); it keeps
-    references to the tensors it points into."""
+def make_qweight_group(codes, meta, N, K, bits, group, side=None, idx=None, book_ids=None,
+                       books=None) -> qweight:
+    """A qweight descriptor (optionally with outlier side columns, or with
+    per-group books of a dictionary); it keeps references to the tensors it
+    points into."""
     n_out = 0 if idx is None else idx.numel()
     w = qweight(Q_FMT_GROUP, N, K, bits, group, codes.data_ptr(), meta.data_ptr(), 0, None, None, None, None,
-                side.data_ptr() if n_out else None, idx.data_ptr() if n_out else None, n_out)
-    w._tensors = (codes, meta, side, idx)
+                side.data_ptr() if n_out else None, idx.data_ptr() if n_out else None, n_out,
+                None if book_ids is None else book_ids.data_ptr(), None if books is None else books.data_ptr(),
+                0 if books is None else books.shape[0])
+    w._tensors = (codes, meta, side, idx, book_ids, books)
     return w
 
 

@@ -378,6 +378,15 @@ int qgemm_prefill(const qweight* w, const void* X, int x_dtype, int64_t M, void*
     if (!aligned(w->codes, 16) || !aligned(w->meta, 4) || !aligned(w->side, 2) || !aligned(w->oidx, 4))
       return Q_EALIGN;
     if (w->N * w->n_out > INT32_MAX) return Q_EUNSUPPORTED;
+    if (w->books) {
+      if (w->n_out > 0 || !w->book_ids) return Q_EINVAL;   // codebooks come without outlier columns
+      const int cst = cb_args_ok(w->N, w->K, w->bits, w->group, w->books, w->n_books);
+      if (cst != Q_OK) return cst;
+      return hip_status(qg::launch_gemm_group_cb(static_cast<const uint32_t*>(w->codes),
+                                                 static_cast<const uint32_t*>(w->meta), w->book_ids, w->books,
+                                                 w->n_books, w->N, w->K, w->bits, w->group,
+                                                 static_cast<const uint16_t*>(X), M, Y, y_dtype, stream));
+    }
     return hip_status(qg::launch_gemm_group(static_cast<const uint32_t*>(w->codes),
                                             static_cast<const uint32_t*>(w->meta), w->N, w->K,
                                             w->bits, w->group, static_cast<const uint16_t*>(X),

@@ -25,6 +25,7 @@
 // T = bf16((X (.) s2) V) into the workspace, then Y = (T U^T) (.) s1.
 #pragma once
 
+#include "codebook.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,6 +37,7 @@ namespace qg {
 // into 16 bf16 pairs in k order.
 template <int BITS, int G>
 struct DecRTN {
+  static constexpr int kDictWords = 0;     // no per-kernel table
   const uint32_t* codes; const uint32_t* meta; int N; int U;
   struct Raw { uint32_t w[BITS]; uint32_t m; };
   __device__ __forceinline__ void load(int n, int u, Raw& r) const {
@@ -70,6 +72,7 @@ struct DecRTN {
 };
 
 struct DecBIN {
+  static constexpr int kDictWords = 0;
   const uint32_t* bits; int N; int Wn;   // rows, words per stored row
   struct Raw { uint32_t w; };
   __device__ __forceinline__ void load(int n, int u, Raw& r) const {
@@ -88,6 +91,56 @@ struct DecBIN {
       const uint32_t hi = nw << (30 - 2 * i);
       outp[i] = (lo & 0x00008000u) | (hi & 0x80000000u) | 0x3F803F80u;
     }
+  }
+};
+
+// Group codes read through per-group books: the dictionary (<= 16 books of
+// 2^BITS bytes) is staged in LDS once per workgroup (bind), each unit's book
+// id is loaded with its meta word, and a unit decodes to
+// fl32(s e[q] 2^(BITS-7) + o) rounded to bf16, as DecRTN does for s q + o.
+template <int BITS, int G>
+struct DecCB {
+  static constexpr int kDictWords = 64;
+  const uint32_t* codes; const uint32_t* meta; const uint8_t* ids; const uint8_t* dict; int nb; int N; int U;
+  const uint32_t* lds_dict;
+  CbConst kc;
+  struct Raw { uint32_t w[BITS]; uint32_t m; uint32_t k; };
+  // stage the dictionary (all threads of the workgroup; a barrier follows)
+  __device__ __forceinline__ void bind(uint32_t* lds, int tid, int nt) {
+    for (int t = tid; t < (nb << BITS); t += nt) reinterpret_cast<uint8_t*>(lds)[t] = dict[t];
+    lds_dict = lds;
+    kc = cb_consts();
+  }
+  __device__ __forceinline__ void load(int n, int u, Raw& r) const {
+    const int GN = U * 32 / G;
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
+    const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(ids, (uint32_t)((size_t)N * GN));
+    const bool ok = n < N && u < U;
+    const uint32_t co = ok ? (uint32_t)(n * U + u) * (BITS * 4) : 0xFFFFFF00u;
+    const uint32_t go = ok ? (uint32_t)(n * GN + (u * 32) / G) : 0x3FFFFFC0u;
+    buf_load_unit<BITS, 0>(crs, co, 0u, r.w);
+    r.m = __builtin_amdgcn_raw_buffer_load_b32(mrs, go * 4, 0u, 0);
+    r.k = __builtin_amdgcn_raw_buffer_load_b8(krs, go, 0u, 0);
+  }
+  __device__ __forceinline__ void decode(const Raw& r, uint32_t (&outp)[16]) const {
+    uint32_t T[4] = {0u, 0u, 0u, 0u};
+    const uint32_t* tp = lds_dict + ((r.k & 15u) << BITS) / 4;   // ids < 16 (packer)
+#pragma unroll
+    for (int i = 0; i < (1 << BITS) / 4; ++i) T[i] = tp[i];
+    uint32_t pr[16];
+    decode_unit_cb<BITS>(r.w, T, pr, kc);
+    const float s = f16_bits_to_f32(r.m & 0xFFFFu) * (1.0f / (float)(1 << (7 - BITS)));
+    const float o = f16_bits_to_f32(r.m >> 16);
+    float wv[32];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const PairInfo pi = Unit<BITS>::pair(k);
+      wv[pi.ca] = __builtin_fmaf(bf16_lo_to_f32(pr[k]) - 128.0f, s, o);
+      wv[pi.cb] = __builtin_fmaf(bf16_hi_to_f32(pr[k]) - 128.0f, s, o);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) outp[i] = cvt_pk_bf16(wv[2 * i], wv[2 * i + 1]);
   }
 };
 
@@ -123,7 +176,9 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   constexpr int WU = TN * UPR / NT;                   // weight units per thread and step
   static_assert(AC >= 1 && WU >= 1 && NT % (TK / 8) == 0, "tile configuration");
   __shared__ __align__(16) uint16_t lds[2][(TM + TN) * LP];
+  __shared__ __align__(16) uint32_t dict_lds[Dec::kDictWords > 0 ? Dec::kDictWords : 1];
   const int tid = threadIdx.x;
+  if constexpr (Dec::kDictWords > 0) dec.bind(dict_lds, tid, NT);   // staged before the first decode
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   int bid = blockIdx.x;
@@ -250,6 +305,7 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   Stage s0, s1;
   gload(0, s0);
   gload(1, s1);
+  if constexpr (Dec::kDictWords > 0) __syncthreads();   // dictionary staged
   lstore(0, s0, 0);
   __syncthreads();
   // Whole pairs of steps, so the loop has one exit: with an odd step count

@@ -6,6 +6,20 @@
 // plain codes.
 #include "gemv_kernels.hpp"
 
+// Tile choice of the B = 1 kernel for codebook decode.  The lookups about
+// double the VALU work per code (4-bit: ~3 instructions per code against
+// ~1.4), so two waves per SIMD (2048 waves) hide the dependent permute
+// chains better than the plain kernel's one; rows per stage as for plain
+// codes.  Measured on MI355X over the gate, q and down shapes (sums of the
+// three, us): 4-bit 83.0 -> 73.3, 3-bit 71.2 -> 67.7, 2-bit 55.1 -> 55.0.
+// QG_CB_WAVES / QG_CB_RPW force one choice.
+#ifndef QG_CB_WAVES
+#define QG_CB_WAVES 0
+#endif
+#ifndef QG_CB_RPW
+#define QG_CB_RPW 0
+#endif
+
 namespace qg {
 
 template <int BITS, int G>
@@ -16,8 +30,8 @@ static hipError_t gemv_cb_dispatch(const uint32_t* codes, const uint32_t* meta, 
   if (B == 1) {
     if (x_dtype == 0)
       return gemv_b1_t<BITS, G, true, 2, 2, true>(codes, meta, N, K, x, y, y_bf16, s, 2048, none, nullptr, bk);
-    constexpr int kRpw = BITS == 3 ? 2 : 1;
-    const int64_t waves = BITS == 2 ? 2048 : 1024;
+    constexpr int kRpw = QG_CB_RPW ? QG_CB_RPW : (BITS == 3 ? 2 : 1);
+    const int64_t waves = QG_CB_WAVES ? QG_CB_WAVES : 2048;
     return gemv_b1_t<BITS, G, false, 4, kRpw, true>(codes, meta, N, K, x, y, y_bf16, s, waves, none, nullptr, bk);
   }
   if (x_dtype != 1) return hipErrorInvalidValue;

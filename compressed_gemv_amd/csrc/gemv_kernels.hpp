@@ -24,6 +24,7 @@
 //    and feeds two v_mfma_f32_16x16x32_bf16 with the activations (bf16) as
 //    the 16-column operand, fp32 accumulation.
 #pragma once
+#include "codebook.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,68 +49,6 @@
 #endif
 
 namespace qg {
-
-// ----------------------------------------------------- per-group codebooks
-// Codebook format ("TurboQuant: cuantizar modelos grandes...", introduction
-// and "Compresión por bloques": block compression with a shared dictionary,
-// a compressed codebook per group): a dictionary of up to 16 books of 2^b
-// byte entries e <= 127 is shared by a matrix; each group names one book in
-// a byte, and code q of the group stands for the level e[q] / 2^(7-b) in
-// code units, w_hat = s * e[q] / 2^(7-b) + o.
-struct Books { const uint8_t* ids; const uint8_t* dict; int n; };   // n = 0: plain codes
-
-// Decode one unit through its book T (the book's entries as bytes, little
-// endian) into the 16 bf16x2 operands of decode_unit, 128 + e[q] per lane in
-// the pair order of Unit<B> (every pair lands at mantissa bit 0).  The
-// lookups are byte permutes: each code becomes a selector byte of
-// v_perm_b32 over the table words.  2-bit codes: four codes per permute,
-// one table word.  3-bit codes: one pair per permute over two table words.
-// 4-bit codes: four codes per two permutes (entries 0..7 and 8..15) plus a
-// third that keeps, byte by byte, the half that code bit 3 names.  A final
-// permute or masked OR writes the 0x43 high bytes (bf16 128 + e, exact for
-// e <= 127).
-template <int B>
-__device__ __forceinline__ void decode_unit_cb(const uint32_t (&w)[B], const uint32_t (&T)[4],
-                                               uint32_t (&pr)[16]) {
-  constexpr uint32_t k43 = 0x43434343u;
-  if constexpr (B == 2) {
-#pragma unroll
-    for (int wi = 0; wi < 2; ++wi)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // bytes: low-half fields j, j+4, high-half fields j, j+4
-        const uint32_t r = __builtin_amdgcn_perm(0u, T[0], (w[wi] >> (2 * j)) & 0x03030303u);
-        pr[8 * wi + j] = __builtin_amdgcn_perm(k43, r, 0x04020400u);
-        pr[8 * wi + j + 4] = __builtin_amdgcn_perm(k43, r, 0x04030401u);
-      }
-  } else if constexpr (B == 3) {
-    auto look = [&](uint32_t t) { return (__builtin_amdgcn_perm(T[1], T[0], t) & 0x00FF00FFu) | 0x43004300u; };
-#pragma unroll
-    for (int k = 0; k < 15; ++k) pr[k] = look((w[k / 5] >> (3 * (k % 5))) & 0x00070007u);
-    uint32_t t = 0;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) t |= (w[i] >> (15 - i)) & (0x00010001u << i);
-    pr[15] = look(t);
-  } else {
-    static_assert(B == 4, "codebooks hold 4, 8 or 16 entries");
-    auto look = [&](uint32_t t) {
-      const uint32_t a = t & 0x07070707u;
-      const uint32_t lo = __builtin_amdgcn_perm(T[1], T[0], a);
-      const uint32_t hi = __builtin_amdgcn_perm(T[3], T[2], a);
-      return __builtin_amdgcn_perm(hi, lo, ((t >> 1) & 0x04040404u) | 0x03020100u);
-    };
-#pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-      // bytes: low-half fields 0, 2, high-half fields 0, 2 (then 1, 3)
-      const uint32_t r0 = look(w[wi] & 0x0F0F0F0Fu);
-      const uint32_t r1 = look((w[wi] >> 4) & 0x0F0F0F0Fu);
-      pr[4 * wi + 0] = __builtin_amdgcn_perm(k43, r0, 0x04020400u);
-      pr[4 * wi + 2] = __builtin_amdgcn_perm(k43, r0, 0x04030401u);
-      pr[4 * wi + 1] = __builtin_amdgcn_perm(k43, r1, 0x04020400u);
-      pr[4 * wi + 3] = __builtin_amdgcn_perm(k43, r1, 0x04030401u);
-    }
-  }
-}
 
 // ------------------------------------------------------------------ B = 1
 // OUT: outlier side columns (fp16 side[N][n_out] at input channels oidx[],
@@ -324,6 +263,8 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   }
 
   const uint32_t bias = opaque_bias();
+  CbConst kc{};
+  if constexpr (CB) kc = cb_consts();
   auto compute = [&](const uint32_t (&w)[RPW][UI][BITS], const uint32_t (&m)[RPW][UI], const uint32_t (&sv)[RPW],
                      const uint32_t (&kk)[RPW][UI], int row0, int m0) {
 #pragma unroll
@@ -343,7 +284,7 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 #pragma unroll
             for (int i = 0; i < (1 << BITS) / 4; ++i) T[i] = tp[i];
           }
-          decode_unit_cb<BITS>(w[r][it], T, pr);
+          decode_unit_cb<BITS>(w[r][it], T, pr, kc);
         } else {
           decode_unit<BITS>(w[r][it], pr, bias);
         }
@@ -488,6 +429,8 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     }
   };
   using UN = UnitH<BITS>;
+  CbConst kc{};
+  if constexpr (CB) kc = cb_consts();
   auto compute = [&](const Buf& b) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
@@ -499,7 +442,7 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
         const uint32_t* tp = dict + ((b.k[t] & 15u) << BITS) / 4;   // ids < 16 (packer)
 #pragma unroll
         for (int i = 0; i < (1 << BITS) / 4; ++i) T[i] = tp[i];
-        decode_unit_cb<BITS>(b.w[t], T, pr);
+        decode_unit_cb<BITS>(b.w[t], T, pr, kc);
         const float sc = s * (1.0f / (float)(1 << (7 - BITS)));
 #pragma unroll
         for (int k = 0; k < 16; ++k) {

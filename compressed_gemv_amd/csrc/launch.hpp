@@ -49,6 +49,9 @@ size_t pack_group_outlier_ws_bytes(int64_t K);
 hipError_t launch_pack_group_cb(const float* W, int64_t N, int64_t K, int bits, int group, const uint8_t* books,
                                 int n_books, uint32_t* codes, uint32_t* meta, uint8_t* book_ids, int* status,
                                 hipStream_t s);
+hipError_t launch_gemm_group_cb(const uint32_t* codes, const uint32_t* meta, const uint8_t* book_ids,
+                                const uint8_t* books, int n_books, int64_t N, int64_t K, int bits, int group,
+                                const uint16_t* X, int64_t M, void* Y, int y_dtype, hipStream_t s);
 hipError_t launch_gemv_group_cb(const uint32_t* codes, const uint32_t* meta, const uint8_t* book_ids,
                                 const uint8_t* books, int n_books, int64_t N, int64_t K, int bits, int group,
                                 const void* x, int x_dtype, int64_t B, void* y, int y_dtype, hipStream_t s);

@@ -71,7 +71,7 @@ enum {
 enum { Q_F32 = 0, Q_BF16 = 1, Q_F16 = 2 };
 enum { Q_FMT_GROUP = 1, Q_FMT_BINLR = 2 };
 
-#define Q_ABI_VERSION 2
+#define Q_ABI_VERSION 3
 #define Q_FORMAT_VERSION 1
 
 int q_abi_version(void);
@@ -237,6 +237,9 @@ typedef struct qweight {
   const uint16_t* side;       /* Q_FMT_GROUP outlier columns [N][n_out] fp16, or NULL */
   const int32_t* oidx;        /* their input channels [n_out] */
   int64_t n_out;              /* 0..64; 0 = none */
+  const uint8_t* book_ids;    /* Q_FMT_GROUP with codebooks: [N][K/group] book per group, or NULL */
+  const uint8_t* books;       /* the dictionary (n_books x 2^bits bytes), or NULL for plain codes */
+  int n_books;                /* 1..16 when books is set (bits 2..4, n_out = 0) */
 } qweight;
 
 /* Workspace bytes qgemm_prefill needs for M token rows (host only). */
@@ -244,7 +247,8 @@ int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes);
 
 /* Prefill GEMM Y[M][N] = X[M][K] W_hat^T with X bf16 (x_dtype Q_BF16).
  * Group RTN with n_out > 0 adds X[:, oidx] side^T before the output
- * rounding.
+ * rounding; with books set, the codes are read through the per-group books
+ * as in qgemv_group_cb.
  * Weight tiles are decoded to bf16 in LDS and fed to MFMA with fp32
  * accumulation.  Group RTN: one pass.  Binary: T = (X (.) s2) V into the
  * workspace as bf16, then Y = (T U^T) (.) s1 ("70B en 4GB de VRAM...",

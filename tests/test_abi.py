@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_versions_and_status_strings(lib):
-    assert cg.q_abi_version() == 2
+    assert cg.q_abi_version() == 3
     assert cg.q_format_version() == 1
     for st in (0, -1, -2, -3, -4, -5, -6):
         s = cg.q_status_str(st)
@@ -135,6 +135,17 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemm_prefill(ctypes.byref(w), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
     wb = cg.qweight(cg.Q_FMT_BINLR, 64, 128, 0, 0, None, None, 16, 0x10000, 0x10000, 0x10000, 0x10000)
     assert lib.qgemm_prefill(ctypes.byref(wb), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EWORKSPACE
+    # codebook prefill: ids present, no outlier columns with books, widths 2..4
+    wc = cg.qweight(cg.Q_FMT_GROUP, 64, 128, 4, 32, 0x10000, 0x10000, 0, None, None, None, None, None, None, 0,
+                    None, 0x10000, 8)
+    assert lib.qgemm_prefill(ctypes.byref(wc), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
+    wc.book_ids = 0x10000
+    wc.bits = 5
+    assert lib.qgemm_prefill(ctypes.byref(wc), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
+    wc.bits, wc.n_books = 4, 17
+    assert lib.qgemm_prefill(ctypes.byref(wc), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
+    wc.n_books, wc.n_out, wc.side, wc.oidx = 8, 2, 0x10000, 0x10000
+    assert lib.qgemm_prefill(ctypes.byref(wc), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
     # codebooks: widths 2..4, 1..16 books, books and ids present
     assert lib.qpack_group_cb(good, 64, 128, 5, 32, good, 8, good, good, good, s) == cg.Q_EINVAL
     assert lib.qpack_group_cb(good, 64, 128, 4, 32, good, 0, good, good, good, s) == cg.Q_EINVAL

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import check_err, dev, dev_bf16, host, say
+from gpu_util import PREFILL_RTN_BOUND, check_err, dev, dev_bf16, host, say
 from workloads import gen_weights, gen_x_bf16, gen_x_f32, layer_weights, layer_x, rng_for
 
 pytestmark = pytest.mark.gpu
@@ -130,3 +130,41 @@ def test_full_gate_shape(gpu, bits):
         Xv = oracle.product.bf16_to_f64(X)
         err = check_err(y[:, rows], oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv))
         say(f"  B={B} err={err:.2e}")
+
+
+@pytest.mark.parametrize("bits,M,N,K", [(4, 40, 257, 512), (3, 64, 300, 1024), (2, 40, 257, 512),
+                                        (4, 4000, 7900, 1024)])
+def test_prefill(gpu, bits, M, N, K):
+    """Both tile shapes (the last takes the 256 x 256 tile); the weight tiles
+    are bf16, so the bound is the prefill RTN bound; sampled rows and columns
+    at the large size."""
+    say(f"codebook prefill b={bits} M={M} N={N} K={K}")
+    books = _random_books(bits, 40 + bits)
+    W = gen_weights(N, K, rng_for(377, M + bits), outliers=True)
+    c, m, k = gpu.qpack_group_cb(dev(W), bits, 64, dev(books))
+    bd = dev(books)
+    X = gen_x_bf16(M, K, rng_for(378, M))
+    w = gpu.make_qweight_group(c, m, N, K, bits, 64, book_ids=k, books=bd)
+    Y = host(gpu.qgemm_prefill(w, dev_bf16(X)))
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(17).choice(M, min(M, 24), replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(18).choice(N, 48, replace=False)]))
+    q, s, o, ids = oracle.codebook.quantize(W[cols], bits, 64, books)
+    assert np.array_equal(host(k)[cols], ids)
+    W_hat = oracle.codebook.dequantize(q, s, o, ids, books, bits, 64)
+    Xv = oracle.product.bf16_to_f64(X[rows])
+    err = check_err(Y[np.ix_(rows, cols)], oracle.product.matmul_ref(W_hat, Xv),
+                    oracle.product.abs_denominator(W_hat, Xv), PREFILL_RTN_BOUND)
+    say(f"  err={err:.2e}")
+
+
+def test_prefill_bf16_output(gpu):
+    M, N, K = 64, 300, 1024
+    books = oracle.codebook.default_dictionary(4)
+    W = gen_weights(N, K, rng_for(379, 0), outliers=True)
+    c, m, k, W_hat = _check_pack(gpu, W, 4, 32, books)
+    X = gen_x_bf16(M, K, rng_for(380, 0))
+    w = gpu.make_qweight_group(c, m, N, K, 4, 32, book_ids=k, books=dev(books))
+    Y = host(gpu.qgemm_prefill(w, dev_bf16(X), y_dtype=torch.bfloat16))
+    Xv = oracle.product.bf16_to_f64(X)
+    check_err(Y, oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv),
+              PREFILL_RTN_BOUND + 2.0 ** -8)
