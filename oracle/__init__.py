@@ -22,6 +22,9 @@ Sources (web pages, cited by title and section):
   * "TurboQuant: cuantizar modelos grandes...", introduction and
     "Compresión por bloques": block compression with a shared dictionary,
     a compressed codebook per group.
+  * "70B en 4GB de VRAM...", section 3 (TurboQuant): random rotation, one
+    Lloyd-Max codebook for the known coordinate law, 1-bit QJL residual for
+    unbiased inner products.
   * "AirLLM corre un modelo 70B en una GPU de 4GB", "Por qué es lento":
     time per token ~ bytes moved / bandwidth (the roofline the metric uses).
 
@@ -36,8 +39,9 @@ Modules:
   sizes    byte counts and bits per weight
   outlier  outlier channels kept aside in fp16, the rest group RTN
   codebook group codes read through a per-group book of a shared dictionary
+  turboquant key-cache quantizer: rotation, Lloyd-Max coordinates, QJL signs
 
 Parity status: every function here is pinned by tests under tests/ marked
 "not gpu" (bounds, brute force, closed forms, special cases, page figures).
 """
-from . import rtn, fmt, binlr, product, sizes, outlier, codebook  # noqa: F401
+from . import rtn, fmt, binlr, product, sizes, outlier, codebook, turboquant  # noqa: F401
