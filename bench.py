@@ -375,6 +375,58 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
     for bits, B in [(4, 1), (4, 16), (2, 1)]:
         rows[f"gemv_{bits}b_g64_gate_codebook_B{B}"] = codebook_row(W_gate, bits, 64, B)
         log(f"codebook {bits}b B{B}:", rows[f"gemv_{bits}b_g64_gate_codebook_B{B}"])
+    # attention logits from quantized keys (random rotation + Lloyd-Max codes
+    # + QJL sign bits): 8 KV heads x 131072 keys (a 128K context), 4 grouped
+    # queries per head; bytes = codes + signs + norms.  For scale, the same
+    # logits from unquantized keys with torch (bf16 and fp32 batched matmul).
+    def kv_row(bits, H=8, n=131072, nq=4):
+        rng = np.random.default_rng(np.random.SeedSequence([0, 9, bits]))
+        Pi = to_dev(cg.qtq_rotation(rng.standard_normal((128, 128))))
+        S = to_dev(rng.standard_normal((128, 128)))
+        delta, table = cg.qtq_centroids(128, bits - 1)
+        Kf = torch.randn((H * n, 128), device=dev, generator=torch.Generator(device=dev).manual_seed(bits))
+        c, sg, nm = cg.qtq_quant_keys(Kf, bits, Pi, S, delta, table)
+        Qv = torch.randn((H, nq, 128), device=dev, generator=torch.Generator(device=dev).manual_seed(100 + bits))
+        nbytes = c.numel() * 4 + sg.numel() * 4 + nm.numel() * 4
+        pool = pool_of((c, sg, nm), nbytes)
+        out = torch.empty((H, nq, n), dtype=torch.float32, device=dev)
+        ws = torch.empty(H * nq * 132 * 4, dtype=torch.uint8, device=dev)
+
+        def f(i):
+            a, b_, m_ = pool[i % len(pool)]
+            cg.qtq_logits(a, b_, m_, n, H, bits, delta, table, Pi, S, Qv, out=out, ws=ws)
+        wall, ev = time_launches(f, 100, 10, period=len(pool))
+        del pool
+        torch.cuda.empty_cache()
+        us = ev / 100 * 1e6
+        base = {}
+        Kh = Kf.view(H, n, 128)
+        for label, dt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+            kd = Kh.to(dt).contiguous()
+            qt = Qv.to(dt).transpose(1, 2).contiguous()
+            kp = pool_of((kd,), kd.numel() * kd.element_size())
+            for i in range(3):
+                torch.bmm(kp[i % len(kp)][0], qt)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(40):
+                torch.bmm(kp[i % len(kp)][0], qt)
+            e1.record()
+            torch.cuda.synchronize()
+            base[label] = round(e0.elapsed_time(e1) * 1e3 / 40, 2)
+            del kp, kd
+            torch.cuda.empty_cache()
+        del Kf
+        return {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "pct_hbm_peak": round(100 * nbytes / (us * 1e-6) / 8e12, 2), "bytes": nbytes,
+                "keys_per_s": round(H * n / (us * 1e-6) / 1e9, 2), "unit_keys_per_s": "1e9",
+                "torch_bf16_keys_us": base["bf16"], "torch_fp32_keys_us": base["fp32"],
+                "speedup_vs_fp32": round(base["fp32"] / us, 2), "speedup_vs_bf16": round(base["bf16"] / us, 2)}
+
+    for kb in (4, 3):
+        rows[f"kv_logits_{kb}bit_h8_n131072_q4"] = kv_row(kb)
+        log(f"kv logits {kb}-bit:", rows[f"kv_logits_{kb}bit_h8_n131072_q4"])
     # mixed widths at batch 8 (MLP shape)
     for bits in (3, 2):
         rows[f"gemv_{bits}b_g32_gate_B8"] = gemv_row("gate", W_gate, bits, 32, 8)

@@ -20,6 +20,7 @@ __all__ = [
     "qgroup_sizes", "qpack_group", "qunpack_group", "qgemv_group",
     "qgroup_outlier_ws", "qpack_group_outlier", "qgemv_group_outlier", "qgemv_group_multi",
     "qcodebook_default", "qpack_group_cb", "qgemv_group_cb",
+    "qtq_centroids", "qtq_rotation", "qtq_quant_keys", "qtq_logits",
     "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr",
     "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
 ]
@@ -84,6 +85,12 @@ def load() -> ctypes.CDLL:
         "qcodebook_default": (I32, [I32, P, ctypes.POINTER(ctypes.c_int)]),
         "qpack_group_cb": (I32, [P, I64, I64, I32, I32, P, I32, P, P, P, P]),
         "qgemv_group_cb": (I32, [P, P, P, P, I32, I64, I64, I32, I32, P, I32, I64, P, I32, P]),
+        "qtq_centroids": (I32, [I32, I32, ctypes.POINTER(ctypes.c_float), P]),
+        "qtq_rotation": (I32, [I32, P, P]),
+        "qtq_sizes": (I32, [I64, I32, SZ, SZ, SZ]),
+        "qtq_quant_keys": (I32, [P, I64, I32, P, P, ctypes.c_float, P, P, P, P, P]),
+        "qtq_logits_ws": (I32, [I64, I64, SZ]),
+        "qtq_logits": (I32, [P, P, P, I64, I64, I32, ctypes.c_float, P, P, P, P, I64, P, P, ctypes.c_size_t, P]),
         "qbinlr_sizes": (I32, [I64, I64, I64, I64, SZ, SZ, SZ]),
         "qpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
         "qunpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
@@ -269,6 +276,62 @@ def qgemv_group_cb(codes, meta, book_ids, books, N: int, K: int, bits: int, grou
                                  bits, group, _ptr(x), _dtype_code(x), B, _ptr(y), _dtype_code(y),
                                  _stream(stream)), "qgemv_group_cb")
     return y
+
+
+# ------------------------------------------------- key-cache quantization
+def qtq_centroids(d: int, mbits: int):
+    """(delta, table uint8 numpy [2^mbits]) on the 7-bit centroid grid."""
+    import numpy as np
+    t = np.zeros(1 << mbits, dtype=np.uint8)
+    dl = ctypes.c_float()
+    _check(load().qtq_centroids(d, mbits, ctypes.byref(dl), t.ctypes.data_as(ctypes.c_void_p)), "qtq_centroids")
+    return dl.value, t
+
+
+def qtq_rotation(G):
+    """Q of G = QR, diag(R) > 0, for a host fp64 array G [d][d]."""
+    import numpy as np
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    out = np.empty_like(G)
+    _check(load().qtq_rotation(G.shape[0], G.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p)),
+           "qtq_rotation")
+    return out
+
+
+def qtq_quant_keys(K: torch.Tensor, bits: int, Pi: torch.Tensor, S: torch.Tensor, delta: float, table,
+                   stream=None):
+    """(codes int32[n*4*(bits-1)], signs int32[n][4], norms int32[n]) for fp32 keys K[n][128]."""
+    import numpy as np
+    _need_cuda(K, Pi, S)
+    n = K.shape[0]
+    cb, sb, nb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().qtq_sizes(n, bits, ctypes.byref(cb), ctypes.byref(sb), ctypes.byref(nb)), "qtq_sizes")
+    codes = torch.empty(cb.value // 4, dtype=torch.int32, device=K.device)
+    signs = torch.empty((n, 4), dtype=torch.int32, device=K.device)
+    norms = torch.empty(n, dtype=torch.int32, device=K.device)
+    t = np.ascontiguousarray(table, dtype=np.uint8)
+    _check(load().qtq_quant_keys(_ptr(K), n, bits, _ptr(Pi), _ptr(S), float(delta), t.ctypes.data_as(ctypes.c_void_p),
+                                 _ptr(codes), _ptr(signs), _ptr(norms), _stream(stream)), "qtq_quant_keys")
+    return codes, signs, norms
+
+
+def qtq_logits(codes, signs, norms, n: int, heads: int, bits: int, delta: float, table, Pi, S, Qv: torch.Tensor,
+               out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """out[heads][nq][n] fp32 logits for queries Qv[heads][nq][128] (fp32)."""
+    import numpy as np
+    _need_cuda(codes, signs, norms, Pi, S, Qv, out, ws)
+    nq = Qv.shape[1]
+    if out is None:
+        out = torch.empty((heads, nq, n), dtype=torch.float32, device=Qv.device)
+    if ws is None:
+        need = ctypes.c_size_t()
+        _check(load().qtq_logits_ws(heads, nq, ctypes.byref(need)), "qtq_logits_ws")
+        ws = torch.empty(need.value, dtype=torch.uint8, device=Qv.device)
+    t = np.ascontiguousarray(table, dtype=np.uint8)
+    _check(load().qtq_logits(_ptr(codes), _ptr(signs), _ptr(norms), n, heads, bits, float(delta),
+                             t.ctypes.data_as(ctypes.c_void_p), _ptr(Pi), _ptr(S), _ptr(Qv), nq, _ptr(out), _ptr(ws),
+                             ws.numel(), _stream(stream)), "qtq_logits")
+    return out
 
 
 # ---------------------------------------------------------------- binary LR

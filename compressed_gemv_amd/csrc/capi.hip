@@ -286,6 +286,108 @@ int qgemv_group_cb(const void* codes, const void* meta, const uint8_t* book_ids,
                                              N, K, bits, group, x, x_dtype, B, y, y_dtype, stream));
 }
 
+int qtq_centroids(int d, int mbits, float* delta, uint8_t* table) {
+  if (d < 3 || d > 65536 || mbits < 1 || mbits > 4 || !delta || !table) return Q_EINVAL;
+  double c[16];
+  qg::tq_lloyd_max(d, mbits, c);
+  const int L = 1 << mbits;
+  double cmax = 0.0;
+  for (int k = 0; k < L; ++k) cmax = fmax(cmax, fabs(c[k]));
+  const float dl = (float)(cmax / 63.0);
+  for (int k = 0; k < L; ++k) {
+    const double e = nearbyint(c[k] / (double)dl) + 64.0;
+    if (e < 1.0 || e > 127.0) return Q_ERANGE;
+    table[k] = (uint8_t)e;
+  }
+  *delta = dl;
+  return Q_OK;
+}
+
+int qtq_rotation(int d, const double* G, double* Pi) {
+  if (d < 1 || d > 4096 || !G || !Pi) return Q_EINVAL;
+  qg::tq_rotation(d, G, Pi);
+  for (int i = 0; i < d * d; ++i)
+    if (!isfinite(Pi[i])) return Q_ERANGE;   // G was singular
+  return Q_OK;
+}
+
+namespace {
+constexpr int kTqDim = 128;
+int tq_args_ok(int64_t n, int64_t heads, int bits, float delta, const uint8_t* table) {
+  if (n < 1 || heads < 1 || bits < 3 || bits > 4 || !table) return Q_EINVAL;
+  if (!(delta > 0.0f) || !isfinite(delta)) return Q_EINVAL;
+  // keys of one head are addressed through 32-bit buffer offsets
+  if (n * 64 >= ((int64_t)1 << 32) - 256 || n * heads > INT32_MAX || heads > 65535) return Q_EUNSUPPORTED;
+  const int L = 1 << (bits - 1);
+  for (int k = 0; k < L; ++k)
+    if (table[k] < 1 || table[k] > 127) return Q_EINVAL;
+  return Q_OK;
+}
+void tq_table_words(const uint8_t* t, int L, uint32_t* lo, uint32_t* hi) {
+  *lo = 0; *hi = 0;
+  for (int k = 0; k < L; ++k) {
+    if (k < 4) *lo |= (uint32_t)t[k] << (8 * k);
+    else *hi |= (uint32_t)t[k] << (8 * (k - 4));
+  }
+}
+}  // namespace
+
+int qtq_sizes(int64_t n, int bits, size_t* codes_bytes, size_t* signs_bytes, size_t* norms_bytes) {
+  if (n < 1 || bits < 3 || bits > 4) return Q_EINVAL;
+  if (codes_bytes) *codes_bytes = (size_t)(n * kTqDim * (bits - 1) / 8);
+  if (signs_bytes) *signs_bytes = (size_t)(n * kTqDim / 8);
+  if (norms_bytes) *norms_bytes = (size_t)(n * 4);
+  return Q_OK;
+}
+
+int qtq_quant_keys(const float* K, int64_t n, int bits, const double* Pi, const double* S, float delta,
+                   const uint8_t* table, void* codes, uint32_t* signs, uint32_t* norms, hipStream_t stream) {
+  const int st = tq_args_ok(n, 1, bits, delta, table);
+  if (st != Q_OK) return st;
+  if (!K || !Pi || !S || !codes || !signs || !norms) return Q_EINVAL;
+  if (!aligned(K, 4) || !aligned(Pi, 8) || !aligned(S, 8) || !aligned(codes, 4) || !aligned(signs, 4) ||
+      !aligned(norms, 4))
+    return Q_EALIGN;
+  uint32_t lo, hi;
+  tq_table_words(table, 1 << (bits - 1), &lo, &hi);
+  hipError_t e;
+  int* status = qg::pack_status_ptr(&e);
+  if (!status) return Q_EHIP;
+  if ((e = qg::launch_zero_status(status, stream)) != hipSuccess) return Q_EHIP;
+  e = qg::launch_tq_quant(K, n, bits - 1, Pi, S, delta, lo, hi, static_cast<uint32_t*>(codes), signs, norms,
+                          status, stream);
+  if (e != hipSuccess) return Q_EHIP;
+  int host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return Q_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return Q_EHIP;
+  return host ? Q_ERANGE : Q_OK;
+}
+
+int qtq_logits_ws(int64_t heads, int64_t nq, size_t* ws_bytes) {
+  if (heads < 1 || nq < 1 || nq > 65535 || heads > 65535 || !ws_bytes) return Q_EINVAL;
+  *ws_bytes = (size_t)(heads * nq * 132 * 4);
+  return Q_OK;
+}
+
+int qtq_logits(const void* codes, const uint32_t* signs, const uint32_t* norms, int64_t n, int64_t heads,
+               int bits, float delta, const uint8_t* table, const double* Pi, const double* S, const float* Qv,
+               int64_t nq, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = tq_args_ok(n, heads, bits, delta, table);
+  if (st != Q_OK) return st;
+  size_t need = 0;
+  if ((st = qtq_logits_ws(heads, nq, &need)) != Q_OK) return st;
+  if (!codes || !signs || !norms || !Pi || !S || !Qv || !out) return Q_EINVAL;
+  if (!ws || ws_bytes < need) return Q_EWORKSPACE;
+  if (!aligned(codes, 4) || !aligned(signs, 4) || !aligned(norms, 4) || !aligned(Pi, 8) || !aligned(S, 8) ||
+      !aligned(Qv, 4) || !aligned(out, 4) || !aligned(ws, 16))
+    return Q_EALIGN;
+  if (heads * nq * n > ((int64_t)1 << 40)) return Q_EUNSUPPORTED;
+  uint32_t lo, hi;
+  tq_table_words(table, 1 << (bits - 1), &lo, &hi);
+  return hip_status(qg::launch_tq_logits(static_cast<const uint32_t*>(codes), signs, norms, n, heads, bits - 1,
+                                         delta, lo, hi, Pi, S, Qv, nq, out, static_cast<uint32_t*>(ws), stream));
+}
+
 int qbinlr_sizes(int64_t N, int64_t K, int64_t r, int64_t B, size_t* ubits_bytes,
                  size_t* vtbits_bytes, size_t* ws_bytes) {
   if (N < 1 || K < 1 || r < 1 || N > kMaxDim || K > kMaxDim || r > kMaxDim) return Q_EINVAL;

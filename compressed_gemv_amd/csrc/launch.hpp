@@ -49,6 +49,15 @@ size_t pack_group_outlier_ws_bytes(int64_t K);
 hipError_t launch_pack_group_cb(const float* W, int64_t N, int64_t K, int bits, int group, const uint8_t* books,
                                 int n_books, uint32_t* codes, uint32_t* meta, uint8_t* book_ids, int* status,
                                 hipStream_t s);
+void tq_lloyd_max(int d, int m, double* c);
+void tq_rotation(int d, const double* G, double* Pi);
+hipError_t launch_tq_quant(const float* X, int64_t n, int mbits, const double* Pi, const double* S, float delta,
+                           uint32_t tab_lo, uint32_t tab_hi, uint32_t* codes, uint32_t* signs, uint32_t* norms,
+                           int* status, hipStream_t s);
+hipError_t launch_tq_logits(const uint32_t* codes, const uint32_t* signs, const uint32_t* norms, int64_t n,
+                            int64_t heads, int mbits, float delta, uint32_t tab_lo, uint32_t tab_hi,
+                            const double* Pi, const double* S, const float* Qv, int64_t nq, float* out,
+                            uint32_t* ws, hipStream_t s);
 hipError_t launch_gemm_group_cb(const uint32_t* codes, const uint32_t* meta, const uint8_t* book_ids,
                                 const uint8_t* books, int n_books, int64_t N, int64_t K, int bits, int group,
                                 const uint16_t* X, int64_t M, void* Y, int y_dtype, hipStream_t s);

@@ -652,4 +652,107 @@ hipError_t launch_unpack_binlr(const uint32_t* ubits, const uint32_t* vtbits, in
   return hipSuccess;
 }
 
+// ------------------------------------------------------- key-cache encoder
+// Inner-product key quantizer ("70B en 4GB de VRAM...", section 3,
+// TurboQuant): y = Pi x / |x| (random rotation), each coordinate to the
+// nearest stored Lloyd-Max centroid (M bits, ties to the lower index), the
+// residual r = y - c of the rotated unit vector, gamma = |r|, and the signs of
+// S r (bit 1 <-> >= 0).  One 64-lane workgroup per 128-dimensional key; every
+// sum runs in fp64 in increasing index order (contraction is off in this
+// file), so the codes and signs are those of any IEEE implementation of the
+// same steps.  Centroid k is delta * (e_k - 64), e_k the k-th byte of
+// (tab_lo, tab_hi).  Outputs: codes [n][4][M] (units of 32 coordinates in
+// the group-code layout), signs [n][4] (bit j of word w: coordinate 32w + j),
+// norms [n] = fp16 |x| | fp16 gamma << 16.
+template <int M>
+__global__ __launch_bounds__(64) void tq_quant_kernel(const float* __restrict__ X, const double* __restrict__ Pi,
+                                                      const double* __restrict__ S, double delta, uint32_t tab_lo,
+                                                      uint32_t tab_hi, uint32_t* __restrict__ codes,
+                                                      uint32_t* __restrict__ signs, uint32_t* __restrict__ norms,
+                                                      int* status) {
+  constexpr int D = 128, L = 1 << M;
+  __shared__ double xs[D], rs[D], sh[2];
+  __shared__ uint32_t cs[D], zs[D];
+  const int64_t key = blockIdx.x;
+  const int l = threadIdx.x;
+  double cv[L];
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    const uint32_t e = ((k < 4 ? tab_lo >> (8 * k) : tab_hi >> (8 * (k - 4)))) & 0xFFu;
+    cv[k] = delta * ((double)e - 64.0);
+  }
+  const float x0 = X[key * D + l], x1 = X[key * D + l + 64];
+  if (!isfinite(x0) || !isfinite(x1)) atomicOr(status, 1);
+  xs[l] = (double)x0;
+  xs[l + 64] = (double)x1;
+  __syncthreads();
+  if (l == 0) {
+    double a = 0.0;
+    for (int j = 0; j < D; ++j) a = a + xs[j] * xs[j];
+    sh[0] = sqrt(a);
+  }
+  __syncthreads();
+  const double nrm = sh[0], safe = nrm > 0.0 ? nrm : 1.0;
+  for (int h = 0; h < 2; ++h) {
+    const int i = l + 64 * h;
+    double a = 0.0;
+    for (int j = 0; j < D; ++j) a = a + xs[j] * Pi[i * D + j];
+    const double y = a / safe;
+    int best = 0;
+    double bd = fabs(y - cv[0]);
+#pragma unroll
+    for (int k = 1; k < L; ++k) {
+      const double dd = fabs(y - cv[k]);
+      if (dd < bd) { bd = dd; best = k; }
+    }
+    cs[i] = (uint32_t)best;
+    rs[i] = y - cv[best];
+  }
+  __syncthreads();
+  if (l == 0) {
+    double a = 0.0;
+    for (int j = 0; j < D; ++j) a = a + rs[j] * rs[j];
+    sh[1] = sqrt(a);
+  }
+  for (int h = 0; h < 2; ++h) {
+    const int i = l + 64 * h;
+    double a = 0.0;
+    for (int j = 0; j < D; ++j) a = a + rs[j] * S[i * D + j];
+    zs[i] = a >= 0.0 ? 1u : 0u;
+  }
+  __syncthreads();
+  if (l < 4) {
+    uint32_t w[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) w[i] = 0u;
+    uint32_t sg = 0u;
+    for (int c = 0; c < 32; ++c) {
+      place_code<M>(w, c, cs[32 * l + c]);
+      sg |= zs[32 * l + c] << c;
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) codes[(key * 4 + l) * M + i] = w[i];
+    signs[key * 4 + l] = sg;
+  }
+  if (l == 0) {
+    bool bad = false;
+    norms[key] = f16_rne_bits(sh[0], &bad) | (f16_rne_bits(sh[1], &bad) << 16);
+    if (bad) atomicOr(status, 1);
+  }
+}
+
+hipError_t launch_tq_quant(const float* X, int64_t n, int mbits, const double* Pi, const double* S, float delta,
+                           uint32_t tab_lo, uint32_t tab_hi, uint32_t* codes, uint32_t* signs, uint32_t* norms,
+                           int* status, hipStream_t s) {
+  if (mbits == 2)
+    hipLaunchKernelGGL((tq_quant_kernel<2>), dim3((unsigned)n), dim3(64), 0, s, X, Pi, S, (double)delta, tab_lo,
+                       tab_hi, codes, signs, norms, status);
+  else if (mbits == 3)
+    hipLaunchKernelGGL((tq_quant_kernel<3>), dim3((unsigned)n), dim3(64), 0, s, X, Pi, S, (double)delta, tab_lo,
+                       tab_hi, codes, signs, norms, status);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace qg

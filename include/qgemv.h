@@ -195,6 +195,53 @@ int qpack_group_cb(const float* W, int64_t N, int64_t K, int bits, int group, co
 int qgemv_group_cb(const void* codes, const void* meta, const uint8_t* book_ids, const uint8_t* books,
                    int n_books, int64_t N, int64_t K, int bits, int group, const void* x, int x_dtype,
                    int64_t B, void* y, int y_dtype, hipStream_t stream);
+/* ------------------------------------------------ key-cache quantization
+ * Inner-product quantizer for attention keys ("70B en 4GB de VRAM: la
+ * compresión neural de 2026, ¿es real?", section 3, TurboQuant): a random
+ * orthogonal rotation Pi makes every coordinate of a rotated unit vector
+ * follow one known law, so one Lloyd-Max codebook serves all keys with no
+ * per-block constants; one more bit per coordinate holds the signs of a
+ * Gaussian projection S of the residual, which makes the inner-product
+ * estimate unbiased.  Keys are 128-dimensional (d = 128).  bits = 3 or 4
+ * bits per coordinate: m = bits - 1 codebook bits plus the sign bit.
+ *   codes  [n][4][m] u32: per key, 4 units of 32 coordinates in the
+ *          group-code layout of m-bit codes (format 1).
+ *   signs  [n][4] u32: bit j of word w <-> coordinate 32w + j, 1 <-> >= 0.
+ *   norms  [n] u32: fp16 |x| in bits 0..15, fp16 gamma = |r| in 16..31.
+ * Centroid k = delta * (table[k] - 64) with table bytes 1..127 (a 7-bit
+ * grid; table is a HOST array of 2^m bytes, delta > 0).  Pi and S are
+ * row-major 128 x 128 fp64 DEVICE arrays.
+ *
+ * Lloyd-Max centroids of the coordinate law of a uniform unit vector in R^d,
+ * f(t) ~ (1 - t^2)^((d-3)/2), on the 7-bit grid: delta = max|c| / 63 (fp32),
+ * table[k] = nearest integer to c_k / delta, plus 64 (host only; 3 <= d,
+ * 1 <= mbits <= 4, table holds 2^mbits bytes). */
+int qtq_centroids(int d, int mbits, float* delta, uint8_t* table);
+/* Q of G = QR with diag(R) > 0 (modified Gram-Schmidt; host, row-major d x
+ * d); with G of i.i.d. N(0, 1) entries, a random rotation.  Q_ERANGE if G is
+ * singular. */
+int qtq_rotation(int d, const double* G, double* Pi);
+/* Byte sizes of codes, signs and norms for n keys (host only). */
+int qtq_sizes(int64_t n, int bits, size_t* codes_bytes, size_t* signs_bytes, size_t* norms_bytes);
+/* Encode n keys K[n][128] (fp32, device): y = Pi x / |x|, each coordinate
+ * to the nearest centroid (ties to the lower index), residual r = y - c,
+ * gamma = |r|, signs of S r; every sum in fp64 in increasing index order,
+ * norms rounded to fp16 (nearest even).  Synchronizes `stream`; Q_ERANGE on
+ * a non-finite key or a norm beyond fp16. */
+int qtq_quant_keys(const float* K, int64_t n, int bits, const double* Pi, const double* S, float delta,
+                   const uint8_t* table, void* codes, uint32_t* signs, uint32_t* norms, hipStream_t stream);
+/* Workspace bytes of qtq_logits for `heads` heads of nq queries (host). */
+int qtq_logits_ws(int64_t heads, int64_t nq, size_t* ws_bytes);
+/* Attention logits from quantized keys: for every head h < heads, query
+ * i < nq (Qv[h][i][128], fp32, device) and key j < n of that head (the keys
+ * of head h are rows h*n .. h*n + n - 1 of codes/signs/norms),
+ *   out[h][i][j] = |x| (<Pi q, c[code]> + gamma sqrt(pi/2)/128 <S Pi q, sign>),
+ * with Pi q and S Pi q formed in fp64 and rounded once to bf16, products
+ * accumulated in fp32.  ws: device, >= the qtq_logits_ws value, 16-byte
+ * aligned.  Asynchronous. */
+int qtq_logits(const void* codes, const uint32_t* signs, const uint32_t* norms, int64_t n, int64_t heads,
+               int bits, float delta, const uint8_t* table, const double* Pi, const double* S, const float* Qv,
+               int64_t nq, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 /* ------------------------------------------------------------- binary LR
  * Sizes of Ubits, VTbits and of the qgemv_binlr workspace for batch B
  * (host only).  r >= 1, N >= 1, K >= 1, 1 <= B <= 16. */

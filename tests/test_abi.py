@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -174,3 +174,46 @@ def test_default_codebooks_reject_widths(lib):
     buf = (ctypes.c_uint8 * 256)()
     assert lib.qcodebook_default(5, buf, None) == cg.Q_EINVAL
     assert lib.qcodebook_default(4, None, None) == cg.Q_EINVAL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_centroids_and_rotation_match_the_oracle(lib, d):
+    """The library's Lloyd-Max tables and Gram-Schmidt rotation equal the
+    oracle's (incomplete-beta centroids, numpy QR with the sign fix)."""
+    from oracle import turboquant as tq
+    for m in (1, 2, 3, 4):
+        dl, t = cg.qtq_centroids(d, m)
+        d2, t2 = tq.stored_table(tq.lloyd_max(d, m))
+        assert np.float32(dl) == d2 and np.array_equal(t, t2), (m, dl, d2)
+    G = np.random.default_rng(d).standard_normal((d, d))
+    assert np.abs(cg.qtq_rotation(G) - tq.rotation(G)).max() < 1e-11
+
+
+def test_key_cache_entry_points_validate(lib):
+    P = ctypes.c_void_p
+    good, odd = P(0x10000), P(0x10004)
+    s = P(0)
+    t = (ctypes.c_uint8 * 8)(1, 24, 42, 57, 71, 86, 104, 127)
+    bad = (ctypes.c_uint8 * 8)(0, 24, 42, 57, 71, 86, 104, 127)
+    f = ctypes.c_float
+    assert lib.qtq_quant_keys(good, 16, 5, good, good, f(0.003), t, good, good, good, s) == cg.Q_EINVAL
+    assert lib.qtq_quant_keys(good, 16, 4, good, good, f(0.0), t, good, good, good, s) == cg.Q_EINVAL
+    assert lib.qtq_quant_keys(good, 16, 4, good, good, f(0.003), bad, good, good, good, s) == cg.Q_EINVAL
+    assert lib.qtq_quant_keys(good, 16, 4, odd, good, f(0.003), t, good, good, good, s) == cg.Q_EALIGN
+    assert lib.qtq_quant_keys(good, 1 << 26, 4, good, good, f(0.003), t, good, good, good, s) == cg.Q_EUNSUPPORTED
+    n = ctypes.c_size_t()
+    assert lib.qtq_logits_ws(2, 4, ctypes.byref(n)) == 0 and n.value == 2 * 4 * 132 * 4
+    assert lib.qtq_logits(good, good, good, 64, 2, 4, f(0.003), t, good, good, good, 4, good, good, 16,
+                          s) == cg.Q_EWORKSPACE
+    assert lib.qtq_logits(good, good, good, 64, 2, 4, f(0.003), t, good, good, good, 4, good, P(0), 1 << 20,
+                          s) == cg.Q_EWORKSPACE
+    assert lib.qtq_logits(good, good, good, 64, 0, 4, f(0.003), t, good, good, good, 4, good, good, 1 << 20,
+                          s) == cg.Q_EINVAL
+    assert lib.qtq_logits(good, good, good, 64, 2, 4, f(0.003), t, good, good, good, 4, good, P(0x10008), 1 << 20,
+                          s) == cg.Q_EALIGN
+    cb, sb, nb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.qtq_sizes(1000, 4, ctypes.byref(cb), ctypes.byref(sb), ctypes.byref(nb)) == 0
+    assert (cb.value, sb.value, nb.value) == (48000, 16000, 4000)
+    buf = (ctypes.c_uint8 * 16)()
+    assert lib.qtq_centroids(2, 3, ctypes.byref(f()), buf) == cg.Q_EINVAL
+    assert lib.qtq_centroids(128, 5, ctypes.byref(f()), buf) == cg.Q_EINVAL
