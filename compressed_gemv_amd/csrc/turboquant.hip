@@ -9,13 +9,12 @@
 //   <q, x> ~ |x| (delta sum_j (e[code_j] - 64) (Pi q)_j
 //                 + gamma sqrt(pi/2)/d sum_j sign_j (S Pi q)_j).
 // A prep kernel forms Pi q and S Pi q once per query (fp64 sums, rounded to
-// bf16 and laid out as the dot-product pairs of the logit kernel).  The logit
-// kernel streams the keys: four lanes per key, one 32-coordinate unit each;
-// the centroid codes go through the codebook byte-permute decode (pairs
-// 128 + e[code] in bf16) and the sign bits become bf16 +-1 pairs with one
-// shift and one masked OR; v_dot2_f32_bf16 against the query pairs, a
-// two-step DPP sum over the quad, and the per-key fp16 norms scale the
-// result.  A key is read once for up to 4 queries (grouped-query heads).
+// bf16 and laid out as the operand pairs of the logit kernel).  The logit
+// kernel streams the keys: the centroid codes go through the codebook
+// byte-permute decode (pairs 128 + e[code] in bf16) and the sign bits become
+// bf16 +-1 pairs with one shift and one masked OR; the products with up to
+// 16 queries (a grouped-query head's) run on the matrix cores, so a key is
+// read once for all of them.
 #include <math.h>
 
 #include "codebook.hpp"
@@ -96,6 +95,7 @@ void tq_rotation(int d, const double* G, double* Pi) {
 // bf16-rounded qr values of unit w (the 128-bias correction).
 constexpr int kTqQueryWords = 132;
 
+
 template <int M>
 __global__ __launch_bounds__(128) void tq_prep_kernel(const float* __restrict__ Qv, int nq, const double* __restrict__ Pi,
                                                       const double* __restrict__ S, uint32_t* __restrict__ ws) {
@@ -130,84 +130,125 @@ __global__ __launch_bounds__(128) void tq_prep_kernel(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------ logit kernel
-// Grid (blocks, heads, query chunks of Q); 4 waves per workgroup; a wave
-// takes 16 keys per step (lane = 4 * key slot + unit), grid-stride over the
-// head's n keys with the next step's loads issued before the current step is
-// decoded.  Keys past n read zeros and are not stored.
-template <int M, int Q>
+// The logits of a wave step are a small matrix product: 16 keys x 128
+// coordinates times up to 16 queries, on v_mfma_f32_16x16x32_bf16.  Lane l
+// decodes unit l / 16 (32 coordinates) of key l % 16: its 16 code pairs
+// (bf16 128 + e[code]) are the A operand of four K-steps (4 pair words each)
+// and its 16 sign pairs (bf16 +-1) those of four more; lane l of the B
+// operand holds the matching query pairs of query l % 16 for the same unit
+// (the order of the contraction is free as long as A and B agree).  D lane l
+// then holds keys 4 (l / 16) + i, i < 4, of query l % 16; the bias
+// 192 sum(Pi q), delta, gamma sqrt(pi/2)/128 and |x| are applied per
+// element.  Grid (blocks, heads, chunks of 16 queries); 4 waves per
+// workgroup; grid-stride over the head's keys with TQ_DEPTH steps in flight.
+#ifndef TQ_WAVES
+#define TQ_WAVES 2048  // target waves per launch
+#endif
+#ifndef TQ_DEPTH
+#define TQ_DEPTH 4    // key steps in flight per wave
+#endif
+
+template <int M>
 __global__ __launch_bounds__(256) void tq_logits_kernel(const uint32_t* __restrict__ codes,
                                                         const uint32_t* __restrict__ signs,
                                                         const uint32_t* __restrict__ norms, int n, int nq,
                                                         float delta, uint32_t tab_lo, uint32_t tab_hi,
                                                         const uint32_t* __restrict__ ws, float* __restrict__ out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int w = lane & 3, slot = lane >> 2;
-  const int h = blockIdx.y, q0 = blockIdx.z * Q;
-  uint32_t qp[Q][16], up[Q][16];
-  float qsum[Q];
+  const int r = lane & 15, kg = lane >> 4;             // A: key r, unit kg; B: query r, unit kg
+  const int h = blockIdx.y, q = blockIdx.z * 16 + r;
+  const bool qok = q < nq;
+  u32x4_t qa[4], ua[4];
+  float qsum = 0.f;
+  {
+    const uint32_t* src = ws + ((size_t)h * nq + (qok ? q : 0)) * kTqQueryWords;
 #pragma unroll
-  for (int t = 0; t < Q; ++t) {
-    const int qi = q0 + t < nq ? q0 + t : nq - 1;      // padded queries repeat the last one, never stored
-    const uint32_t* src = ws + ((size_t)h * nq + qi) * kTqQueryWords;
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      qp[t][k] = src[w * 32 + k];
-      up[t][k] = src[w * 32 + 16 + k];
-    }
-    qsum[t] = __uint_as_float(src[128 + w]);
+      for (int e = 0; e < 4; ++e) {
+        qa[s][e] = qok ? src[kg * 32 + 4 * s + e] : 0u;
+        ua[s][e] = qok ? src[kg * 32 + 16 + 4 * s + e] : 0u;
+      }
+    if (qok)
+      for (int w = 0; w < 4; ++w) qsum += __uint_as_float(src[128 + w]);
   }
   const uint32_t T[4] = {tab_lo, tab_hi, 0u, 0u};
   const CbConst kc = cb_consts();
+  uint32_t smask = 0x80008000u, sone = 0x3F803F80u;     // opaque: one v_and_or per sign pair
+  asm volatile("" : "+v"(smask), "+v"(sone));
   const float gk = 1.2533141373155003f / 128.0f;        // sqrt(pi/2) / d
+  const float bias = 192.0f * qsum;
+  const bool vec_out = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   const size_t hk = (size_t)h * n;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes + hk * 4 * M, (uint32_t)((size_t)n * 16 * M));
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(signs + hk * 4, (uint32_t)((size_t)n * 16));
   const __amdgpu_buffer_rsrc_t nrs = make_rsrc(norms + hk, (uint32_t)((size_t)n * 4));
-  struct Raw { uint32_t c[M]; uint32_t s; uint32_t nm; };
+  struct Raw { uint32_t c[M]; uint32_t s; uint32_t nm[4]; };
   // keys past n get offsets past every buffer (n * 64 < 2^32 - 256): zeros
-  auto load = [&](int key, Raw& r) {
+  auto load = [&](int base, Raw& rw) {
+    const int key = base + r;
+    const uint32_t u = (uint32_t)key * 4 + (uint32_t)kg;
     const bool ok = key < n;
-    const uint32_t u = (uint32_t)key * 4 + (uint32_t)w;
-    buf_load_unit<M>(crs, ok ? u * (M * 4) : 0xFFFFFF00u, 0u, r.c);
-    r.s = buf_load_u32(srs, ok ? u * 4 : 0xFFFFFF00u, 0u);
-    r.nm = buf_load_u32(nrs, ok ? (uint32_t)key * 4 : 0xFFFFFF00u, 0u);
-  };
-  auto compute = [&](int key, const Raw& r) {
-    uint32_t pr[16];
-    decode_unit_cb<M>(r.c, T, pr, kc);
-    const uint32_t ns = ~r.s;
-    uint32_t sp[16];
+    buf_load_unit<M>(crs, ok ? u * (M * 4) : 0xFFFFFF00u, 0u, rw.c);
+    rw.s = buf_load_u32(srs, ok ? u * 4 : 0xFFFFFF00u, 0u);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sp[j] = ((ns << (15 - j)) & 0x80008000u) | 0x3F803F80u;
-    const float nrm = f16_bits_to_f32(r.nm & 0xFFFFu), g = f16_bits_to_f32(r.nm >> 16) * gk;
-#pragma unroll
-    for (int t = 0; t < Q; ++t) {
-      float a0 = -192.0f * qsum[t], a1 = 0.f, b0 = 0.f, b1 = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; k += 2) {
-        a0 = dot2_bf16(pr[k], qp[t][k], a0);
-        a1 = dot2_bf16(pr[k + 1], qp[t][k + 1], a1);
-        b0 = dot2_bf16(sp[k], up[t][k], b0);
-        b1 = dot2_bf16(sp[k + 1], up[t][k + 1], b1);
-      }
-      float part = delta * (a0 + a1) + g * (b0 + b1);
-      part += dpp_f32<0xB1>(part);   // quad_perm [1,0,3,2]
-      part += dpp_f32<0x4E>(part);   // quad_perm [2,3,0,1]
-      if (w == 0 && key < n && q0 + t < nq) out[((size_t)h * nq + q0 + t) * n + key] = nrm * part;
+    for (int i = 0; i < 4; ++i) {
+      const int kk = base + 4 * kg + i;
+      rw.nm[i] = buf_load_u32(nrs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
     }
   };
+  auto compute = [&](int base, const Raw& rw) {
+    uint32_t pr[16];
+    decode_unit_cb<M>(rw.c, T, pr, kc);
+    const uint32_t ns = ~rw.s;
+    f32x4_t dm = {0.f, 0.f, 0.f, 0.f}, ds = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t a, sg;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * s + e;
+        a[e] = pr[j];
+        sg[e] = ((ns << (15 - j)) & smask) | sone;   // bits j, j + 16 -> bf16 +-1
+      }
+      dm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qa[s]),
+                                                   dm, 0, 0, 0);
+      ds = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, sg),
+                                                   __builtin_bit_cast(bf16x8_t, ua[s]), ds, 0, 0, 0);
+    }
+    if (qok) {
+      float* orow = out + ((size_t)h * nq + q) * n;
+      const int k0 = base + 4 * kg;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float nrm = f16_bits_to_f32(rw.nm[i] & 0xFFFFu), g = f16_bits_to_f32(rw.nm[i] >> 16) * gk;
+        v[i] = nrm * (delta * (dm[i] - bias) + g * ds[i]);
+      }
+      if (vec_out && k0 + 3 < n) {   // rows 16-byte aligned (n % 4 == 0): one store of 4 keys
+        *reinterpret_cast<f32x4_t*>(orow + k0) = f32x4_t{v[0], v[1], v[2], v[3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + i < n) orow[k0 + i] = v[i];
+      }
+    }
+  };
+  constexpr int DEPTH = TQ_DEPTH;
   const int stride = gridDim.x * 4 * 16;
-  int key = (blockIdx.x * 4 + wave) * 16 + slot;
-  Raw ra{}, rb{};
-  if (key - slot < n) load(key, ra);
-  while (key - slot < n) {
-    const int nxt = key + stride;
-    const bool more = nxt - slot < n;                    // wave-uniform
-    if (more) load(nxt, rb);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(key, ra);
-    ra = rb;
-    key = nxt;
+  const int base0 = (blockIdx.x * 4 + wave) * 16;
+  Raw rg[DEPTH];
+#pragma unroll
+  for (int t = 0; t < DEPTH - 1; ++t) load(base0 + t * stride, rg[t]);
+  // loads past n read zeros; the last ring turn may decode such zero keys,
+  // whose results are not stored
+  for (int base = base0; base < n; base += DEPTH * stride) {   // wave-uniform
+#pragma unroll
+    for (int t = 0; t < DEPTH; ++t) {
+      load(base + (t + DEPTH - 1) * stride, rg[(t + DEPTH - 1) % DEPTH]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(base + t * stride, rg[t]);
+    }
   }
 }
 
@@ -221,19 +262,18 @@ hipError_t launch_tq_logits(const uint32_t* codes, const uint32_t* signs, const 
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // about 2048 waves over all heads, at least one workgroup per head
-  const int Q = nq <= 1 ? 1 : (nq <= 2 ? 2 : 4);
-  int64_t per_head = (2048 / 4 + heads - 1) / heads;
+  // about TQ_WAVES waves over all heads, at least one workgroup per head
+  int64_t per_head = (TQ_WAVES / 4 + heads - 1) / heads;
   const int64_t need = (n + 63) / 64;
   if (per_head > need) per_head = need;
   if (per_head < 1) per_head = 1;
-  const dim3 grid((unsigned)per_head, (unsigned)heads, (unsigned)((nq + Q - 1) / Q));
-#define L(MB, QQ)                                                                                       \
-  hipLaunchKernelGGL((tq_logits_kernel<MB, QQ>), grid, dim3(256), 0, s, codes, signs, norms, (int)n, (int)nq, \
-                     delta, tab_lo, tab_hi, ws, out)
-  if (mbits == 2) { if (Q == 1) L(2, 1); else if (Q == 2) L(2, 2); else L(2, 4); }
-  else { if (Q == 1) L(3, 1); else if (Q == 2) L(3, 2); else L(3, 4); }
-#undef L
+  const dim3 grid((unsigned)per_head, (unsigned)heads, (unsigned)((nq + 15) / 16));
+  if (mbits == 2)
+    hipLaunchKernelGGL((tq_logits_kernel<2>), grid, dim3(256), 0, s, codes, signs, norms, (int)n, (int)nq, delta,
+                       tab_lo, tab_hi, ws, out);
+  else
+    hipLaunchKernelGGL((tq_logits_kernel<3>), grid, dim3(256), 0, s, codes, signs, norms, (int)n, (int)nq, delta,
+                       tab_lo, tab_hi, ws, out);
   return hipGetLastError();
 }
 
