@@ -102,7 +102,7 @@ def main():
         lines += ["Commands (run from /tmp with TMPDIR=/tmp):", "", "```", a.commands.strip(), "```", ""]
     lines += ["## Kernel stats (rocprofv3 --kernel-trace --stats)", "",
               "| kernel | calls | avg us | min us | % time |", "|---|---|---|---|---|"]
-    for name, calls, avg, mn, pct in kernel_stats(a.trace)[:25]:
+    for name, calls, avg, mn, pct in kernel_stats(a.trace)[:40]:
         lines.append(f"| `{name[:110]}` | {calls} | {avg:.2f} | {mn:.2f} | {pct:.2f} |")
     if a.fetch and a.write:
         s = summarize(a.trace, a.fetch, a.write, a.kernel, a.bytes, a.last or None)

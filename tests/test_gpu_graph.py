@@ -111,3 +111,35 @@ def test_graph_gemv_multi(gpu):
         run(ref)
         return ref
     _check_replays(g, out, eager, xs, x)
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_graph_gemv_codebook(gpu, B):
+    say(f"graph gemv_group_cb B={B}")
+    N, K = 1000, 4096
+    W = gen_weights(N, K, rng_for(95, B), outliers=True)
+    books = dev(np.asarray(gpu.qcodebook_default(4)))
+    codes, meta, ids = gpu.qpack_group_cb(dev(W), 4, 64, books)
+    x = dev_bf16(gen_x_bf16(B, K, rng_for(96, 0)))
+    y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    g = _capture(lambda: gpu.qgemv_group_cb(codes, meta, ids, books, N, K, 4, 64, x, y=y))
+    xs = [dev_bf16(gen_x_bf16(B, K, rng_for(97, i))) for i in range(3)]
+    _check_replays(g, y, lambda: gpu.qgemv_group_cb(codes, meta, ids, books, N, K, 4, 64, x), xs, x)
+
+
+def test_graph_key_logits(gpu):
+    """Query prep and logits (two launches) replayed with new queries."""
+    say("graph qtq_logits")
+    rng = rng_for(98, 0)
+    Pi = dev(gpu.qtq_rotation(rng.standard_normal((128, 128))))
+    S = dev(rng.standard_normal((128, 128)))
+    delta, table = gpu.qtq_centroids(128, 3)
+    H, n, nq = 2, 3000, 4
+    K = dev(rng.standard_normal((H * n, 128)).astype(np.float32))
+    c, sg, nm = gpu.qtq_quant_keys(K, 4, Pi, S, delta, table)
+    Qv = dev(rng.standard_normal((H, nq, 128)).astype(np.float32))
+    out = torch.empty((H, nq, n), dtype=torch.float32, device=Qv.device)
+    ws = torch.empty(H * nq * 132 * 4, dtype=torch.uint8, device=Qv.device)
+    g = _capture(lambda: gpu.qtq_logits(c, sg, nm, n, H, 4, delta, table, Pi, S, Qv, out=out, ws=ws))
+    qs = [dev(rng_for(99, i).standard_normal((H, nq, 128)).astype(np.float32)) for i in range(3)]
+    _check_replays(g, out, lambda: gpu.qtq_logits(c, sg, nm, n, H, 4, delta, table, Pi, S, Qv), qs, Qv)
