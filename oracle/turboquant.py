@@ -183,3 +183,17 @@ def logits_prod(Q: np.ndarray, codes, signs, norm16, gamma16, Pi, S, cv) -> np.n
     qjl = u @ pm.T
     g = np.asarray(gamma16, dtype=np.float64) * math.sqrt(math.pi / 2) / d
     return np.asarray(norm16, dtype=np.float64)[None, :] * (mse + g[None, :] * qjl)
+
+
+def quantize_values(X: np.ndarray, Pi: np.ndarray, cv: np.ndarray):
+    """Reconstruction variant for values: (codes [n][d], norm16 float16 [n]),
+    the MSE codes of y = Pi x / |x| with |x| stored in fp16."""
+    codes, norm, _ = quantize_mse(X, Pi, cv)
+    return codes, norm.astype(np.float16)
+
+
+def attend_values(P: np.ndarray, codes, norm16, Pi, cv) -> np.ndarray:
+    """Attention output over quantized values: o[q] = sum_i P[q][i] v_hat_i
+    with v_hat_i = |v_i| Pi^T c[code_i] (fp64); P [nq][n]."""
+    Vh = dequantize_mse(codes, np.asarray(norm16, dtype=np.float64), Pi, cv)
+    return np.asarray(P, dtype=np.float64) @ Vh
