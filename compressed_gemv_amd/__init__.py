@@ -20,7 +20,7 @@ __all__ = [
     "qgroup_sizes", "qpack_group", "qunpack_group", "qgemv_group",
     "qgroup_outlier_ws", "qpack_group_outlier", "qgemv_group_outlier", "qgemv_group_multi",
     "qcodebook_default", "qpack_group_cb", "qgemv_group_cb",
-    "qtq_centroids", "qtq_rotation", "qtq_quant_keys", "qtq_logits",
+    "qtq_centroids", "qtq_rotation", "qtq_quant_keys", "qtq_logits", "qtq_quant_values", "qtq_attend",
     "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr",
     "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
 ]
@@ -91,6 +91,9 @@ def load() -> ctypes.CDLL:
         "qtq_quant_keys": (I32, [P, I64, I32, P, P, ctypes.c_float, P, P, P, P, P]),
         "qtq_logits_ws": (I32, [I64, I64, SZ]),
         "qtq_logits": (I32, [P, P, P, I64, I64, I32, ctypes.c_float, P, P, P, P, I64, P, P, ctypes.c_size_t, P]),
+        "qtq_quant_values": (I32, [P, I64, I32, P, ctypes.c_float, P, P, P, P]),
+        "qtq_attend_ws": (I32, [I64, I64, I64, SZ]),
+        "qtq_attend": (I32, [P, P, I64, I64, I32, ctypes.c_float, P, P, P, I64, P, P, ctypes.c_size_t, P]),
         "qbinlr_sizes": (I32, [I64, I64, I64, I64, SZ, SZ, SZ]),
         "qpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
         "qunpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
@@ -331,6 +334,37 @@ def qtq_logits(codes, signs, norms, n: int, heads: int, bits: int, delta: float,
     _check(load().qtq_logits(_ptr(codes), _ptr(signs), _ptr(norms), n, heads, bits, float(delta),
                              t.ctypes.data_as(ctypes.c_void_p), _ptr(Pi), _ptr(S), _ptr(Qv), nq, _ptr(out), _ptr(ws),
                              ws.numel(), _stream(stream)), "qtq_logits")
+    return out
+
+
+def qtq_quant_values(V: torch.Tensor, bits: int, Pi: torch.Tensor, delta: float, table, stream=None):
+    """(codes int32[n*4*bits], norms int32[n]) for fp32 values V[n][128]."""
+    import numpy as np
+    _need_cuda(V, Pi)
+    n = V.shape[0]
+    codes = torch.empty(n * 4 * bits, dtype=torch.int32, device=V.device)
+    norms = torch.empty(n, dtype=torch.int32, device=V.device)
+    t = np.ascontiguousarray(table, dtype=np.uint8)
+    _check(load().qtq_quant_values(_ptr(V), n, bits, _ptr(Pi), float(delta), t.ctypes.data_as(ctypes.c_void_p),
+                                   _ptr(codes), _ptr(norms), _stream(stream)), "qtq_quant_values")
+    return codes, norms
+
+
+def qtq_attend(codes, norms, n: int, heads: int, bits: int, delta: float, table, Pi, P: torch.Tensor,
+               out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """out[heads][nq][128] = P[heads][nq][n] times the dequantized values."""
+    import numpy as np
+    _need_cuda(codes, norms, Pi, P, out, ws)
+    nq = P.shape[1]
+    if out is None:
+        out = torch.empty((heads, nq, 128), dtype=torch.float32, device=P.device)
+    if ws is None:
+        need = ctypes.c_size_t()
+        _check(load().qtq_attend_ws(n, heads, nq, ctypes.byref(need)), "qtq_attend_ws")
+        ws = torch.empty(need.value, dtype=torch.uint8, device=P.device)
+    t = np.ascontiguousarray(table, dtype=np.uint8)
+    _check(load().qtq_attend(_ptr(codes), _ptr(norms), n, heads, bits, float(delta), t.ctypes.data_as(ctypes.c_void_p),
+                             _ptr(Pi), _ptr(P), nq, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "qtq_attend")
     return out
 
 

@@ -313,6 +313,14 @@ int qtq_rotation(int d, const double* G, double* Pi) {
 
 namespace {
 constexpr int kTqDim = 128;
+// bits = stored bits per coordinate; the table has 2^m entries, m = bits - 1
+// for keys (one sign bit) and m = bits for values
+int tq_table_ok(int m, float delta, const uint8_t* table) {
+  if (!table || !(delta > 0.0f) || !isfinite(delta)) return Q_EINVAL;
+  for (int k = 0; k < (1 << m); ++k)
+    if (table[k] < 1 || table[k] > 127) return Q_EINVAL;
+  return Q_OK;
+}
 int tq_args_ok(int64_t n, int64_t heads, int bits, float delta, const uint8_t* table) {
   if (n < 1 || heads < 1 || bits < 3 || bits > 4 || !table) return Q_EINVAL;
   if (!(delta > 0.0f) || !isfinite(delta)) return Q_EINVAL;
@@ -323,12 +331,9 @@ int tq_args_ok(int64_t n, int64_t heads, int bits, float delta, const uint8_t* t
     if (table[k] < 1 || table[k] > 127) return Q_EINVAL;
   return Q_OK;
 }
-void tq_table_words(const uint8_t* t, int L, uint32_t* lo, uint32_t* hi) {
-  *lo = 0; *hi = 0;
-  for (int k = 0; k < L; ++k) {
-    if (k < 4) *lo |= (uint32_t)t[k] << (8 * k);
-    else *hi |= (uint32_t)t[k] << (8 * (k - 4));
-  }
+void tq_table_words(const uint8_t* t, int L, uint32_t* w4) {
+  for (int i = 0; i < 4; ++i) w4[i] = 0;
+  for (int k = 0; k < L; ++k) w4[k >> 2] |= (uint32_t)t[k] << (8 * (k & 3));
 }
 }  // namespace
 
@@ -348,13 +353,13 @@ int qtq_quant_keys(const float* K, int64_t n, int bits, const double* Pi, const 
   if (!aligned(K, 4) || !aligned(Pi, 8) || !aligned(S, 8) || !aligned(codes, 4) || !aligned(signs, 4) ||
       !aligned(norms, 4))
     return Q_EALIGN;
-  uint32_t lo, hi;
-  tq_table_words(table, 1 << (bits - 1), &lo, &hi);
+  uint32_t tw[4];
+  tq_table_words(table, 1 << (bits - 1), tw);
   hipError_t e;
   int* status = qg::pack_status_ptr(&e);
   if (!status) return Q_EHIP;
   if ((e = qg::launch_zero_status(status, stream)) != hipSuccess) return Q_EHIP;
-  e = qg::launch_tq_quant(K, n, bits - 1, Pi, S, delta, lo, hi, static_cast<uint32_t*>(codes), signs, norms,
+  e = qg::launch_tq_quant(K, n, bits - 1, true, Pi, S, delta, tw, static_cast<uint32_t*>(codes), signs, norms,
                           status, stream);
   if (e != hipSuccess) return Q_EHIP;
   int host = 0;
@@ -382,10 +387,60 @@ int qtq_logits(const void* codes, const uint32_t* signs, const uint32_t* norms, 
       !aligned(Qv, 4) || !aligned(out, 4) || !aligned(ws, 16))
     return Q_EALIGN;
   if (heads * nq * n > ((int64_t)1 << 40)) return Q_EUNSUPPORTED;
-  uint32_t lo, hi;
-  tq_table_words(table, 1 << (bits - 1), &lo, &hi);
+  uint32_t tw[4];
+  tq_table_words(table, 1 << (bits - 1), tw);
   return hip_status(qg::launch_tq_logits(static_cast<const uint32_t*>(codes), signs, norms, n, heads, bits - 1,
-                                         delta, lo, hi, Pi, S, Qv, nq, out, static_cast<uint32_t*>(ws), stream));
+                                         delta, tw[0], tw[1], Pi, S, Qv, nq, out, static_cast<uint32_t*>(ws), stream));
+}
+
+int qtq_quant_values(const float* V, int64_t n, int bits, const double* Pi, float delta, const uint8_t* table,
+                     void* codes, uint32_t* norms, hipStream_t stream) {
+  if (n < 1 || bits < 2 || bits > 4) return Q_EINVAL;
+  int st = tq_table_ok(bits, delta, table);
+  if (st != Q_OK) return st;
+  if (!V || !Pi || !codes || !norms) return Q_EINVAL;
+  if (n * 64 >= ((int64_t)1 << 32) - 256) return Q_EUNSUPPORTED;
+  if (!aligned(V, 4) || !aligned(Pi, 8) || !aligned(codes, 4) || !aligned(norms, 4)) return Q_EALIGN;
+  uint32_t tw[4];
+  tq_table_words(table, 1 << bits, tw);
+  hipError_t e;
+  int* status = qg::pack_status_ptr(&e);
+  if (!status) return Q_EHIP;
+  if ((e = qg::launch_zero_status(status, stream)) != hipSuccess) return Q_EHIP;
+  e = qg::launch_tq_quant(V, n, bits, false, Pi, nullptr, delta, tw, static_cast<uint32_t*>(codes), nullptr, norms,
+                          status, stream);
+  if (e != hipSuccess) return Q_EHIP;
+  int host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return Q_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return Q_EHIP;
+  return host ? Q_ERANGE : Q_OK;
+}
+
+int qtq_attend_ws(int64_t n, int64_t heads, int64_t nq, size_t* ws_bytes) {
+  if (n < 1 || heads < 1 || heads > 65535 || nq < 1 || nq > 65535 || !ws_bytes) return Q_EINVAL;
+  const int64_t Q = nq <= 1 ? 1 : (nq <= 2 ? 2 : 4);
+  *ws_bytes = (size_t)(heads * ((nq + Q - 1) / Q) * qg::tq_attend_blocks(n, heads) * Q * 129 * 4);
+  return Q_OK;
+}
+
+int qtq_attend(const void* codes, const uint32_t* norms, int64_t n, int64_t heads, int bits, float delta,
+               const uint8_t* table, const double* Pi, const float* P, int64_t nq, float* out, void* ws,
+               size_t ws_bytes, hipStream_t stream) {
+  if (bits < 2 || bits > 4) return Q_EINVAL;
+  int st = tq_table_ok(bits, delta, table);
+  if (st != Q_OK) return st;
+  size_t need = 0;
+  if ((st = qtq_attend_ws(n, heads, nq, &need)) != Q_OK) return st;
+  if (!codes || !norms || !Pi || !P || !out) return Q_EINVAL;
+  if (!ws || ws_bytes < need) return Q_EWORKSPACE;
+  if (n * 64 >= ((int64_t)1 << 32) - 256 || n * heads > INT32_MAX) return Q_EUNSUPPORTED;
+  if (!aligned(codes, 4) || !aligned(norms, 4) || !aligned(Pi, 8) || !aligned(P, 4) || !aligned(out, 4) ||
+      !aligned(ws, 16))
+    return Q_EALIGN;
+  uint32_t tw[4];
+  tq_table_words(table, 1 << bits, tw);
+  return hip_status(qg::launch_tq_attend(static_cast<const uint32_t*>(codes), norms, n, heads, bits, delta, tw, Pi, P,
+                                         nq, out, static_cast<float*>(ws), stream));
 }
 
 int qbinlr_sizes(int64_t N, int64_t K, int64_t r, int64_t B, size_t* ubits_bytes,

@@ -51,9 +51,13 @@ hipError_t launch_pack_group_cb(const float* W, int64_t N, int64_t K, int bits, 
                                 hipStream_t s);
 void tq_lloyd_max(int d, int m, double* c);
 void tq_rotation(int d, const double* G, double* Pi);
-hipError_t launch_tq_quant(const float* X, int64_t n, int mbits, const double* Pi, const double* S, float delta,
-                           uint32_t tab_lo, uint32_t tab_hi, uint32_t* codes, uint32_t* signs, uint32_t* norms,
+hipError_t launch_tq_quant(const float* X, int64_t n, int mbits, bool prod, const double* Pi, const double* S,
+                           float delta, const uint32_t* tab, uint32_t* codes, uint32_t* signs, uint32_t* norms,
                            int* status, hipStream_t s);
+int64_t tq_attend_blocks(int64_t n, int64_t heads);
+hipError_t launch_tq_attend(const uint32_t* codes, const uint32_t* norms, int64_t n, int64_t heads, int mbits,
+                            float delta, const uint32_t* tab, const double* Pi, const float* P, int64_t nq,
+                            float* out, float* part, hipStream_t s);
 hipError_t launch_tq_logits(const uint32_t* codes, const uint32_t* signs, const uint32_t* norms, int64_t n,
                             int64_t heads, int mbits, float delta, uint32_t tab_lo, uint32_t tab_hi,
                             const double* Pi, const double* S, const float* Qv, int64_t nq, float* out,

@@ -664,12 +664,13 @@ hipError_t launch_unpack_binlr(const uint32_t* ubits, const uint32_t* vtbits, in
 // (tab_lo, tab_hi).  Outputs: codes [n][4][M] (units of 32 coordinates in
 // the group-code layout), signs [n][4] (bit j of word w: coordinate 32w + j),
 // norms [n] = fp16 |x| | fp16 gamma << 16.
-template <int M>
+// PROD = false: the reconstruction variant for values (M = 2..4 bits): codes
+// and fp16 |x| only (no residual, no signs; norms' upper half 0).
+template <int M, bool PROD>
 __global__ __launch_bounds__(64) void tq_quant_kernel(const float* __restrict__ X, const double* __restrict__ Pi,
-                                                      const double* __restrict__ S, double delta, uint32_t tab_lo,
-                                                      uint32_t tab_hi, uint32_t* __restrict__ codes,
-                                                      uint32_t* __restrict__ signs, uint32_t* __restrict__ norms,
-                                                      int* status) {
+                                                      const double* __restrict__ S, double delta, uint4 tab,
+                                                      uint32_t* __restrict__ codes, uint32_t* __restrict__ signs,
+                                                      uint32_t* __restrict__ norms, int* status) {
   constexpr int D = 128, L = 1 << M;
   __shared__ double xs[D], rs[D], sh[2];
   __shared__ uint32_t cs[D], zs[D];
@@ -678,7 +679,8 @@ __global__ __launch_bounds__(64) void tq_quant_kernel(const float* __restrict__ 
   double cv[L];
 #pragma unroll
   for (int k = 0; k < L; ++k) {
-    const uint32_t e = ((k < 4 ? tab_lo >> (8 * k) : tab_hi >> (8 * (k - 4)))) & 0xFFu;
+    const uint32_t tw = k < 4 ? tab.x : (k < 8 ? tab.y : (k < 12 ? tab.z : tab.w));
+    const uint32_t e = (tw >> (8 * (k & 3))) & 0xFFu;
     cv[k] = delta * ((double)e - 64.0);
   }
   const float x0 = X[key * D + l], x1 = X[key * D + l + 64];
@@ -709,18 +711,20 @@ __global__ __launch_bounds__(64) void tq_quant_kernel(const float* __restrict__ 
     rs[i] = y - cv[best];
   }
   __syncthreads();
-  if (l == 0) {
-    double a = 0.0;
-    for (int j = 0; j < D; ++j) a = a + rs[j] * rs[j];
-    sh[1] = sqrt(a);
+  if constexpr (PROD) {
+    if (l == 0) {
+      double a = 0.0;
+      for (int j = 0; j < D; ++j) a = a + rs[j] * rs[j];
+      sh[1] = sqrt(a);
+    }
+    for (int h = 0; h < 2; ++h) {
+      const int i = l + 64 * h;
+      double a = 0.0;
+      for (int j = 0; j < D; ++j) a = a + rs[j] * S[i * D + j];
+      zs[i] = a >= 0.0 ? 1u : 0u;
+    }
+    __syncthreads();
   }
-  for (int h = 0; h < 2; ++h) {
-    const int i = l + 64 * h;
-    double a = 0.0;
-    for (int j = 0; j < D; ++j) a = a + rs[j] * S[i * D + j];
-    zs[i] = a >= 0.0 ? 1u : 0u;
-  }
-  __syncthreads();
   if (l < 4) {
     uint32_t w[M];
 #pragma unroll
@@ -728,30 +732,33 @@ __global__ __launch_bounds__(64) void tq_quant_kernel(const float* __restrict__ 
     uint32_t sg = 0u;
     for (int c = 0; c < 32; ++c) {
       place_code<M>(w, c, cs[32 * l + c]);
-      sg |= zs[32 * l + c] << c;
+      if constexpr (PROD) sg |= zs[32 * l + c] << c;
     }
 #pragma unroll
     for (int i = 0; i < M; ++i) codes[(key * 4 + l) * M + i] = w[i];
-    signs[key * 4 + l] = sg;
+    if constexpr (PROD) signs[key * 4 + l] = sg;
   }
   if (l == 0) {
     bool bad = false;
-    norms[key] = f16_rne_bits(sh[0], &bad) | (f16_rne_bits(sh[1], &bad) << 16);
+    norms[key] = f16_rne_bits(sh[0], &bad) | (PROD ? f16_rne_bits(sh[1], &bad) << 16 : 0u);
     if (bad) atomicOr(status, 1);
   }
 }
 
-hipError_t launch_tq_quant(const float* X, int64_t n, int mbits, const double* Pi, const double* S, float delta,
-                           uint32_t tab_lo, uint32_t tab_hi, uint32_t* codes, uint32_t* signs, uint32_t* norms,
+hipError_t launch_tq_quant(const float* X, int64_t n, int mbits, bool prod, const double* Pi, const double* S,
+                           float delta, const uint32_t* tab, uint32_t* codes, uint32_t* signs, uint32_t* norms,
                            int* status, hipStream_t s) {
-  if (mbits == 2)
-    hipLaunchKernelGGL((tq_quant_kernel<2>), dim3((unsigned)n), dim3(64), 0, s, X, Pi, S, (double)delta, tab_lo,
-                       tab_hi, codes, signs, norms, status);
-  else if (mbits == 3)
-    hipLaunchKernelGGL((tq_quant_kernel<3>), dim3((unsigned)n), dim3(64), 0, s, X, Pi, S, (double)delta, tab_lo,
-                       tab_hi, codes, signs, norms, status);
-  else
-    return hipErrorInvalidValue;
+  const uint4 t4{tab[0], tab[1], tab[2], tab[3]};
+#define L(MB, P)                                                                                                \
+  hipLaunchKernelGGL((tq_quant_kernel<MB, P>), dim3((unsigned)n), dim3(64), 0, s, X, Pi, S, (double)delta, t4, \
+                     codes, signs, norms, status)
+  if (prod && mbits == 2) L(2, true);
+  else if (prod && mbits == 3) L(3, true);
+  else if (!prod && mbits == 2) L(2, false);
+  else if (!prod && mbits == 3) L(3, false);
+  else if (!prod && mbits == 4) L(4, false);
+  else return hipErrorInvalidValue;
+#undef L
   return hipGetLastError();
 }
 

@@ -242,6 +242,24 @@ int qtq_logits_ws(int64_t heads, int64_t nq, size_t* ws_bytes);
 int qtq_logits(const void* codes, const uint32_t* signs, const uint32_t* norms, int64_t n, int64_t heads,
                int bits, float delta, const uint8_t* table, const double* Pi, const double* S, const float* Qv,
                int64_t nq, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Values (the page's reconstruction variant): bits = 2, 3 or 4 codebook
+ * bits per coordinate, no sign bits; codes [n][4][bits] as for keys, norms
+ * [n] u32 = fp16 |v| (upper half 0); the table has 2^bits bytes.
+ * Encode n values V[n][128] (fp32, device) as the keys' codebook part:
+ * y = Pi v / |v|, nearest stored centroid, fp64 sums in increasing index
+ * order.  Synchronizes `stream`; Q_ERANGE as qtq_quant_keys. */
+int qtq_quant_values(const float* V, int64_t n, int bits, const double* Pi, float delta, const uint8_t* table,
+                     void* codes, uint32_t* norms, hipStream_t stream);
+/* Workspace bytes of qtq_attend (host). */
+int qtq_attend_ws(int64_t n, int64_t heads, int64_t nq, size_t* ws_bytes);
+/* Attention output over quantized values: for head h, query i < nq and
+ * weights P[h][i][n] (fp32, device; e.g. the softmax of qtq_logits),
+ *   out[h][i][:] = sum_j P[h][i][j] |v_j| Pi^T c[code_j]   (fp32, [heads][nq][128]).
+ * Sums over the values in fp32 in the rotated domain, then one Pi^T product.
+ * ws: device, >= the qtq_attend_ws value, 16-byte aligned.  Asynchronous. */
+int qtq_attend(const void* codes, const uint32_t* norms, int64_t n, int64_t heads, int bits, float delta,
+               const uint8_t* table, const double* Pi, const float* P, int64_t nq, float* out, void* ws,
+               size_t ws_bytes, hipStream_t stream);
 /* ------------------------------------------------------------- binary LR
  * Sizes of Ubits, VTbits and of the qgemv_binlr workspace for batch B
  * (host only).  r >= 1, N >= 1, K >= 1, 1 <= B <= 16. */

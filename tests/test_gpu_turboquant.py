@@ -154,3 +154,48 @@ def test_logits_estimate_inner_products(gpu):
     slope = float(est @ true / (true @ true))
     assert abs(slope - 1.0) < 0.02, slope
     assert np.corrcoef(est, true)[0, 1] > 0.96
+
+
+# ------------------------------------------------------------------ values
+def _value_setup(bits, seed):
+    rng = rng_for(420, seed)
+    Pi = tq.rotation(rng.standard_normal((128, 128)))
+    delta, table = tq.stored_table(tq.lloyd_max(128, bits))
+    return Pi, delta, table, tq.table_values(delta, table)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_value_encoder_bit_exact(gpu, bits):
+    Pi, delta, table, cv = _value_setup(bits, bits)
+    V = _keys(300, 30 + bits)
+    V[9] = 0.0
+    codes, n16 = tq.quantize_values(V, Pi, cv)
+    words = oracle.fmt.pack_codes(codes.astype(np.uint8), bits)
+    c, nm = gpu.qtq_quant_values(dev(V), bits, dev(Pi), delta, table)
+    assert np.array_equal(host(c).view(np.uint32), words.reshape(-1))
+    assert np.array_equal(host(nm).view(np.uint32), n16.view(np.uint16).astype(np.uint32))
+
+
+@pytest.mark.parametrize("bits,nq,n", [(3, 1, 1000), (3, 4, 1000), (4, 2, 1000), (2, 5, 1000), (4, 4, 20000)])
+def test_attend(gpu, bits, nq, n):
+    """Attention output over quantized values against the oracle's fp64
+    sum; fp32 sums over the values in the rotated domain, so the error is a
+    small multiple of 2^-24 of sum |P| |v_hat|; tested at 1e-4 of its largest
+    coordinate."""
+    Pi, delta, table, cv = _value_setup(bits, 40 + nq)
+    H = 3
+    V = _keys(H * n, 50 + bits)
+    say(f"tq attend bits={bits} nq={nq} n={n}")
+    codes, n16 = tq.quantize_values(V, Pi, cv)
+    c, nm = gpu.qtq_quant_values(dev(V), bits, dev(Pi), delta, table)
+    rng = rng_for(421, nq)
+    P = rng.random((H, nq, n)).astype(np.float32)
+    P /= P.sum(axis=2, keepdims=True)
+    out = host(gpu.qtq_attend(c, nm, n, H, bits, delta, table, dev(Pi), dev(P)))
+    for h in range(H):
+        sl = slice(h * n, (h + 1) * n)
+        ref = tq.attend_values(P[h], codes[sl], n16[sl], Pi, cv)
+        Vh = tq.dequantize_mse(codes[sl], n16[sl].astype(np.float64), Pi, cv)
+        D = np.abs(P[h]).astype(np.float64) @ np.abs(Vh)
+        err = np.max(np.abs(out[h] - ref) / D.max(axis=1, keepdims=True))
+        assert err <= 1e-4, (h, err)
