@@ -427,6 +427,54 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
     for kb in (4, 3):
         rows[f"kv_logits_{kb}bit_h8_n131072_q4"] = kv_row(kb)
         log(f"kv logits {kb}-bit:", rows[f"kv_logits_{kb}bit_h8_n131072_q4"])
+
+    # attention output over quantized values (3-bit codes), the same heads,
+    # context and queries; bytes = codes + norms + the weights P read.  For
+    # scale, torch's batched matmul of P with the unquantized values.
+    def kv_attend_row(bits, H=8, n=131072, nq=4):
+        rng = np.random.default_rng(np.random.SeedSequence([0, 10, bits]))
+        Pi = to_dev(cg.qtq_rotation(rng.standard_normal((128, 128))))
+        delta, table = cg.qtq_centroids(128, bits)
+        Vf = torch.randn((H * n, 128), device=dev, generator=torch.Generator(device=dev).manual_seed(200 + bits))
+        c, nm = cg.qtq_quant_values(Vf, bits, Pi, delta, table)
+        Pw = torch.softmax(torch.randn((H, nq, n), device=dev), dim=2).contiguous()
+        nbytes = c.numel() * 4 + nm.numel() * 4 + Pw.numel() * 4
+        pool = pool_of((c, nm), c.numel() * 4 + nm.numel() * 4)
+        out = torch.empty((H, nq, 128), dtype=torch.float32, device=dev)
+        ws = torch.empty(cg.qtq_attend_ws(n, H, nq), dtype=torch.uint8, device=dev)
+
+        def f(i):
+            a, m_ = pool[i % len(pool)]
+            cg.qtq_attend(a, m_, n, H, bits, delta, table, Pi, Pw, out=out, ws=ws)
+        wall, ev = time_launches(f, 100, 10, period=len(pool))
+        del pool
+        torch.cuda.empty_cache()
+        us = ev / 100 * 1e6
+        base = {}
+        for label, dt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+            vd = Vf.view(H, n, 128).to(dt).contiguous()
+            pd = Pw.to(dt).contiguous()
+            vp = pool_of((vd,), vd.numel() * vd.element_size())
+            for i in range(3):
+                torch.bmm(pd, vp[i % len(vp)][0])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(40):
+                torch.bmm(pd, vp[i % len(vp)][0])
+            e1.record()
+            torch.cuda.synchronize()
+            base[label] = round(e0.elapsed_time(e1) * 1e3 / 40, 2)
+            del vp, vd, pd
+            torch.cuda.empty_cache()
+        del Vf
+        return {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "pct_hbm_peak": round(100 * nbytes / (us * 1e-6) / 8e12, 2), "bytes": nbytes,
+                "torch_bf16_values_us": base["bf16"], "torch_fp32_values_us": base["fp32"],
+                "speedup_vs_fp32": round(base["fp32"] / us, 2), "speedup_vs_bf16": round(base["bf16"] / us, 2)}
+
+    rows["kv_attend_3bit_h8_n131072_q4"] = kv_attend_row(3)
+    log("kv attend 3-bit:", rows["kv_attend_3bit_h8_n131072_q4"])
     # mixed widths at batch 8 (MLP shape)
     for bits in (3, 2):
         rows[f"gemv_{bits}b_g32_gate_B8"] = gemv_row("gate", W_gate, bits, 32, 8)

@@ -350,6 +350,12 @@ def qtq_quant_values(V: torch.Tensor, bits: int, Pi: torch.Tensor, delta: float,
     return codes, norms
 
 
+def qtq_attend_ws(n: int, heads: int, nq: int) -> int:
+    need = ctypes.c_size_t()
+    _check(load().qtq_attend_ws(n, heads, nq, ctypes.byref(need)), "qtq_attend_ws")
+    return need.value
+
+
 def qtq_attend(codes, norms, n: int, heads: int, bits: int, delta: float, table, Pi, P: torch.Tensor,
                out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
     """out[heads][nq][128] = P[heads][nq][n] times the dequantized values."""
@@ -359,9 +365,7 @@ def qtq_attend(codes, norms, n: int, heads: int, bits: int, delta: float, table,
     if out is None:
         out = torch.empty((heads, nq, 128), dtype=torch.float32, device=P.device)
     if ws is None:
-        need = ctypes.c_size_t()
-        _check(load().qtq_attend_ws(n, heads, nq, ctypes.byref(need)), "qtq_attend_ws")
-        ws = torch.empty(need.value, dtype=torch.uint8, device=P.device)
+        ws = torch.empty(qtq_attend_ws(n, heads, nq), dtype=torch.uint8, device=P.device)
     t = np.ascontiguousarray(table, dtype=np.uint8)
     _check(load().qtq_attend(_ptr(codes), _ptr(norms), n, heads, bits, float(delta), t.ctypes.data_as(ctypes.c_void_p),
                              _ptr(Pi), _ptr(P), nq, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "qtq_attend")
