@@ -418,8 +418,7 @@ int qtq_quant_values(const float* V, int64_t n, int bits, const double* Pi, floa
 
 int qtq_attend_ws(int64_t n, int64_t heads, int64_t nq, size_t* ws_bytes) {
   if (n < 1 || heads < 1 || heads > 65535 || nq < 1 || nq > 65535 || !ws_bytes) return Q_EINVAL;
-  const int64_t Q = nq <= 1 ? 1 : (nq <= 2 ? 2 : 4);
-  *ws_bytes = (size_t)(heads * ((nq + Q - 1) / Q) * qg::tq_attend_blocks(n, heads) * Q * 129 * 4);
+  *ws_bytes = (size_t)(heads * ((nq + 15) / 16) * qg::tq_attend_blocks(n, heads) * 16 * 129 * 4);
   return Q_OK;
 }
 

@@ -255,133 +255,130 @@ __global__ __launch_bounds__(256) void tq_logits_kernel(const uint32_t* __restri
 // ------------------------------------------------------------ value output
 // Attention output over quantized values (the reconstruction variant):
 //   o[h][q] = sum_i P[h][q][i] |v_i| Pi^T c[code_i].
-// Pass 1 streams the values (4 lanes per value, one 32-coordinate unit each,
-// the codebook byte-permute decode) and accumulates, per coordinate of the
-// rotated domain, a[q][j] = sum_i w_i (128 + e[code_ij]) and W[q] = sum_i w_i
-// with w_i = P[q][i] |v_i| in fp32; the 16 value slots of a wave meet by
-// cross-lane sums, the 4 waves of a workgroup in LDS, and each workgroup
-// leaves its partial sums in the workspace.  Pass 2 adds the partials,
-// forms o_rot = delta (a - 192 W) and o = Pi^T o_rot (fp32).
+// Pass 1 sums in the rotated domain on the matrix cores:
+//   a[j][q] = sum_i (128 + e[code_ij]) w_q,i,  W_q = sum_i w_q,i,  w = P |v|.
+// A wave takes 16 values per step.  Lane l decodes unit l / 16 of value l % 16
+// (codebook byte-permute decode, bf16 128 + e) and writes its 32 coordinates
+// into a per-wave LDS tile laid out [coordinate][value]; then
+// v_mfma_f32_16x16x16_bf16 multiplies 8 tiles of 16 coordinates x 16 values
+// (A, read back with one 8-byte LDS load per tile) by the weights of 16
+// values x 16 queries (B, bf16 hi + lo, two MFMAs), lane l of B holding query
+// l % 16 and values 4 (l / 16) .. + 3 straight from P and the norms.  The
+// four waves of a workgroup meet in LDS and each workgroup leaves its
+// partial sums in the workspace.  Pass 2 adds the partials, forms
+// o_rot = delta (a - 192 W) and o = Pi^T o_rot (fp32).
 constexpr int kTqPart = 129;             // floats per (workgroup, query): 128 sums + W
+constexpr int kTqVPitch = 20;            // u16 per coordinate row of a wave's value tile (8-byte aligned rows)
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-template <int M, int Q>
+template <int M>
 __global__ __launch_bounds__(256) void tq_attend_kernel(const uint32_t* __restrict__ codes,
                                                         const uint32_t* __restrict__ norms, int n, int nq,
                                                         const float* __restrict__ P, uint4 tab,
                                                         float* __restrict__ part) {
-  __shared__ float red[4][Q][128];
-  __shared__ float wred[4][Q];
+  __shared__ __align__(16) uint16_t vt[4][128 * kTqVPitch];
+  __shared__ float red[4][16][129];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kg = lane & 3, slot = lane >> 2;
-  const int h = blockIdx.y, q0 = blockIdx.z * Q;
+  const int r = lane & 15, kg = lane >> 4;            // decode: value r, unit kg; B: query r, values 4 kg ..
+  const int h = blockIdx.y, q = blockIdx.z * 16 + r;
+  const bool qok = q < nq;
   const uint32_t T[4] = {tab.x, tab.y, tab.z, tab.w};
   const CbConst kc = cb_consts();
   const size_t hk = (size_t)h * n;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes + hk * 4 * M, (uint32_t)((size_t)n * 16 * M));
   const __amdgpu_buffer_rsrc_t nrs = make_rsrc(norms + hk, (uint32_t)((size_t)n * 4));
-  __amdgpu_buffer_rsrc_t prs[Q];
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(P + ((size_t)h * nq + (qok ? q : 0)) * n, qok ? (uint32_t)((size_t)n * 4) : 0u);
+  uint16_t* tile = vt[wave];
+  f32x4_t acc[8];
 #pragma unroll
-  for (int t = 0; t < Q; ++t) {
-    const int q = q0 + t < nq ? q0 + t : nq - 1;         // padded queries read a real row, never stored
-    prs[t] = make_rsrc(P + ((size_t)h * nq + q) * n, (uint32_t)((size_t)n * 4));
-  }
-  float acc[Q][32], ws_[Q];
-#pragma unroll
-  for (int t = 0; t < Q; ++t) {
-    ws_[t] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) acc[t][e] = 0.f;
-  }
-  struct Raw { uint32_t c[M]; uint32_t nm; uint32_t p[Q]; };
-  auto load = [&](int key, Raw& r) {
-    const bool ok = key < n;
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  struct Raw { uint32_t c[M]; uint32_t nm[4]; uint32_t p[4]; };
+  auto load = [&](int base, Raw& rw) {
+    const int key = base + r;
     const uint32_t u = (uint32_t)key * 4 + (uint32_t)kg;
-    buf_load_unit<M>(crs, ok ? u * (M * 4) : 0xFFFFFF00u, 0u, r.c);
-    r.nm = buf_load_u32(nrs, ok ? (uint32_t)key * 4 : 0xFFFFFF00u, 0u);
+    buf_load_unit<M>(crs, key < n ? u * (M * 4) : 0xFFFFFF00u, 0u, rw.c);
 #pragma unroll
-    for (int t = 0; t < Q; ++t) r.p[t] = buf_load_u32(prs[t], ok ? (uint32_t)key * 4 : 0xFFFFFF00u, 0u);
+    for (int i = 0; i < 4; ++i) {
+      const int kk = base + 4 * kg + i;
+      rw.nm[i] = buf_load_u32(nrs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
+      rw.p[i] = buf_load_u32(prs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
+    }
   };
-  auto compute = [&](const Raw& r) {
+  auto compute = [&](const Raw& rw) {
     uint32_t pr[16];
-    decode_unit_cb<M>(r.c, T, pr, kc);
-    const float nrm = f16_bits_to_f32(r.nm & 0xFFFFu);
-    float lo[16], hi[16];
+    decode_unit_cb<M>(rw.c, T, pr, kc);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      lo[k] = bf16_lo_to_f32(pr[k]);
-      hi[k] = bf16_hi_to_f32(pr[k]);
+      const PairInfo pi = Unit<M>::pair(k);
+      tile[(32 * kg + pi.ca) * kTqVPitch + r] = (uint16_t)(pr[k] & 0xFFFFu);
+      tile[(32 * kg + pi.cb) * kTqVPitch + r] = (uint16_t)(pr[k] >> 16);
     }
+    // B: weights w = P |v| of values 4 kg .. 4 kg + 3 for query r, bf16 hi + lo
+    float w[4];
 #pragma unroll
-    for (int t = 0; t < Q; ++t) {
-      const float w = __uint_as_float(r.p[t]) * nrm;     // 0 past n (loads read 0)
-      if (kg == 0) ws_[t] += w;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        acc[t][2 * k] = __builtin_fmaf(w, lo[k], acc[t][2 * k]);
-        acc[t][2 * k + 1] = __builtin_fmaf(w, hi[k], acc[t][2 * k + 1]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      w[i] = __uint_as_float(rw.p[i]) * f16_bits_to_f32(rw.nm[i] & 0xFFFFu);
+      wsum += w[i];
     }
+    const uint32_t h01 = cvt_pk_bf16(w[0], w[1]), h23 = cvt_pk_bf16(w[2], w[3]);
+    const uint32_t l01 = cvt_pk_bf16(w[0] - bf16_lo_to_f32(h01), w[1] - bf16_hi_to_f32(h01));
+    const uint32_t l23 = cvt_pk_bf16(w[2] - bf16_lo_to_f32(h23), w[3] - bf16_hi_to_f32(h23));
+    const s16x4_t bh = __builtin_bit_cast(s16x4_t, (uint64_t)h01 | ((uint64_t)h23 << 32));
+    const s16x4_t bl = __builtin_bit_cast(s16x4_t, (uint64_t)l01 | ((uint64_t)l23 << 32));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      // A: coordinate 16 t + r, values 4 kg .. 4 kg + 3
+      const s16x4_t a = *reinterpret_cast<const s16x4_t*>(tile + (16 * t + r) * kTqVPitch + 4 * kg);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bh, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bl, acc[t], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   const int stride = gridDim.x * 4 * 16;
-  int key = (blockIdx.x * 4 + wave) * 16 + slot;
+  int base = (blockIdx.x * 4 + wave) * 16;
   Raw ra{}, rb{};
-  load(key, ra);
-  while (key - slot < n) {                                 // wave-uniform
-    load(key + stride, rb);
+  load(base, ra);
+  while (base < n) {                                   // wave-uniform
+    load(base + stride, rb);
     __builtin_amdgcn_sched_barrier(0);
     compute(ra);
     ra = rb;
-    key += stride;
+    base += stride;
   }
-  // the 16 value slots of a wave (lane bits 2..5) share each unit kg
+  // lane l of tile t holds a[16 t + 4 (l / 16) + i][query l % 16]; W over the 4 lane groups
+  wsum += __shfl_xor(wsum, 16);
+  wsum += __shfl_xor(wsum, 32);
 #pragma unroll
-  for (int t = 0; t < Q; ++t) {
+  for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      float v = acc[t][e];
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[t][e] = v;
-    }
-    ws_[t] = wave_sum(ws_[t]);
-  }
-  if (slot == 0) {
-#pragma unroll
-    for (int t = 0; t < Q; ++t)
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const PairInfo pi = Unit<M>::pair(k);
-        red[wave][t][32 * kg + pi.ca] = acc[t][2 * k];
-        red[wave][t][32 * kg + pi.cb] = acc[t][2 * k + 1];
-      }
-  }
-  if (lane == 0)
-#pragma unroll
-    for (int t = 0; t < Q; ++t) wred[wave][t] = ws_[t];
+    for (int i = 0; i < 4; ++i) red[wave][r][16 * t + 4 * kg + i] = acc[t][i];
+  if (kg == 0) red[wave][r][128] = wsum;
   __syncthreads();
-  float* dst = part + (((size_t)h * gridDim.z + blockIdx.z) * gridDim.x + blockIdx.x) * Q * kTqPart;
-  for (int i = threadIdx.x; i < Q * kTqPart; i += 256) {
-    const int t = i / kTqPart, j = i % kTqPart;
-    dst[i] = j < 128 ? red[0][t][j] + red[1][t][j] + red[2][t][j] + red[3][t][j]
-                     : wred[0][t] + wred[1][t] + wred[2][t] + wred[3][t];
+  float* dst = part + (((size_t)h * gridDim.z + blockIdx.z) * gridDim.x + blockIdx.x) * 16 * kTqPart;
+  for (int i = threadIdx.x; i < 16 * kTqPart; i += 256) {
+    const int qq = i / kTqPart, j = i % kTqPart;
+    dst[i] = red[0][qq][j] + red[1][qq][j] + red[2][qq][j] + red[3][qq][j];
   }
 }
 
-template <int Q>
-__global__ __launch_bounds__(128) void tq_attend_finish_kernel(const float* __restrict__ part, int nblk, int nchunk,
-                                                               int nq, const double* __restrict__ Pi, float delta,
+__global__ __launch_bounds__(128) void tq_attend_finish_kernel(const float* __restrict__ part, int nblk, int nq,
+                                                               const double* __restrict__ Pi, float delta,
                                                                float* __restrict__ out) {
   __shared__ float orot[128];
   __shared__ float wtot;
   const int h = blockIdx.x, q = blockIdx.y, i = threadIdx.x;
-  const int ch = q / Q, t = q % Q;
-  const float* src = part + (((size_t)h * nchunk + ch) * nblk) * Q * kTqPart + t * kTqPart;
+  const int nchunk = (nq + 15) / 16, ch = q / 16, t = q % 16;
+  const float* src = part + (((size_t)h * nchunk + ch) * nblk) * 16 * kTqPart + t * kTqPart;
   float a = 0.f, w = 0.f;
   for (int b = 0; b < nblk; ++b) {
-    a += src[(size_t)b * Q * kTqPart + i];
-    if (i == 0) w += src[(size_t)b * Q * kTqPart + 128];
+    a += src[(size_t)b * 16 * kTqPart + i];
+    if (i == 0) w += src[(size_t)b * 16 * kTqPart + 128];
   }
   if (i == 0) wtot = w;
   __syncthreads();
@@ -403,23 +400,21 @@ int64_t tq_attend_blocks(int64_t n, int64_t heads) {
 hipError_t launch_tq_attend(const uint32_t* codes, const uint32_t* norms, int64_t n, int64_t heads, int mbits,
                             float delta, const uint32_t* tab, const double* Pi, const float* P, int64_t nq,
                             float* out, float* part, hipStream_t s) {
-  const int Q = nq <= 1 ? 1 : (nq <= 2 ? 2 : 4);
-  const int64_t nb = tq_attend_blocks(n, heads), nch = (nq + Q - 1) / Q;
+  const int64_t nb = tq_attend_blocks(n, heads), nch = (nq + 15) / 16;
   const dim3 grid((unsigned)nb, (unsigned)heads, (unsigned)nch);
   const uint4 t4{tab[0], tab[1], tab[2], tab[3]};
-#define L(MB, QQ)                                                                                       \
-  hipLaunchKernelGGL((tq_attend_kernel<MB, QQ>), grid, dim3(256), 0, s, codes, norms, (int)n, (int)nq, P, t4, part)
-  if (mbits == 2) { if (Q == 1) L(2, 1); else if (Q == 2) L(2, 2); else L(2, 4); }
-  else if (mbits == 3) { if (Q == 1) L(3, 1); else if (Q == 2) L(3, 2); else L(3, 4); }
-  else if (mbits == 4) { if (Q == 1) L(4, 1); else if (Q == 2) L(4, 2); else L(4, 4); }
-  else return hipErrorInvalidValue;
-#undef L
+  if (mbits == 2)
+    hipLaunchKernelGGL((tq_attend_kernel<2>), grid, dim3(256), 0, s, codes, norms, (int)n, (int)nq, P, t4, part);
+  else if (mbits == 3)
+    hipLaunchKernelGGL((tq_attend_kernel<3>), grid, dim3(256), 0, s, codes, norms, (int)n, (int)nq, P, t4, part);
+  else if (mbits == 4)
+    hipLaunchKernelGGL((tq_attend_kernel<4>), grid, dim3(256), 0, s, codes, norms, (int)n, (int)nq, P, t4, part);
+  else
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 fg((unsigned)heads, (unsigned)nq);
-  if (Q == 1) hipLaunchKernelGGL((tq_attend_finish_kernel<1>), fg, dim3(128), 0, s, part, (int)nb, (int)nch, (int)nq, Pi, delta, out);
-  else if (Q == 2) hipLaunchKernelGGL((tq_attend_finish_kernel<2>), fg, dim3(128), 0, s, part, (int)nb, (int)nch, (int)nq, Pi, delta, out);
-  else hipLaunchKernelGGL((tq_attend_finish_kernel<4>), fg, dim3(128), 0, s, part, (int)nb, (int)nch, (int)nq, Pi, delta, out);
+  hipLaunchKernelGGL(tq_attend_finish_kernel, dim3((unsigned)heads, (unsigned)nq), dim3(128), 0, s, part, (int)nb,
+                     (int)nq, Pi, delta, out);
   return hipGetLastError();
 }
 

@@ -176,7 +176,7 @@ def test_value_encoder_bit_exact(gpu, bits):
     assert np.array_equal(host(nm).view(np.uint32), n16.view(np.uint16).astype(np.uint32))
 
 
-@pytest.mark.parametrize("bits,nq,n", [(3, 1, 1000), (3, 4, 1000), (4, 2, 1000), (2, 5, 1000), (4, 4, 20000)])
+@pytest.mark.parametrize("bits,nq,n", [(3, 1, 1000), (3, 4, 1000), (4, 2, 1000), (2, 5, 1000), (3, 18, 777), (4, 4, 20000)])
 def test_attend(gpu, bits, nq, n):
     """Attention output over quantized values against the oracle's fp64
     sum; fp32 sums over the values in the rotated domain, so the error is a
