@@ -367,26 +367,39 @@ __global__ __launch_bounds__(256) void tq_attend_kernel(const uint32_t* __restri
   }
 }
 
-__global__ __launch_bounds__(128) void tq_attend_finish_kernel(const float* __restrict__ part, int nblk, int nq,
+// 256 threads: output i = t % 128, half t / 128 of the partials and of the
+// Pi^T sum, four independent accumulators each, halves combined in LDS.
+__global__ __launch_bounds__(256) void tq_attend_finish_kernel(const float* __restrict__ part, int nblk, int nq,
                                                                const double* __restrict__ Pi, float delta,
                                                                float* __restrict__ out) {
-  __shared__ float orot[128];
-  __shared__ float wtot;
-  const int h = blockIdx.x, q = blockIdx.y, i = threadIdx.x;
-  const int nchunk = (nq + 15) / 16, ch = q / 16, t = q % 16;
-  const float* src = part + (((size_t)h * nchunk + ch) * nblk) * 16 * kTqPart + t * kTqPart;
-  float a = 0.f, w = 0.f;
-  for (int b = 0; b < nblk; ++b) {
-    a += src[(size_t)b * 16 * kTqPart + i];
-    if (i == 0) w += src[(size_t)b * 16 * kTqPart + 128];
-  }
-  if (i == 0) wtot = w;
+  __shared__ float orot[128], half_a[128], half_o[128];
+  __shared__ float wpart[2];
+  const int h = blockIdx.x, q = blockIdx.y, t = threadIdx.x, i = t & 127, hh = t >> 7;
+  const int nchunk = (nq + 15) / 16, ch = q / 16, qq = q % 16;
+  const float* src = part + (((size_t)h * nchunk + ch) * nblk) * 16 * kTqPart + qq * kTqPart;
+  const size_t bs = (size_t)16 * kTqPart;
+  float a[4] = {0.f, 0.f, 0.f, 0.f}, w = 0.f;
+  const int b0 = hh * ((nblk + 1) / 2), b1 = hh ? nblk : (nblk + 1) / 2;
+  int b = b0;
+  for (; b + 3 < b1; b += 4)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] += src[(b + u) * bs + i];
+  for (; b < b1; ++b) a[0] += src[b * bs + i];
+  if (i == 0)
+    for (int c = b0; c < b1; ++c) w += src[c * bs + 128];
+  if (hh) half_a[i] = (a[0] + a[1]) + (a[2] + a[3]);
+  if (i == 0) wpart[hh] = w;
   __syncthreads();
-  orot[i] = delta * (a - 192.0f * wtot);
+  if (!hh) orot[i] = delta * ((a[0] + a[1]) + (a[2] + a[3]) + half_a[i] - 192.0f * (wpart[0] + wpart[1]));
   __syncthreads();
-  float o = 0.f;
-  for (int j = 0; j < 128; ++j) o = __builtin_fmaf((float)Pi[j * 128 + i], orot[j], o);   // (Pi^T o_rot)_i
-  out[((size_t)h * nq + q) * 128 + i] = o;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int j = 64 * hh; j < 64 * hh + 64; j += 4)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = __builtin_fmaf((float)Pi[(j + u) * 128 + i], orot[j + u], o[u]);   // (Pi^T o_rot)_i
+  if (hh) half_o[i] = (o[0] + o[1]) + (o[2] + o[3]);
+  __syncthreads();
+  if (!hh) out[((size_t)h * nq + q) * 128 + i] = (o[0] + o[1]) + (o[2] + o[3]) + half_o[i];
 }
 
 // workgroups per head for the value pass (also sizes the workspace)
@@ -413,7 +426,7 @@ hipError_t launch_tq_attend(const uint32_t* codes, const uint32_t* norms, int64_
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tq_attend_finish_kernel, dim3((unsigned)heads, (unsigned)nq), dim3(128), 0, s, part, (int)nb,
+  hipLaunchKernelGGL(tq_attend_finish_kernel, dim3((unsigned)heads, (unsigned)nq), dim3(256), 0, s, part, (int)nb,
                      (int)nq, Pi, delta, out);
   return hipGetLastError();
 }
