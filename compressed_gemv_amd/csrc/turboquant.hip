@@ -191,10 +191,18 @@ __global__ __launch_bounds__(256) void tq_logits_kernel(const uint32_t* __restri
     const bool ok = key < n;
     buf_load_unit<M>(crs, ok ? u * (M * 4) : 0xFFFFFF00u, 0u, rw.c);
     rw.s = buf_load_u32(srs, ok ? u * 4 : 0xFFFFFF00u, 0u);
+    // the norms of keys 4 kg .. 4 kg + 3 (the rows of D this lane holds): one
+    // 16-byte load when all four are present, per key in a partial last group
+    const int k0 = base + 4 * kg;
+    if (k0 + 3 < n) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(nrs, (uint32_t)k0 * 4, 0u, kNT);
+      rw.nm[0] = v[0]; rw.nm[1] = v[1]; rw.nm[2] = v[2]; rw.nm[3] = v[3];
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = base + 4 * kg + i;
-      rw.nm[i] = buf_load_u32(nrs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
+      for (int i = 0; i < 4; ++i) {
+        const int kk = k0 + i;
+        rw.nm[i] = buf_load_u32(nrs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
+      }
     }
   };
   auto compute = [&](int base, const Raw& rw) {

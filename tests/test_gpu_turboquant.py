@@ -113,6 +113,22 @@ def test_logits(gpu, bits, nq):
     say(f"  tq logits bits={bits} nq={nq}: err={err:.2e}")
 
 
+@pytest.mark.parametrize("n", [1003, 17])
+def test_logits_ragged_key_count(gpu, n):
+    """Key counts that are not a multiple of 4 (the last group of four keys
+    is partial) and fewer keys than one wave step."""
+    bits = 4
+    Pi, S, delta, table, cv = _setup(bits, 60)
+    H = 2
+    K = _keys(H * n, 61)
+    parts, _, _, _ = _oracle_packed(K, bits, Pi, S, cv)
+    parts = tuple(p.reshape((H, n) + p.shape[1:]) for p in parts)
+    c, s, nm = gpu.qtq_quant_keys(dev(K), bits, dev(Pi), dev(S), delta, table)
+    Qv = rng_for(415, n).standard_normal((H, 3, 128)).astype(np.float32)
+    out = host(gpu.qtq_logits(c, s, nm, n, H, bits, delta, table, dev(Pi), dev(S), dev(Qv)))
+    _check_logits(out, Qv, parts, Pi, S, cv)
+
+
 def test_logits_long_context_sampled(gpu):
     """Two heads of 131072 keys (a 128K context), 4 grouped queries: every
     logit computed on the GPU, a sample of keys checked against the oracle
