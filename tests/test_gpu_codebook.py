@@ -168,3 +168,18 @@ def test_prefill_bf16_output(gpu):
     Xv = oracle.product.bf16_to_f64(X)
     check_err(Y, oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv),
               PREFILL_RTN_BOUND + 2.0 ** -8)
+
+
+@pytest.mark.parametrize("bits,group,K", [(4, 64, 64), (2, 32, 32), (3, 32, 96)])
+def test_gemv_single_group_rows(gpu, bits, group, K):
+    """The smallest rows: one or a few groups (K = 32..96), N = 1 and 5,
+    B = 1 and 3."""
+    books = _random_books(bits, 90 + K)
+    for N in (1, 5):
+        W = gen_weights(N, K, rng_for(380, N + K), outliers=False)
+        c, m, k, W_hat = _check_pack(gpu, W, bits, group, books)
+        for B in (1, 3):
+            xb = gen_x_bf16(B, K, rng_for(381, B))
+            xv = oracle.product.bf16_to_f64(xb)
+            y = host(gpu.qgemv_group_cb(c, m, k, dev(books), N, K, bits, group, dev_bf16(xb)))
+            check_err(y, oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))

@@ -113,7 +113,7 @@ def test_logits(gpu, bits, nq):
     say(f"  tq logits bits={bits} nq={nq}: err={err:.2e}")
 
 
-@pytest.mark.parametrize("n", [1003, 17])
+@pytest.mark.parametrize("n", [1003, 17, 3, 1])
 def test_logits_ragged_key_count(gpu, n):
     """Key counts that are not a multiple of 4 (the last group of four keys
     is partial) and fewer keys than one wave step."""
@@ -192,7 +192,8 @@ def test_value_encoder_bit_exact(gpu, bits):
     assert np.array_equal(host(nm).view(np.uint32), n16.view(np.uint16).astype(np.uint32))
 
 
-@pytest.mark.parametrize("bits,nq,n", [(3, 1, 1000), (3, 4, 1000), (4, 2, 1000), (2, 5, 1000), (3, 18, 777), (4, 4, 20000)])
+@pytest.mark.parametrize("bits,nq,n", [(3, 1, 1000), (3, 4, 1000), (4, 2, 1000), (2, 5, 1000), (3, 18, 777), (4, 4, 20000),
+                                       (3, 2, 1), (2, 1, 5)])
 def test_attend(gpu, bits, nq, n):
     """Attention output over quantized values against the oracle's fp64
     sum; fp32 sums over the values in the rotated domain, so the error is a
