@@ -383,6 +383,7 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         rng = np.random.default_rng(np.random.SeedSequence([0, 9, bits]))
         Pi = to_dev(cg.qtq_rotation(rng.standard_normal((128, 128))))
         S = to_dev(rng.standard_normal((128, 128)))
+        SPi = cg.qtq_project(S, Pi)
         delta, table = cg.qtq_centroids(128, bits - 1)
         Kf = torch.randn((H * n, 128), device=dev, generator=torch.Generator(device=dev).manual_seed(bits))
         c, sg, nm = cg.qtq_quant_keys(Kf, bits, Pi, S, delta, table)
@@ -394,7 +395,7 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
 
         def f(i):
             a, b_, m_ = pool[i % len(pool)]
-            cg.qtq_logits(a, b_, m_, n, H, bits, delta, table, Pi, S, Qv, out=out, ws=ws)
+            cg.qtq_logits(a, b_, m_, n, H, bits, delta, table, Pi, SPi, Qv, out=out, ws=ws)
         wall, ev = time_launches(f, 100, 10, period=len(pool))
         del pool
         torch.cuda.empty_cache()

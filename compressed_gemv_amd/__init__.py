@@ -20,7 +20,7 @@ __all__ = [
     "qgroup_sizes", "qpack_group", "qunpack_group", "qgemv_group",
     "qgroup_outlier_ws", "qpack_group_outlier", "qgemv_group_outlier", "qgemv_group_multi",
     "qcodebook_default", "qpack_group_cb", "qgemv_group_cb",
-    "qtq_centroids", "qtq_rotation", "qtq_quant_keys", "qtq_logits", "qtq_quant_values", "qtq_attend",
+    "qtq_centroids", "qtq_rotation", "qtq_quant_keys", "qtq_project", "qtq_logits", "qtq_quant_values", "qtq_attend",
     "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr",
     "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
 ]
@@ -90,6 +90,7 @@ def load() -> ctypes.CDLL:
         "qtq_sizes": (I32, [I64, I32, SZ, SZ, SZ]),
         "qtq_quant_keys": (I32, [P, I64, I32, P, P, ctypes.c_float, P, P, P, P, P]),
         "qtq_logits_ws": (I32, [I64, I64, SZ]),
+        "qtq_project": (I32, [P, P, P, P]),
         "qtq_logits": (I32, [P, P, P, I64, I64, I32, ctypes.c_float, P, P, P, P, I64, P, P, ctypes.c_size_t, P]),
         "qtq_quant_values": (I32, [P, I64, I32, P, ctypes.c_float, P, P, P, P]),
         "qtq_attend_ws": (I32, [I64, I64, I64, SZ]),
@@ -318,11 +319,20 @@ def qtq_quant_keys(K: torch.Tensor, bits: int, Pi: torch.Tensor, S: torch.Tensor
     return codes, signs, norms
 
 
-def qtq_logits(codes, signs, norms, n: int, heads: int, bits: int, delta: float, table, Pi, S, Qv: torch.Tensor,
+def qtq_project(S: torch.Tensor, Pi: torch.Tensor, stream=None) -> torch.Tensor:
+    """S Pi (fp64, device), the second matrix qtq_logits takes."""
+    _need_cuda(S, Pi)
+    out = torch.empty((128, 128), dtype=torch.float64, device=S.device)
+    _check(load().qtq_project(_ptr(S), _ptr(Pi), _ptr(out), _stream(stream)), "qtq_project")
+    return out
+
+
+def qtq_logits(codes, signs, norms, n: int, heads: int, bits: int, delta: float, table, Pi, SPi, Qv: torch.Tensor,
                out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
-    """out[heads][nq][n] fp32 logits for queries Qv[heads][nq][128] (fp32)."""
+    """out[heads][nq][n] fp32 logits for queries Qv[heads][nq][128] (fp32);
+    SPi = qtq_project(S, Pi)."""
     import numpy as np
-    _need_cuda(codes, signs, norms, Pi, S, Qv, out, ws)
+    _need_cuda(codes, signs, norms, Pi, SPi, Qv, out, ws)
     nq = Qv.shape[1]
     if out is None:
         out = torch.empty((heads, nq, n), dtype=torch.float32, device=Qv.device)
@@ -332,7 +342,7 @@ def qtq_logits(codes, signs, norms, n: int, heads: int, bits: int, delta: float,
         ws = torch.empty(need.value, dtype=torch.uint8, device=Qv.device)
     t = np.ascontiguousarray(table, dtype=np.uint8)
     _check(load().qtq_logits(_ptr(codes), _ptr(signs), _ptr(norms), n, heads, bits, float(delta),
-                             t.ctypes.data_as(ctypes.c_void_p), _ptr(Pi), _ptr(S), _ptr(Qv), nq, _ptr(out), _ptr(ws),
+                             t.ctypes.data_as(ctypes.c_void_p), _ptr(Pi), _ptr(SPi), _ptr(Qv), nq, _ptr(out), _ptr(ws),
                              ws.numel(), _stream(stream)), "qtq_logits")
     return out
 

@@ -374,23 +374,29 @@ int qtq_logits_ws(int64_t heads, int64_t nq, size_t* ws_bytes) {
   return Q_OK;
 }
 
+int qtq_project(const double* S, const double* Pi, double* SPi, hipStream_t stream) {
+  if (!S || !Pi || !SPi) return Q_EINVAL;
+  if (!aligned(S, 8) || !aligned(Pi, 8) || !aligned(SPi, 8)) return Q_EALIGN;
+  return hip_status(qg::launch_tq_project(S, Pi, SPi, stream));
+}
+
 int qtq_logits(const void* codes, const uint32_t* signs, const uint32_t* norms, int64_t n, int64_t heads,
-               int bits, float delta, const uint8_t* table, const double* Pi, const double* S, const float* Qv,
+               int bits, float delta, const uint8_t* table, const double* Pi, const double* SPi, const float* Qv,
                int64_t nq, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = tq_args_ok(n, heads, bits, delta, table);
   if (st != Q_OK) return st;
   size_t need = 0;
   if ((st = qtq_logits_ws(heads, nq, &need)) != Q_OK) return st;
-  if (!codes || !signs || !norms || !Pi || !S || !Qv || !out) return Q_EINVAL;
+  if (!codes || !signs || !norms || !Pi || !SPi || !Qv || !out) return Q_EINVAL;
   if (!ws || ws_bytes < need) return Q_EWORKSPACE;
-  if (!aligned(codes, 4) || !aligned(signs, 4) || !aligned(norms, 4) || !aligned(Pi, 8) || !aligned(S, 8) ||
+  if (!aligned(codes, 4) || !aligned(signs, 4) || !aligned(norms, 4) || !aligned(Pi, 8) || !aligned(SPi, 8) ||
       !aligned(Qv, 4) || !aligned(out, 4) || !aligned(ws, 16))
     return Q_EALIGN;
   if (heads * nq * n > ((int64_t)1 << 40)) return Q_EUNSUPPORTED;
   uint32_t tw[4];
   tq_table_words(table, 1 << (bits - 1), tw);
   return hip_status(qg::launch_tq_logits(static_cast<const uint32_t*>(codes), signs, norms, n, heads, bits - 1,
-                                         delta, tw[0], tw[1], Pi, S, Qv, nq, out, static_cast<uint32_t*>(ws), stream));
+                                         delta, tw[0], tw[1], Pi, SPi, Qv, nq, out, static_cast<uint32_t*>(ws), stream));
 }
 
 int qtq_quant_values(const float* V, int64_t n, int bits, const double* Pi, float delta, const uint8_t* table,

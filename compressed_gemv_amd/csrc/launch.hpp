@@ -58,9 +58,10 @@ int64_t tq_attend_blocks(int64_t n, int64_t heads);
 hipError_t launch_tq_attend(const uint32_t* codes, const uint32_t* norms, int64_t n, int64_t heads, int mbits,
                             float delta, const uint32_t* tab, const double* Pi, const float* P, int64_t nq,
                             float* out, float* part, hipStream_t s);
+hipError_t launch_tq_project(const double* S, const double* Pi, double* SPi, hipStream_t s);
 hipError_t launch_tq_logits(const uint32_t* codes, const uint32_t* signs, const uint32_t* norms, int64_t n,
                             int64_t heads, int mbits, float delta, uint32_t tab_lo, uint32_t tab_hi,
-                            const double* Pi, const double* S, const float* Qv, int64_t nq, float* out,
+                            const double* Pi, const double* SPi, const float* Qv, int64_t nq, float* out,
                             uint32_t* ws, hipStream_t s);
 hipError_t launch_gemm_group_cb(const uint32_t* codes, const uint32_t* meta, const uint8_t* book_ids,
                                 const uint8_t* books, int n_books, int64_t N, int64_t K, int bits, int group,

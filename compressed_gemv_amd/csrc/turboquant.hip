@@ -8,8 +8,9 @@
 // unbiased estimate
 //   <q, x> ~ |x| (delta sum_j (e[code_j] - 64) (Pi q)_j
 //                 + gamma sqrt(pi/2)/d sum_j sign_j (S Pi q)_j).
-// A prep kernel forms Pi q and S Pi q once per query (fp64 sums, rounded to
-// bf16 and laid out as the operand pairs of the logit kernel).  The logit
+// A prep kernel forms Pi q and S Pi q = (S Pi) q once per query (fp32,
+// rounded to bf16 and laid out as the operand pairs of the logit kernel); S Pi
+// is formed once per (Pi, S) pair (qtq_project).  The logit
 // kernel streams the keys: the centroid codes go through the codebook
 // byte-permute decode (pairs 128 + e[code] in bf16) and the sign bits become
 // bf16 +-1 pairs with one shift and one masked OR; the products with up to
@@ -88,44 +89,73 @@ void tq_rotation(int d, const double* G, double* Pi) {
 }
 
 // ------------------------------------------------------------ query prep
-// Per (query, head): qr = Pi q, u = S qr in fp64 (increasing index order),
-// then for unit w and pair k: word w*32 + k = bf16 (qr[32w + ca], qr[32w + cb])
-// with (ca, cb) the code pair k of an M-bit unit; word w*32 + 16 + j =
-// bf16 (u[32w + j], u[32w + j + 16]); float at 128 + w = the sum of the 32
-// bf16-rounded qr values of unit w (the 128-bias correction).
-constexpr int kTqQueryWords = 132;
+// SPi = S Pi, formed once per (Pi, S) pair: then Pi q and S Pi q = SPi q are
+// independent products and one launch forms both.
+__global__ __launch_bounds__(128) void tq_project_kernel(const double* __restrict__ S, const double* __restrict__ Pi,
+                                                         double* __restrict__ SPi) {
+  const int i = blockIdx.x, k = threadIdx.x;
+  double a = 0.0;
+  for (int j = 0; j < 128; ++j) a = __builtin_fma(S[i * 128 + j], Pi[j * 128 + k], a);
+  SPi[i * 128 + k] = a;
+}
 
+// Per (query, head): qr = Pi q and u = SPi q, then for unit w and pair k:
+// word w*32 + k = bf16 (qr[32w + ca], qr[32w + cb]) with (ca, cb) the code
+// pair k of an M-bit unit; word w*32 + 16 + j = bf16 (u[32w + j],
+// u[32w + j + 16]); float at 128 + w = the sum of the 32 bf16-rounded qr
+// values of unit w (the 128-bias correction).  Grid (heads, 2 matrices, 4
+// units): a workgroup stages the unit's 32 rows of its matrix in LDS as fp32
+// (coalesced reads, 129-word pitch), multiplies them by every query of the
+// head and writes that unit's words of its half (fp32 products, rounded once
+// to bf16).
+constexpr int kTqQueryWords = 132;
+constexpr int kTqPitch = 129;
 
 template <int M>
-__global__ __launch_bounds__(128) void tq_prep_kernel(const float* __restrict__ Qv, int nq, const double* __restrict__ Pi,
-                                                      const double* __restrict__ S, uint32_t* __restrict__ ws) {
-  constexpr int D = 128;
-  __shared__ double qs[D], qr[D];
-  __shared__ uint32_t qb[D], ub[D];
-  const int qi = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
-  const size_t row = (size_t)h * nq + qi;
-  qs[i] = (double)Qv[row * D + i];
-  __syncthreads();
-  double a = 0.0;
-  for (int j = 0; j < D; ++j) a = a + qs[j] * Pi[i * D + j];
-  qr[i] = a;
-  qb[i] = f32_to_bf16_rne((float)a);
-  __syncthreads();
-  double b = 0.0;
-  for (int j = 0; j < D; ++j) b = b + qr[j] * S[i * D + j];
-  ub[i] = f32_to_bf16_rne((float)b);
-  __syncthreads();
-  uint32_t* out = ws + row * kTqQueryWords;
-  if (i < 64) {
-    const int w = i / 16, k = i % 16;
-    const PairInfo pi = Unit<M>::pair(k);
-    out[w * 32 + k] = qb[32 * w + pi.ca] | (qb[32 * w + pi.cb] << 16);
-    out[w * 32 + 16 + k] = ub[32 * w + k] | (ub[32 * w + k + 16] << 16);
-  } else if (i < 68) {
-    const int w = i - 64;
-    float s = 0.f;
-    for (int c = 0; c < 32; ++c) s += bf16_bits_to_f32(qb[32 * w + c]);
-    out[128 + w] = __float_as_uint(s);
+__global__ __launch_bounds__(256) void tq_prep_kernel(const float* __restrict__ Qv, int nq, const double* __restrict__ Pi,
+                                                      const double* __restrict__ SPi, uint32_t* __restrict__ ws) {
+  __shared__ float As[32][kTqPitch], v[16][128], res[16][32];
+  const int h = blockIdx.x, mat = blockIdx.y, w = blockIdx.z, t = threadIdx.x;
+  const double* A = mat ? SPi : Pi;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int e = t + 256 * k;                          // rows 32 w .. 32 w + 31
+    As[e >> 7][e & 127] = (float)A[(size_t)(32 * w) * 128 + e];
+  }
+  for (int q0 = 0; q0 < nq; q0 += 16) {
+    const int cnt = nq - q0 < 16 ? nq - q0 : 16;
+    for (int i = t; i < cnt * 128; i += 256) v[i >> 7][i & 127] = Qv[((size_t)h * nq + q0) * 128 + i];
+    __syncthreads();
+    {
+      const int r = t & 31;
+      for (int j = t >> 5; j < cnt; j += 8) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < 128; c += 2) {
+          a0 = __builtin_fmaf(As[r][c], v[j][c], a0);
+          a1 = __builtin_fmaf(As[r][c + 1], v[j][c + 1], a1);
+        }
+        res[j][r] = a0 + a1;
+      }
+    }
+    __syncthreads();
+    for (int i = t; i < cnt * 17; i += 256) {
+      const int j = i / 17, k = i % 17;
+      uint32_t* out = ws + ((size_t)h * nq + q0 + j) * kTqQueryWords;
+      if (mat == 0) {
+        if (k < 16) {
+          const PairInfo pi = Unit<M>::pair(k);
+          out[w * 32 + k] = f32_to_bf16_rne(res[j][pi.ca]) | (f32_to_bf16_rne(res[j][pi.cb]) << 16);
+        } else {
+          float sum = 0.f;
+          for (int c = 0; c < 32; ++c) sum += bf16_bits_to_f32(f32_to_bf16_rne(res[j][c]));
+          out[128 + w] = __float_as_uint(sum);
+        }
+      } else if (k < 16) {
+        out[w * 32 + 16 + k] = f32_to_bf16_rne(res[j][k]) | (f32_to_bf16_rne(res[j][k + 16]) << 16);
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -439,13 +469,18 @@ hipError_t launch_tq_attend(const uint32_t* codes, const uint32_t* norms, int64_
   return hipGetLastError();
 }
 
+hipError_t launch_tq_project(const double* S, const double* Pi, double* SPi, hipStream_t s) {
+  hipLaunchKernelGGL(tq_project_kernel, dim3(128), dim3(128), 0, s, S, Pi, SPi);
+  return hipGetLastError();
+}
+
 hipError_t launch_tq_logits(const uint32_t* codes, const uint32_t* signs, const uint32_t* norms, int64_t n,
                             int64_t heads, int mbits, float delta, uint32_t tab_lo, uint32_t tab_hi,
-                            const double* Pi, const double* S, const float* Qv, int64_t nq, float* out,
+                            const double* Pi, const double* SPi, const float* Qv, int64_t nq, float* out,
                             uint32_t* ws, hipStream_t s) {
-  const dim3 pg((unsigned)nq, (unsigned)heads);
-  if (mbits == 2) hipLaunchKernelGGL((tq_prep_kernel<2>), pg, dim3(128), 0, s, Qv, (int)nq, Pi, S, ws);
-  else if (mbits == 3) hipLaunchKernelGGL((tq_prep_kernel<3>), pg, dim3(128), 0, s, Qv, (int)nq, Pi, S, ws);
+  const dim3 pg((unsigned)heads, 2, 4);
+  if (mbits == 2) hipLaunchKernelGGL((tq_prep_kernel<2>), pg, dim3(256), 0, s, Qv, (int)nq, Pi, SPi, ws);
+  else if (mbits == 3) hipLaunchKernelGGL((tq_prep_kernel<3>), pg, dim3(256), 0, s, Qv, (int)nq, Pi, SPi, ws);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -230,17 +230,20 @@ int qtq_sizes(int64_t n, int bits, size_t* codes_bytes, size_t* signs_bytes, siz
  * a non-finite key or a norm beyond fp16. */
 int qtq_quant_keys(const float* K, int64_t n, int bits, const double* Pi, const double* S, float delta,
                    const uint8_t* table, void* codes, uint32_t* signs, uint32_t* norms, hipStream_t stream);
+/* SPi = S Pi (row-major 128 x 128 fp64, device), formed once per (Pi, S)
+ * pair for qtq_logits: S Pi q is then one product.  Asynchronous. */
+int qtq_project(const double* S, const double* Pi, double* SPi, hipStream_t stream);
 /* Workspace bytes of qtq_logits for `heads` heads of nq queries (host). */
 int qtq_logits_ws(int64_t heads, int64_t nq, size_t* ws_bytes);
 /* Attention logits from quantized keys: for every head h < heads, query
  * i < nq (Qv[h][i][128], fp32, device) and key j < n of that head (the keys
  * of head h are rows h*n .. h*n + n - 1 of codes/signs/norms),
  *   out[h][i][j] = |x| (<Pi q, c[code]> + gamma sqrt(pi/2)/128 <S Pi q, sign>),
- * with Pi q and S Pi q formed in fp64 and rounded once to bf16, products
- * accumulated in fp32.  ws: device, >= the qtq_logits_ws value, 16-byte
- * aligned.  Asynchronous. */
+ * with Pi q and S Pi q = SPi q (SPi from qtq_project) formed in fp32 and
+ * rounded once to bf16, products accumulated in fp32.  ws: device, >= the
+ * qtq_logits_ws value, 16-byte aligned.  Asynchronous. */
 int qtq_logits(const void* codes, const uint32_t* signs, const uint32_t* norms, int64_t n, int64_t heads,
-               int bits, float delta, const uint8_t* table, const double* Pi, const double* S, const float* Qv,
+               int bits, float delta, const uint8_t* table, const double* Pi, const double* SPi, const float* Qv,
                int64_t nq, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 /* Values (the page's reconstruction variant): bits = 2, 3 or 4 codebook
  * bits per coordinate, no sign bits; codes [n][4][bits] as for keys, norms

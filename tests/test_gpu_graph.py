@@ -140,6 +140,7 @@ def test_graph_key_logits(gpu):
     Qv = dev(rng.standard_normal((H, nq, 128)).astype(np.float32))
     out = torch.empty((H, nq, n), dtype=torch.float32, device=Qv.device)
     ws = torch.empty(H * nq * 132 * 4, dtype=torch.uint8, device=Qv.device)
-    g = _capture(lambda: gpu.qtq_logits(c, sg, nm, n, H, 4, delta, table, Pi, S, Qv, out=out, ws=ws))
+    SPi = gpu.qtq_project(S, Pi)
+    g = _capture(lambda: gpu.qtq_logits(c, sg, nm, n, H, 4, delta, table, Pi, SPi, Qv, out=out, ws=ws))
     qs = [dev(rng_for(99, i).standard_normal((H, nq, 128)).astype(np.float32)) for i in range(3)]
-    _check_replays(g, out, lambda: gpu.qtq_logits(c, sg, nm, n, H, 4, delta, table, Pi, S, Qv), qs, Qv)
+    _check_replays(g, out, lambda: gpu.qtq_logits(c, sg, nm, n, H, 4, delta, table, Pi, SPi, Qv), qs, Qv)

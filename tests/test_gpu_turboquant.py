@@ -108,7 +108,7 @@ def test_logits(gpu, bits, nq):
     parts = tuple(p.reshape((H, n) + p.shape[1:]) for p in parts)
     c, s, nm = gpu.qtq_quant_keys(dev(K), bits, dev(Pi), dev(S), delta, table)
     Qv = rng_for(412, nq).standard_normal((H, nq, 128)).astype(np.float32)
-    out = host(gpu.qtq_logits(c, s, nm, n, H, bits, delta, table, dev(Pi), dev(S), dev(Qv)))
+    out = host(gpu.qtq_logits(c, s, nm, n, H, bits, delta, table, dev(Pi), gpu.qtq_project(dev(S), dev(Pi)), dev(Qv)))
     err = _check_logits(out, Qv, parts, Pi, S, cv)
     say(f"  tq logits bits={bits} nq={nq}: err={err:.2e}")
 
@@ -125,7 +125,7 @@ def test_logits_ragged_key_count(gpu, n):
     parts = tuple(p.reshape((H, n) + p.shape[1:]) for p in parts)
     c, s, nm = gpu.qtq_quant_keys(dev(K), bits, dev(Pi), dev(S), delta, table)
     Qv = rng_for(415, n).standard_normal((H, 3, 128)).astype(np.float32)
-    out = host(gpu.qtq_logits(c, s, nm, n, H, bits, delta, table, dev(Pi), dev(S), dev(Qv)))
+    out = host(gpu.qtq_logits(c, s, nm, n, H, bits, delta, table, dev(Pi), gpu.qtq_project(dev(S), dev(Pi)), dev(Qv)))
     _check_logits(out, Qv, parts, Pi, S, cv)
 
 
@@ -140,7 +140,7 @@ def test_logits_long_context_sampled(gpu):
     K = _keys(H * n, 31)
     c, s, nm = gpu.qtq_quant_keys(dev(K), bits, dev(Pi), dev(S), delta, table)
     Qv = rng_for(413, 0).standard_normal((H, 4, 128)).astype(np.float32)
-    out = host(gpu.qtq_logits(c, s, nm, n, H, bits, delta, table, dev(Pi), dev(S), dev(Qv)))
+    out = host(gpu.qtq_logits(c, s, nm, n, H, bits, delta, table, dev(Pi), gpu.qtq_project(dev(S), dev(Pi)), dev(Qv)))
     idx = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(19).choice(n, 200, replace=False)]))
     rows = np.concatenate([h * n + idx for h in range(H)])
     parts, words, sw, nw = _oracle_packed(K[rows], bits, Pi, S, cv)
@@ -165,7 +165,7 @@ def test_logits_estimate_inner_products(gpu):
     K = _keys(n, 41, outliers=False)
     c, s, nm = gpu.qtq_quant_keys(dev(K), bits, dev(Pi), dev(S), delta, table)
     Qv = rng_for(414, 0).standard_normal((1, 1, 128)).astype(np.float32)
-    est = host(gpu.qtq_logits(c, s, nm, n, 1, bits, delta, table, dev(Pi), dev(S), dev(Qv)))[0, 0]
+    est = host(gpu.qtq_logits(c, s, nm, n, 1, bits, delta, table, dev(Pi), gpu.qtq_project(dev(S), dev(Pi)), dev(Qv)))[0, 0]
     true = K.astype(np.float64) @ Qv[0, 0].astype(np.float64)
     slope = float(est @ true / (true @ true))
     assert abs(slope - 1.0) < 0.02, slope
