@@ -336,11 +336,21 @@ __global__ __launch_bounds__(256) void tq_attend_kernel(const uint32_t* __restri
     const int key = base + r;
     const uint32_t u = (uint32_t)key * 4 + (uint32_t)kg;
     buf_load_unit<M>(crs, key < n ? u * (M * 4) : 0xFFFFFF00u, 0u, rw.c);
+    // norms and weights of values 4 kg .. 4 kg + 3: one 16-byte load each when
+    // all four are present, per value in a partial last group
+    const int k0 = base + 4 * kg;
+    if (k0 + 3 < n) {
+      const auto vn = __builtin_amdgcn_raw_buffer_load_b128(nrs, (uint32_t)k0 * 4, 0u, kNT);
+      const auto vp = __builtin_amdgcn_raw_buffer_load_b128(prs, (uint32_t)k0 * 4, 0u, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = base + 4 * kg + i;
-      rw.nm[i] = buf_load_u32(nrs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
-      rw.p[i] = buf_load_u32(prs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
+      for (int i = 0; i < 4; ++i) { rw.nm[i] = vn[i]; rw.p[i] = vp[i]; }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = k0 + i;
+        rw.nm[i] = buf_load_u32(nrs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
+        rw.p[i] = buf_load_u32(prs, kk < n ? (uint32_t)kk * 4 : 0xFFFFFF00u, 0u);
+      }
     }
   };
   auto compute = [&](const Raw& rw) {
