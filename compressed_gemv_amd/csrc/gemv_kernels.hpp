@@ -270,7 +270,6 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       float acc_row = 0.f;
-      if constexpr (OUT) acc_row = f16_bits_to_f32(sv[r] & 0xFFFFu) * xo;
 #pragma unroll
       for (int it = 0; it < UI; ++it) {
         uint32_t pr[16];
@@ -307,6 +306,9 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
         const float o = f16_bits_to_f32(m[r][it] >> 16);
         acc_row = __builtin_fmaf(s, sq, __builtin_fmaf(o, xsum[it], acc_row));
       }
+      // the side value is the stage's last load: used last, so the units
+      // above are decoded while it is still in flight
+      if constexpr (OUT) acc_row = __builtin_fmaf(f16_bits_to_f32(sv[r] & 0xFFFFu), xo, acc_row);
       const float total = wave_sum(acc_row);
       const int row = row0 + r * nstreams;
       if (row < N && lane == 0) {
