@@ -144,3 +144,21 @@ def test_graph_key_logits(gpu):
     g = _capture(lambda: gpu.qtq_logits(c, sg, nm, n, H, 4, delta, table, Pi, SPi, Qv, out=out, ws=ws))
     qs = [dev(rng_for(99, i).standard_normal((H, nq, 128)).astype(np.float32)) for i in range(3)]
     _check_replays(g, out, lambda: gpu.qtq_logits(c, sg, nm, n, H, 4, delta, table, Pi, SPi, Qv), qs, Qv)
+
+
+def test_graph_value_attend(gpu):
+    """Value output (the streaming pass and its finishing pass) replayed with
+    new weights."""
+    say("graph qtq_attend")
+    rng = rng_for(100, 0)
+    Pi = dev(gpu.qtq_rotation(rng.standard_normal((128, 128))))
+    delta, table = gpu.qtq_centroids(128, 3)
+    H, n, nq = 2, 3000, 4
+    V = dev(rng.standard_normal((H * n, 128)).astype(np.float32))
+    c, nm = gpu.qtq_quant_values(V, 3, Pi, delta, table)
+    P = dev(rng.random((H, nq, n)).astype(np.float32))
+    out = torch.empty((H, nq, 128), dtype=torch.float32, device=P.device)
+    ws = torch.empty(gpu.qtq_attend_ws(n, H, nq), dtype=torch.uint8, device=P.device)
+    g = _capture(lambda: gpu.qtq_attend(c, nm, n, H, 3, delta, table, Pi, P, out=out, ws=ws))
+    ps = [dev(rng_for(101, i).random((H, nq, n)).astype(np.float32)) for i in range(3)]
+    _check_replays(g, out, lambda: gpu.qtq_attend(c, nm, n, H, 3, delta, table, Pi, P), ps, P)
