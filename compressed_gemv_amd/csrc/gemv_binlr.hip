@@ -28,8 +28,10 @@
 // stage-2 workgroup only copies the table into LDS.
 //
 // Work split: a workgroup owns RT row tiles (16 RT rows) and NS waves that
-// split the 512-bit K-steps; each wave loads all of its sign words for a
-// table chunk up front, the table lands in LDS meanwhile, and the NS partial
+// split the 512-bit K-steps.  Per table chunk a thread first issues its share
+// of the table's loads (x and s2, or the stage-2 table: L2 hits), then all of
+// its wave's sign words (HBM); loads return in issue order, so the table is
+// built in LDS while the sign words are still on their way.  The NS partial
 // sums meet in LDS.
 #include "common.hpp"
 #include "launch.hpp"
@@ -64,16 +66,18 @@ struct Stage2Out {         // where stage 1 leaves the stage-2 table
 // MODE 0: v = s2 * x (x bf16) -> stage-2 table
 // MODE 1: v = s2 * x (x fp32) -> stage-2 table
 // MODE 2: v from the stage-2 table -> y = s1 * dot (fp32 or bf16)
-template <int MODE, int RT>
+template <int MODE, int RT, int SPW>
 __global__ __launch_bounds__(1024) void bin_mfma_kernel(
     const uint32_t* __restrict__ bits, int R, int Wn, int Lk, const void* __restrict__ vin,
     const uint16_t* __restrict__ vscale, const uint16_t* __restrict__ oscale,
     void* __restrict__ out, int y_bf16, int64_t in_bstride, int64_t out_bstride, int vec_ok,
     Stage2Out s2o, int nparts) {
-  constexpr int SPW = 8 / RT;                       // max K-steps per wave and chunk
+  // SPW: max K-steps per wave and chunk (a power of two, SPW RT <= 8)
+  static_assert(SPW * RT <= 8, "sign words held per wave");
   __shared__ u32x4_t tab[kStepsPerChunk * 16 * 2 * 4];   // 32 KB
   __shared__ float red[kMaxNS][RT * 16];
   __shared__ float sums[kMaxNS][2];
+  __shared__ uint16_t junk[2];
   const int lane = threadIdx.x & 63;
   const int NS = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -99,98 +103,163 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
     const int cs = min(kStepsPerChunk, steps - c0);
     // this wave's steps of the chunk: c0 + wave, c0 + wave + NS, ...
     const int my = wave < cs ? (cs - wave + NS - 1) / NS : 0;
+    // Loads return in issue order, so the table's loads (L2 hits) go out
+    // before the sign words (HBM): the table is written to LDS while the
+    // signs are still in flight instead of after the last of them arrives.
+    // The table's share of this thread is known exactly: a chunk has at most
+    // SPW steps per wave, i.e. 2 SPW table entries (MODE 2) or SPW groups of
+    // 8 vector entries (MODE 0/1) per thread.
+    constexpr int CP = 2 * SPW;                     // MODE 2: table entries per thread
+    constexpr int PG = SPW < 2 ? SPW : 2;           // MODE 0/1: groups per load batch
+    u32x4_t pre[CP];
+    u32x4_t rs[PG], ra[PG], rb[PG];                 // raw s2 and x of one batch of groups
+    const int ncopy = cs * 128;
+    const int ngr = cs * 64;
+    // Unconditional buffer loads (reads past the range return 0), so no load
+    // sits in a divergent branch; the fast path's tail test is applied where
+    // the values are used.  With unaligned rows the range is empty and the
+    // scalar path below reads the entries.
+    constexpr uint32_t esz = MODE == 0 ? 2u : 4u;
+    const __amdgpu_buffer_rsrc_t xrs =
+        make_rsrc(MODE == 2 ? static_cast<const void*>(s2o.tab + s2o.tab_bstride * b + c0 * 1024)
+                            : static_cast<const void*>(static_cast<const char*>(vin) + in_bstride * b * esz),
+                  MODE == 2 ? (uint32_t)ncopy * 16u : (vec_ok ? (uint32_t)Lk * esz : 0u));
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(vscale, vec_ok && MODE != 2 ? (uint32_t)Lk * 2u : 0u);
+    auto fetch = [&](int g, int q) {
+      const uint32_t k = (uint32_t)(c0 * 64 + g) * 8u;
+      const auto sv = __builtin_amdgcn_raw_buffer_load_b128(srs, k * 2u, 0, 0);
+      rs[q] = u32x4_t{sv[0], sv[1], sv[2], sv[3]};
+      const auto av = __builtin_amdgcn_raw_buffer_load_b128(xrs, k * esz, 0, 0);
+      ra[q] = u32x4_t{av[0], av[1], av[2], av[3]};
+      if constexpr (MODE == 1) {
+        const auto bv = __builtin_amdgcn_raw_buffer_load_b128(xrs, k * esz + 16u, 0, 0);
+        rb[q] = u32x4_t{bv[0], bv[1], bv[2], bv[3]};
+      }
+    };
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int q = 0; q < CP; ++q) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(xrs, (threadIdx.x + q * blockDim.x) * 16u, 0, 0);
+        pre[q] = u32x4_t{v[0], v[1], v[2], v[3]};
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < PG; ++q) fetch(threadIdx.x + q * blockDim.x, q);
+    }
+    // keep the table's loads ahead of the sign words (neither the optimizer
+    // nor the scheduler may move loads across this point)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // every slot is loaded (no branch, so the waits stay exact); slots past
+    // this wave's steps read past the buffer, which returns 0 and fetches nothing
     u32x4_t w[SPW][RT];
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      if (i < my) {
-        const uint32_t soff = (uint32_t)(c0 + wave + i * NS) * 64u;   // 16 words per step
+      const uint32_t soff = (uint32_t)(c0 + wave + i * NS) * 64u;   // 16 words per step
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, voff[t] + soff, 0, kNT);
-          w[i][t] = u32x4_t{v[0], v[1], v[2], v[3]};
-        }
+      for (int t = 0; t < RT; ++t) {
+        const uint32_t off = i < my ? voff[t] + soff : 0xFFFFFF00u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, kNT);
+        w[i][t] = u32x4_t{v[0], v[1], v[2], v[3]};
       }
     }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (MODE == 2) {
-      // copy this chunk of the stage-2 table
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(s2o.tab + s2o.tab_bstride * b) + c0 * 128;
-      for (int i = threadIdx.x; i < cs * 128; i += blockDim.x) tab[i] = src[i];
+      // this thread's entries of this chunk of the stage-2 table
+#pragma unroll
+      for (int q = 0; q < CP; ++q) {
+        const int i = threadIdx.x + q * blockDim.x;
+        if (i < ncopy) tab[i] = pre[q];
+      }
     } else {
-      // build the chunk from x and s2: a thread takes groups of 8 consecutive
-      // entries (16-byte loads), two groups' loads in flight at a time
-      const int ngr = cs * 64;
-      for (int g0 = threadIdx.x; g0 < ngr; g0 += 2 * blockDim.x) {
-        float v[2][8];
+      // build the chunk from x and s2: group g of 8 consecutive entries
+      // (16-byte loads) goes to thread g mod blockDim; the first batch uses
+      // the loads issued above, in straight-line code so they stay ahead of
+      // the sign words
+      uint16_t* t16 = reinterpret_cast<uint16_t*>(tab);
+      auto emit = [&](int g, int q) {
+        const int k = (c0 * 64 + g) * 8;
+        float v[8];
+        const u32x4_t sc = rs[q];
+        if constexpr (MODE == 0) {
+          const u32x4_t a = ra[q];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int g = g0 + q * blockDim.x;
-          const int k = (c0 * 64 + g) * 8;
-          if (vec_ok && g < ngr && k + 8 <= Lk) {
-            const u32x4_t sc = *reinterpret_cast<const u32x4_t*>(vscale + k);
-            if constexpr (MODE == 0) {
-              const u32x4_t a = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(vin) + in_bstride * b + k);
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_lo_to_f32(a[e]) * f16_bits_to_f32(sc[e] & 0xFFFFu);
+            v[2 * e + 1] = bf16_hi_to_f32(a[e]) * f16_bits_to_f32(sc[e] >> 16);
+          }
+        } else {
+          const u32x4_t a0 = ra[q], a1 = rb[q];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                v[q][2 * e] = bf16_lo_to_f32(a[e]) * f16_bits_to_f32(sc[e] & 0xFFFFu);
-                v[q][2 * e + 1] = bf16_hi_to_f32(a[e]) * f16_bits_to_f32(sc[e] >> 16);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t xw = e < 4 ? a0[e] : a1[e - 4];
+            const uint32_t sh = (e & 1) ? (sc[e / 2] >> 16) : (sc[e / 2] & 0xFFFFu);
+            v[e] = __uint_as_float(xw) * f16_bits_to_f32(sh);
+          }
+        }
+        // tails and unaligned rows replace the fast path's values entry by
+        // entry
+        const bool fast = vec_ok && g < ngr && k + 8 <= Lk;
+        float sl[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (!fast) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (g < ngr && k + e < Lk) {
+              float xv;
+              if constexpr (MODE == 0) {
+                xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k + e]);
+              } else {
+                xv = static_cast<const float*>(vin)[in_bstride * b + k + e];
               }
-            } else {
-              const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(vin) + in_bstride * b + k);
-              const u32x4_t a0 = src[0], a1 = src[1];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t xw = e < 4 ? a0[e] : a1[e - 4];
-                const uint32_t sh = (e & 1) ? (sc[e / 2] >> 16) : (sc[e / 2] & 0xFFFFu);
-                v[q][e] = __uint_as_float(xw) * f16_bits_to_f32(sh);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              float xv = 0.f;
-              if (g < ngr && k + e < Lk) {
-                if constexpr (MODE == 0) {
-                  xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k + e]);
-                } else {
-                  xv = static_cast<const float*>(vin)[in_bstride * b + k + e];
-                }
-                xv *= f16_bits_to_f32(vscale[k + e]);
-              }
-              v[q][e] = xv;
+              sl[e] = xv * f16_bits_to_f32(vscale[k + e]);
             }
           }
         }
-        uint16_t* t16 = reinterpret_cast<uint16_t*>(tab);
+        // the empty asm pins the selected values here, so the compiler
+        // cannot fold the select into the branch and sink the fast path's
+        // loads behind the sign words
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int g = g0 + q * blockDim.x;
-          if (g < ngr) {
-            const int odd = g & 1;
-            const int ep = ((g >> 2) & 3) * 2 + ((g >> 1) & 1);
-            const int ent0 = (g >> 6) * 16 * 8 + ((g >> 4) & 3);
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              // pair j = 8 odd + e (kl & 15) lands on bit j, j - 7 or j - 14
-              const int p0 = odd ? (e < 6 ? e + 1 : e - 6) : e;
-              const int p1 = odd ? (e + 1 < 6 ? e + 2 : e - 5) : (e + 1 < 7 ? e + 1 : 0);
-              const float a0 = v[q][e] * __builtin_ldexpf(1.0f, -p0);     // exact
-              const float a1 = v[q][e + 1] * __builtin_ldexpf(1.0f, -p1);
-              const uint32_t hi = cvt_pk_bf16(a0, a1);
-              const float h0 = bf16_lo_to_f32(hi), h1 = bf16_hi_to_f32(hi);
-              const uint32_t lo = cvt_pk_bf16(a0 - h0, a1 - h1);
-              const float l0 = bf16_lo_to_f32(lo), l1 = bf16_hi_to_f32(lo);
-              const int j0 = 8 * odd + e;
-              t16[(ent0 + j0 * 8) * 8 + ep] = (uint16_t)(hi & 0xFFFFu);
-              t16[(ent0 + j0 * 8 + 4) * 8 + ep] = (uint16_t)(lo & 0xFFFFu);
-              t16[(ent0 + (j0 + 1) * 8) * 8 + ep] = (uint16_t)(hi >> 16);
-              t16[(ent0 + (j0 + 1) * 8 + 4) * 8 + ep] = (uint16_t)(lo >> 16);
-              const float s0 = h0 + l0, s1 = h1 + l1;
-              csum += s0 + s1;
-              vsum = __builtin_fmaf(s0, __builtin_ldexpf(1.0f, p0), vsum);
-              vsum = __builtin_fmaf(s1, __builtin_ldexpf(1.0f, p1), vsum);
-            }
-          }
+        for (int e = 0; e < 8; ++e) {
+          v[e] = fast ? v[e] : sl[e];
+          asm volatile("" : "+v"(v[e]));
         }
+        // groups past the chunk write to a junk slot and add nothing, so
+        // this part has no branch either
+        const bool valid = g < ngr;
+        const int odd = g & 1;
+        const int ep = ((g >> 2) & 3) * 2 + ((g >> 1) & 1);
+        const int ent0 = (g >> 6) * 16 * 8 + ((g >> 4) & 3);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          // pair j = 8 odd + e (kl & 15) lands on bit j, j - 7 or j - 14
+          const int p0 = odd ? (e < 6 ? e + 1 : e - 6) : e;
+          const int p1 = odd ? (e + 1 < 6 ? e + 2 : e - 5) : (e + 1 < 7 ? e + 1 : 0);
+          const float a0 = v[e] * __builtin_ldexpf(1.0f, -p0);     // exact
+          const float a1 = v[e + 1] * __builtin_ldexpf(1.0f, -p1);
+          const uint32_t hi = cvt_pk_bf16(a0, a1);
+          const float h0 = bf16_lo_to_f32(hi), h1 = bf16_hi_to_f32(hi);
+          const uint32_t lo = cvt_pk_bf16(a0 - h0, a1 - h1);
+          const float l0 = bf16_lo_to_f32(lo), l1 = bf16_hi_to_f32(lo);
+          const int j0 = 8 * odd + e;
+          *(valid ? t16 + (ent0 + j0 * 8) * 8 + ep : junk) = (uint16_t)(hi & 0xFFFFu);
+          *(valid ? t16 + (ent0 + j0 * 8 + 4) * 8 + ep : junk) = (uint16_t)(lo & 0xFFFFu);
+          *(valid ? t16 + (ent0 + (j0 + 1) * 8) * 8 + ep : junk) = (uint16_t)(hi >> 16);
+          *(valid ? t16 + (ent0 + (j0 + 1) * 8 + 4) * 8 + ep : junk) = (uint16_t)(lo >> 16);
+          const float s0 = valid ? h0 + l0 : 0.f, s1 = valid ? h1 + l1 : 0.f;
+          csum += s0 + s1;
+          vsum = __builtin_fmaf(s0, __builtin_ldexpf(1.0f, p0), vsum);
+          vsum = __builtin_fmaf(s1, __builtin_ldexpf(1.0f, p1), vsum);
+        }
+      };
+#pragma unroll
+      for (int q = 0; q < PG; ++q) emit(threadIdx.x + q * blockDim.x, q);
+#pragma unroll
+      for (int q0 = PG; q0 < SPW; q0 += PG) {
+#pragma unroll
+        for (int q = 0; q < PG; ++q) fetch(threadIdx.x + (q0 + q) * blockDim.x, q);
+#pragma unroll
+        for (int q = 0; q < PG; ++q) emit(threadIdx.x + (q0 + q) * blockDim.x, q);
       }
     }
     __syncthreads();
@@ -289,15 +358,16 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
   }
 }
 
-// waves per workgroup: enough for ~2048 waves in all, each with at most
-// 8 / RT steps per chunk, never more waves than steps
-int64_t pick_ns(int64_t blocks, int64_t Wn, int rt) {
+// waves per workgroup: enough for ~2048 waves in all, never more waves than
+// steps, and at most max_pw steps per wave and chunk (the sign words a wave
+// holds in registers)
+int64_t pick_ns(int64_t blocks, int64_t Wn, int max_pw) {
   const int64_t steps = (Wn + 15) / 16;
   const int64_t chunk_steps = steps < kStepsPerChunk ? steps : kStepsPerChunk;
   int64_t ns = 1;
   while (ns < kMaxNS && ns < chunk_steps && blocks * ns < 2048) ns *= 2;
-  while ((chunk_steps + ns - 1) / ns > 8 / rt && ns < kMaxNS) ns *= 2;
-  return (chunk_steps + ns - 1) / ns > 8 / rt ? -1 : ns;
+  while ((chunk_steps + ns - 1) / ns > max_pw && ns < kMaxNS) ns *= 2;
+  return (chunk_steps + ns - 1) / ns > max_pw ? -1 : ns;
 }
 
 template <int MODE, int RT>
@@ -305,16 +375,33 @@ hipError_t bin_launch(const uint32_t* bits, int64_t R, int64_t Wn, int64_t Lk, c
                       const uint16_t* vscale, const uint16_t* oscale, void* out, int y_bf16,
                       int64_t B, int64_t in_bstride, int64_t out_bstride, Stage2Out s2o,
                       int nparts, hipStream_t s) {
+  // stage 1 builds its table from registers loaded next to the sign words,
+  // so it keeps fewer steps per wave than stage 2
+  constexpr int kMaxPW = MODE == 2 ? 4 : 2;
   const int64_t blocks = (R + 16 * RT - 1) / (16 * RT);
-  const int64_t ns = pick_ns(blocks, Wn, RT);
+  const int64_t ns = pick_ns(blocks, Wn, kMaxPW);
   if (ns < 0) return hipErrorInvalidValue;
   // 16-byte vector reads of the input vector and s2 need 16-byte aligned rows
   const size_t esz = MODE == 0 ? 2 : 4;
   const int vec_ok = MODE == 2 || ((reinterpret_cast<uintptr_t>(vin) % 16 == 0) && ((in_bstride * esz) % 16 == 0) &&
                                    reinterpret_cast<uintptr_t>(vscale) % 16 == 0);
-  hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT>), dim3((unsigned)blocks, (unsigned)B), dim3((unsigned)(64 * ns)),
-                     0, s, bits, (int)R, (int)Wn, (int)Lk, vin, vscale, oscale, out, y_bf16,
-                     in_bstride, out_bstride, vec_ok, s2o, nparts);
+  // steps per wave, rounded up to a power of two: the kernel holds exactly
+  // that many sign-word slots and table loads per thread
+  const int64_t steps = (Wn + 15) / 16;
+  const int64_t chunk_steps = steps < kStepsPerChunk ? steps : kStepsPerChunk;
+  const int64_t per_wave = (chunk_steps + ns - 1) / ns;
+  const dim3 grid((unsigned)blocks, (unsigned)B), block((unsigned)(64 * ns));
+#define QG_BIN_LAUNCH(SPW_)                                                                          \
+  hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT, SPW_>), grid, block, 0, s, bits, (int)R, (int)Wn, (int)Lk, \
+                     vin, vscale, oscale, out, y_bf16, in_bstride, out_bstride, vec_ok, s2o, nparts)
+  if (per_wave <= 1) {
+    QG_BIN_LAUNCH(1);
+  } else if (per_wave <= 2 || kMaxPW == 2) {
+    QG_BIN_LAUNCH(2);             // pick_ns keeps per_wave <= kMaxPW
+  } else {
+    QG_BIN_LAUNCH(kMaxPW);
+  }
+#undef QG_BIN_LAUNCH
   return hipGetLastError();
 }
 
