@@ -63,7 +63,8 @@ def test_integer_case_exact(gpu):
     assert np.array_equal(y, (xi.astype(np.int64) @ C.T).astype(np.float64))
 
 
-@pytest.mark.parametrize("N,K,r", [(257, 1000, 300), (64, 8192, 2048), (33, 96, 129), (40, 20000, 9000)])
+@pytest.mark.parametrize("N,K,r", [(257, 1000, 300), (64, 8192, 2048), (33, 96, 129), (40, 20000, 9000),
+                                   (16421, 300, 129), (16400, 96, 1100)])
 @pytest.mark.parametrize("xkind", ["bf16", "f32"])
 def test_random_within_bound(gpu, N, K, r, xkind):
     say(f"binlr N={N} K={K} r={r} {xkind}")
