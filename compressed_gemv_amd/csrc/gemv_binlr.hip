@@ -98,6 +98,8 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float csum = 0.f, vsum = 0.f;                     // this thread's share of C and V
   const uint32_t bias = opaque_bias();
+  float part_c = 0.f, part_v = 0.f;                 // stage 2: see below
+  uint32_t s1_bits = 0;
 
   for (int c0 = 0; c0 < steps; c0 += kStepsPerChunk) {
     const int cs = min(kStepsPerChunk, steps - c0);
@@ -162,6 +164,18 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, kNT);
         w[i][t] = u32x4_t{v[0], v[1], v[2], v[3]};
       }
+    }
+    if constexpr (MODE == 2) {
+      // Stage 2's tail needs the (C, V) partials of stage 1 and s1 of the
+      // rows: loaded behind the sign words (every chunk, so no branch), they
+      // arrive while the matrix cores work instead of after them (buffer
+      // loads: past the range they return 0)
+      const __amdgpu_buffer_rsrc_t prs = make_rsrc(s2o.part + s2o.part_bstride * b, (uint32_t)nparts * 8u);
+      const auto pv = __builtin_amdgcn_raw_buffer_load_b64(prs, threadIdx.x * 8u, 0, 0);
+      part_c = __uint_as_float(pv[0]);
+      part_v = __uint_as_float(pv[1]);
+      const __amdgpu_buffer_rsrc_t ors = make_rsrc(oscale, (uint32_t)R * 2u);
+      s1_bits = __builtin_amdgcn_raw_buffer_load_b16(ors, (uint32_t)(row_base + lane) * 2u, 0, 0);
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -292,8 +306,10 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
 
   // C and V of the whole vector (every workgroup has the same sums)
   if constexpr (MODE == 2) {
+    csum += part_c;
+    vsum += part_v;
     const float* pp = s2o.part + s2o.part_bstride * b;
-    for (int i = threadIdx.x; i < nparts; i += blockDim.x) { csum += pp[2 * i]; vsum += pp[2 * i + 1]; }
+    for (int i = threadIdx.x + blockDim.x; i < nparts; i += blockDim.x) { csum += pp[2 * i]; vsum += pp[2 * i + 1]; }
   }
   csum = wave_sum(csum);
   vsum = wave_sum(vsum);
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
     }
     if constexpr (MODE == 2) {
       if (lane < 16 * RT && row < R) {
-        const float yv = dot * f16_bits_to_f32(oscale[row]);
+        const float yv = dot * f16_bits_to_f32(s1_bits & 0xFFFFu);
         if (y_bf16) static_cast<uint16_t*>(out)[out_bstride * b + row] = (uint16_t)f32_to_bf16_rne(yv);
         else static_cast<float*>(out)[out_bstride * b + row] = yv;
       }
