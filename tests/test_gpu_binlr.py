@@ -101,3 +101,31 @@ def test_full_size(gpu, K, N, r):
     xv = oracle.product.bf16_to_f64(x)
     err = check_err(y, oracle.product.matmul_ref(W, xv), oracle.product.abs_denominator(W, xv))
     say(f"  err={err:.3e}")
+
+
+@pytest.mark.parametrize("xkind", ["bf16", "f32"])
+@pytest.mark.parametrize("shift_s2", [False, True])
+def test_unaligned_vector_and_scale(gpu, xkind, shift_s2):
+    """x starting 4 bytes into its buffer (the alignment the entry point
+    requires) and optionally s2 one element in, so neither is 16-byte
+    aligned: stage 1 reads every vector entry one by one; K = 1003 also
+    leaves a ragged last group."""
+    N, K, r = 300, 1003, 200
+    U, V, s1, s2 = gen_binlr(N, K, r, rng_for(65, K))
+    W = oracle.binlr.reconstruct(U, V, s1, s2)
+    rng = rng_for(66, int(shift_s2))
+    if xkind == "bf16":
+        xf = gen_x_bf16(1, K + 2, rng)
+        xd = dev_bf16(xf)[:, 2:]
+        xv = oracle.product.bf16_to_f64(xf[:, 2:])
+    else:
+        xf = gen_x_f32(1, K + 1, rng)
+        xd = dev(xf)[:, 1:]
+        xv = xf[:, 1:].astype(np.float64)
+    s2d = dev(s2.view(np.int16))
+    if shift_s2:
+        s2d = dev(np.concatenate([[0], s2]).astype(np.uint16).view(np.int16))[1:]
+    assert xd.data_ptr() % 16 != 0
+    ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
+    y = host(gpu.qgemv_binlr(ubd, vbd, dev(s1.view(np.int16)), s2d, N, K, r, xd))
+    check_err(y, oracle.product.matmul_ref(W, xv), oracle.product.abs_denominator(W, xv))
