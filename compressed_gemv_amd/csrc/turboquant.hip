@@ -416,35 +416,53 @@ __global__ __launch_bounds__(256) void tq_attend_kernel(const uint32_t* __restri
 }
 
 // 256 threads: output i = t % 128, half t / 128 of the partials and of the
-// Pi^T sum, four independent accumulators each, halves combined in LDS.
+// Pi^T sum, halves combined in LDS.  The kernel is all latency (about 1 MB of
+// partials in all), so loads go out in batches rather than one round trip at
+// a time: the weight column W spread over all 256 threads (one block each)
+// and reduced across the waves, the partial sums 16 at a time, then the
+// thread's 64 entries of Pi in two batches of 32 (a wave can have at most 63
+// loads outstanding), the first issued before the reduction's barriers.
 __global__ __launch_bounds__(256) void tq_attend_finish_kernel(const float* __restrict__ part, int nblk, int nq,
                                                                const double* __restrict__ Pi, float delta,
                                                                float* __restrict__ out) {
   __shared__ float orot[128], half_a[128], half_o[128];
-  __shared__ float wpart[2];
+  __shared__ float wpart[4];
   const int h = blockIdx.x, q = blockIdx.y, t = threadIdx.x, i = t & 127, hh = t >> 7;
   const int nchunk = (nq + 15) / 16, ch = q / 16, qq = q % 16;
   const float* src = part + (((size_t)h * nchunk + ch) * nblk) * 16 * kTqPart + qq * kTqPart;
   const size_t bs = (size_t)16 * kTqPart;
-  float a[4] = {0.f, 0.f, 0.f, 0.f}, w = 0.f;
+  // W: block t now (consumed after the partial sums), further blocks after
+  float w = t < nblk ? src[(size_t)t * bs + 128] : 0.f;
+  float a[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) a[u] = 0.f;
   const int b0 = hh * ((nblk + 1) / 2), b1 = hh ? nblk : (nblk + 1) / 2;
   int b = b0;
-  for (; b + 3 < b1; b += 4)
+  for (; b + 15 < b1; b += 16)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] += src[(b + u) * bs + i];
+    for (int u = 0; u < 16; ++u) a[u] += src[(b + u) * bs + i];
   for (; b < b1; ++b) a[0] += src[b * bs + i];
-  if (i == 0)
-    for (int c = b0; c < b1; ++c) w += src[c * bs + 128];
-  if (hh) half_a[i] = (a[0] + a[1]) + (a[2] + a[3]);
-  if (i == 0) wpart[hh] = w;
-  __syncthreads();
-  if (!hh) orot[i] = delta * ((a[0] + a[1]) + (a[2] + a[3]) + half_a[i] - 192.0f * (wpart[0] + wpart[1]));
-  __syncthreads();
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int j = 64 * hh; j < 64 * hh + 64; j += 4)
+  for (int c = t + 256; c < nblk; c += 256) w += src[c * bs + 128];
+  float as = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = __builtin_fmaf((float)Pi[(j + u) * 128 + i], orot[j + u], o[u]);   // (Pi^T o_rot)_i
+  for (int u = 0; u < 16; ++u) as += a[u];
+  // Pi[j][i] for the first 32 of this thread's 64 j
+  double pv[32];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) pv[u] = Pi[(size_t)(64 * hh + u) * 128 + i];
+  w = wave_sum(w);
+  if (hh) half_a[i] = as;
+  if ((t & 63) == 0) wpart[t >> 6] = w;
+  __syncthreads();
+  if (!hh) orot[i] = delta * (as + half_a[i] - 192.0f * ((wpart[0] + wpart[1]) + (wpart[2] + wpart[3])));
+  __syncthreads();
+  float o[4] = {0.f, 0.f, 0.f, 0.f};                   // (Pi^T o_rot)_i
+#pragma unroll
+  for (int u = 0; u < 32; ++u) o[u & 3] = __builtin_fmaf((float)pv[u], orot[64 * hh + u], o[u & 3]);
+#pragma unroll
+  for (int u = 0; u < 32; ++u) pv[u] = Pi[(size_t)(64 * hh + 32 + u) * 128 + i];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) o[u & 3] = __builtin_fmaf((float)pv[u], orot[64 * hh + 32 + u], o[u & 3]);
   if (hh) half_o[i] = (o[0] + o[1]) + (o[2] + o[3]);
   __syncthreads();
   if (!hh) out[((size_t)h * nq + q) * 128 + i] = (o[0] + o[1]) + (o[2] + o[3]) + half_o[i];
