@@ -66,13 +66,16 @@ struct Stage2Out {         // where stage 1 leaves the stage-2 table
 // MODE 0: v = s2 * x (x bf16) -> stage-2 table
 // MODE 1: v = s2 * x (x fp32) -> stage-2 table
 // MODE 2: v from the stage-2 table -> y = s1 * dot (fp32 or bf16)
-template <int MODE, int RT, int SPW>
+template <int MODE, int RT, int SPW, bool FULL>
 __global__ __launch_bounds__(1024) void bin_mfma_kernel(
     const uint32_t* __restrict__ bits, int R, int Wn, int Lk, const void* __restrict__ vin,
     const uint16_t* __restrict__ vscale, const uint16_t* __restrict__ oscale,
     void* __restrict__ out, int y_bf16, int64_t in_bstride, int64_t out_bstride, int vec_ok,
     Stage2Out s2o, int nparts) {
-  // SPW: max K-steps per wave and chunk (a power of two, SPW RT <= 8)
+  // SPW: max K-steps per wave and chunk (a power of two, SPW RT <= 8).
+  // FULL (stage 1): every chunk has SPW steps per wave, the rows are 16-byte
+  // aligned and K is a multiple of 512, so every group of 8 entries takes the
+  // fast path and lies inside its chunk: no selects, no element-wise path.
   static_assert(SPW * RT <= 8, "sign words held per wave");
   __shared__ u32x4_t tab[kStepsPerChunk * 16 * 2 * 4];   // 32 KB
   __shared__ float red[kMaxNS][RT * 16];
@@ -212,35 +215,37 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
             v[e] = __uint_as_float(xw) * f16_bits_to_f32(sh);
           }
         }
-        // tails and unaligned rows replace the fast path's values entry by
-        // entry
-        const bool fast = vec_ok && g < ngr && k + 8 <= Lk;
-        float sl[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (!fast) {
+        if constexpr (!FULL) {
+          // tails and unaligned rows replace the fast path's values entry by
+          // entry
+          const bool fast = vec_ok && g < ngr && k + 8 <= Lk;
+          float sl[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (!fast) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (g < ngr && k + e < Lk) {
-              float xv;
-              if constexpr (MODE == 0) {
-                xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k + e]);
-              } else {
-                xv = static_cast<const float*>(vin)[in_bstride * b + k + e];
+            for (int e = 0; e < 8; ++e) {
+              if (g < ngr && k + e < Lk) {
+                float xv;
+                if constexpr (MODE == 0) {
+                  xv = bf16_bits_to_f32(static_cast<const uint16_t*>(vin)[in_bstride * b + k + e]);
+                } else {
+                  xv = static_cast<const float*>(vin)[in_bstride * b + k + e];
+                }
+                sl[e] = xv * f16_bits_to_f32(vscale[k + e]);
               }
-              sl[e] = xv * f16_bits_to_f32(vscale[k + e]);
             }
           }
-        }
-        // the empty asm pins the selected values here, so the compiler
-        // cannot fold the select into the branch and sink the fast path's
-        // loads behind the sign words
+          // the empty asm pins the selected values here, so the compiler
+          // cannot fold the select into the branch and sink the fast path's
+          // loads behind the sign words
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v[e] = fast ? v[e] : sl[e];
-          asm volatile("" : "+v"(v[e]));
+          for (int e = 0; e < 8; ++e) {
+            v[e] = fast ? v[e] : sl[e];
+            asm volatile("" : "+v"(v[e]));
+          }
         }
         // groups past the chunk write to a junk slot and add nothing, so
         // this part has no branch either
-        const bool valid = g < ngr;
+        const bool valid = FULL || g < ngr;
         const int odd = g & 1;
         const int ep = ((g >> 2) & 3) * 2 + ((g >> 1) & 1);
         const int ent0 = (g >> 6) * 16 * 8 + ((g >> 4) & 3);
@@ -407,9 +412,16 @@ hipError_t bin_launch(const uint32_t* bits, int64_t R, int64_t Wn, int64_t Lk, c
   const int64_t chunk_steps = steps < kStepsPerChunk ? steps : kStepsPerChunk;
   const int64_t per_wave = (chunk_steps + ns - 1) / ns;
   const dim3 grid((unsigned)blocks, (unsigned)B), block((unsigned)(64 * ns));
-#define QG_BIN_LAUNCH(SPW_)                                                                          \
-  hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT, SPW_>), grid, block, 0, s, bits, (int)R, (int)Wn, (int)Lk, \
-                     vin, vscale, oscale, out, y_bf16, in_bstride, out_bstride, vec_ok, s2o, nparts)
+  const bool full_ok = MODE != 2 && vec_ok && Lk % 512 == 0 && steps % chunk_steps == 0;
+#define QG_BIN_LAUNCH(SPW_)                                                                                  \
+  do {                                                                                                       \
+    if (full_ok && chunk_steps == (SPW_) * ns)                                                               \
+      hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT, SPW_, MODE != 2>), grid, block, 0, s, bits, (int)R, (int)Wn, \
+                         (int)Lk, vin, vscale, oscale, out, y_bf16, in_bstride, out_bstride, vec_ok, s2o, nparts); \
+    else                                                                                                     \
+      hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT, SPW_, false>), grid, block, 0, s, bits, (int)R, (int)Wn, \
+                         (int)Lk, vin, vscale, oscale, out, y_bf16, in_bstride, out_bstride, vec_ok, s2o, nparts); \
+  } while (0)
   if (per_wave <= 1) {
     QG_BIN_LAUNCH(1);
   } else if (per_wave <= 2 || kMaxPW == 2) {
