@@ -73,9 +73,10 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
     void* __restrict__ out, int y_bf16, int64_t in_bstride, int64_t out_bstride, int vec_ok,
     Stage2Out s2o, int nparts) {
   // SPW: max K-steps per wave and chunk (a power of two, SPW RT <= 8).
-  // FULL (stage 1): every chunk has SPW steps per wave, the rows are 16-byte
-  // aligned and K is a multiple of 512, so every group of 8 entries takes the
-  // fast path and lies inside its chunk: no selects, no element-wise path.
+  // FULL: every chunk has exactly SPW steps per wave (so every slot and
+  // table entry is in use), and in stage 1 the rows are 16-byte aligned and K
+  // is a multiple of 512, so every group of 8 entries takes the fast path and
+  // lies inside its chunk: no range tests, selects or element-wise path.
   static_assert(SPW * RT <= 8, "sign words held per wave");
   __shared__ u32x4_t tab[kStepsPerChunk * 16 * 2 * 4];   // 32 KB
   __shared__ float red[kMaxNS][RT * 16];
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
       const uint32_t soff = (uint32_t)(c0 + wave + i * NS) * 64u;   // 16 words per step
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        const uint32_t off = i < my ? voff[t] + soff : 0xFFFFFF00u;
+        const uint32_t off = (FULL || i < my) ? voff[t] + soff : 0xFFFFFF00u;
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, kNT);
         w[i][t] = u32x4_t{v[0], v[1], v[2], v[3]};
       }
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
 #pragma unroll
       for (int q = 0; q < CP; ++q) {
         const int i = threadIdx.x + q * blockDim.x;
-        if (i < ncopy) tab[i] = pre[q];
+        if (FULL || i < ncopy) tab[i] = pre[q];
       }
     } else {
       // build the chunk from x and s2: group g of 8 consecutive entries
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
     const int n1 = r16 & 1;
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      if (i < my) {
+      if (FULL || i < my) {
         const int sl = wave + i * NS;                 // step within the chunk
         u32x4_t w7[RT], w14[RT];
 #pragma unroll
@@ -412,11 +413,14 @@ hipError_t bin_launch(const uint32_t* bits, int64_t R, int64_t Wn, int64_t Lk, c
   const int64_t chunk_steps = steps < kStepsPerChunk ? steps : kStepsPerChunk;
   const int64_t per_wave = (chunk_steps + ns - 1) / ns;
   const dim3 grid((unsigned)blocks, (unsigned)B), block((unsigned)(64 * ns));
-  const bool full_ok = MODE != 2 && vec_ok && Lk % 512 == 0 && steps % chunk_steps == 0;
+  const bool full_ok = (MODE == 2 || (vec_ok && Lk % 512 == 0)) && steps % chunk_steps == 0;
+  // (the FULL stage-2 kernel with one row tile and 4 steps per wave would
+  // spill registers: that shape keeps the general kernel)
 #define QG_BIN_LAUNCH(SPW_)                                                                                  \
   do {                                                                                                       \
+    constexpr bool kFull = !(MODE == 2 && RT == 1 && (SPW_) == 4);                                           \
     if (full_ok && chunk_steps == (SPW_) * ns)                                                               \
-      hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT, SPW_, MODE != 2>), grid, block, 0, s, bits, (int)R, (int)Wn, \
+      hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT, SPW_, kFull>), grid, block, 0, s, bits, (int)R, (int)Wn,     \
                          (int)Lk, vin, vscale, oscale, out, y_bf16, in_bstride, out_bstride, vec_ok, s2o, nparts); \
     else                                                                                                     \
       hipLaunchKernelGGL((bin_mfma_kernel<MODE, RT, SPW_, false>), grid, block, 0, s, bits, (int)R, (int)Wn, \
