@@ -64,7 +64,7 @@ def test_integer_case_exact(gpu):
 
 
 @pytest.mark.parametrize("N,K,r", [(257, 1000, 300), (64, 8192, 2048), (33, 96, 129), (40, 20000, 9000),
-                                   (16421, 300, 129), (16400, 96, 1100)])
+                                   (16421, 300, 129), (16400, 96, 1100), (48, 1024, 8200)])
 @pytest.mark.parametrize("xkind", ["bf16", "f32"])
 def test_random_within_bound(gpu, N, K, r, xkind):
     say(f"binlr N={N} K={K} r={r} {xkind}")
