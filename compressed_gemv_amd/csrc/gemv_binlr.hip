@@ -124,7 +124,8 @@ __global__ __launch_bounds__(1024) void bin_mfma_kernel(
     // Unconditional buffer loads (reads past the range return 0), so no load
     // sits in a divergent branch; the fast path's tail test is applied where
     // the values are used.  With unaligned rows the range is empty and the
-    // scalar path below reads the entries.
+    // scalar path below reads the entries.  xrs covers this batch row of x
+    // (stage 1) or this chunk of the stage-2 table (stage 2); srs covers s2.
     constexpr uint32_t esz = MODE == 0 ? 2u : 4u;
     const __amdgpu_buffer_rsrc_t xrs =
         make_rsrc(MODE == 2 ? static_cast<const void*>(s2o.tab + s2o.tab_bstride * b + c0 * 1024)
