@@ -102,10 +102,13 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   uint32_t ka[RPW][UI], kb[RPW][UI];         // book id of each unit (CB)
   uint32_t sva[RPW], svb[RPW];               // side value of each row (OUT)
   // Weight loads go through buffer resources (row offset in soffset, the
-  // lane's unit offset in voffset).  A lane without a unit reads whatever
-  // lies at its offset (or 0 past the end): its activation pairs are zero.
-  // Rows past N read 0 and are never stored.  No branches around loads, so
-  // the next stage stays in flight while the current one is decoded.
+  // lane's unit offset in voffset).  The hardware range check covers the
+  // voffset only, so every load is kept inside its buffer by construction:
+  // a row past N (the tail of the last stage) is loaded as row N - 1 and
+  // never stored, and a lane without a unit (unit index past K/32) loads
+  // its row's first unit, which meets zero activation pairs.  No branches
+  // around loads, so the next stage stays in flight while the current one
+  // is decoded.
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(bk.ids, CB ? (uint32_t)((size_t)N * GN) : 0u);
@@ -139,7 +142,8 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
   uint32_t cvoff[UI], mvoff[UI];
 #pragma unroll
   for (int it = 0; it < UI; ++it) {
-    const int u = sl * USL + it * 64 + lane;
+    const int u0 = sl * USL + it * 64 + lane;
+    const int u = u0 < U ? u0 : 0;
     cvoff[it] = (uint32_t)u * (BITS * 4);
     mvoff[it] = (uint32_t)((u * 32) / G) * 4;
   }
@@ -150,7 +154,8 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
                   uint32_t (&kk)[RPW][UI], int row0) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      const uint32_t row = (uint32_t)(row0 + r * nstreams);
+      // wave-uniform; rows past N load row N - 1 (never stored)
+      const uint32_t row = (uint32_t)min(row0 + r * nstreams, N - 1);
       if constexpr (MULTI) {
         const int mi = seg_of(row);
         const uint32_t lr = row - (uint32_t)segs.start[mi];

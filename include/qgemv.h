@@ -107,9 +107,11 @@ int qunpack_group(const void* codes, const void* meta, int64_t N, int64_t K,
  * ("AirLLM corre un modelo 70B...", "Por qué es lento": a decode step moves
  * every weight byte once, so it is bound by the bytes read).
  * x: [B][K], x_dtype Q_BF16 or Q_F32; y: [B][N], y_dtype Q_F32 or Q_BF16;
- * accumulation in fp32.  1 <= B <= 16.  codes/meta 16-byte aligned, x and y
- * 4-byte aligned (x bf16: 2-byte aligned when K is odd is not possible since
- * K % 32 == 0).  Asynchronous on `stream`. */
+ * accumulation in fp32.  1 <= B <= 16.  codes, meta and x must be 16-byte
+ * aligned (the activations are read with 16-byte loads), y 4-byte aligned;
+ * Q_EALIGN otherwise.  Batch 1 supports K <= 65536 (bf16 x) or 32768 (fp32
+ * x); B > 1 takes bf16 x only (Q_EUNSUPPORTED otherwise).  Asynchronous on
+ * `stream`. */
 int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K,
                 int bits, int group, const void* x, int x_dtype, int64_t B,
                 void* y, int y_dtype, hipStream_t stream);
@@ -118,8 +120,9 @@ int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K,
  * (a decoder layer's q, k, v or its gate and up projections), multiplied in
  * one launch for B = 1 (one launch per matrix for B > 1): y_i = x W_i^T for
  * each entry of mats (a HOST array of 1..4 entries; each codes/meta/y as in
- * qgemv_group, y_i [B][N_i]).  Same limits and dtypes as qgemv_group; the
- * sum of the N_i is below 2^31.  Asynchronous. */
+ * qgemv_group, y_i [B][N_i]).  Same limits, dtypes and alignment as
+ * qgemv_group (x 16-byte aligned); the sum of the N_i is below 2^31.
+ * Asynchronous. */
 typedef struct qgroup_mat {
   const void* codes;
   const void* meta;
@@ -155,8 +158,9 @@ int qpack_group_outlier(const float* W, int64_t N, int64_t K, int bits, int grou
                         size_t ws_bytes, hipStream_t stream);
 
 /* qgemv_group plus the outlier term: y[b][n] = sum_k (s*q + o) x[b][k] +
- * sum_j side[n][j] x[b][idx[j]], fp32 accumulation; same arguments and
- * limits as qgemv_group (n_out = 0 is qgemv_group).  Asynchronous. */
+ * sum_j side[n][j] x[b][idx[j]], fp32 accumulation; same arguments, limits
+ * and alignment as qgemv_group (x 16-byte aligned; side 2-byte and idx
+ * 4-byte aligned; n_out = 0 is qgemv_group).  Asynchronous. */
 int qgemv_group_outlier(const void* codes, const void* meta, const uint16_t* side, const int32_t* idx,
                         int64_t n_out, int64_t N, int64_t K, int bits, int group, const void* x,
                         int x_dtype, int64_t B, void* y, int y_dtype, hipStream_t stream);
@@ -189,9 +193,9 @@ int qcodebook_default(int bits, uint8_t* books, int* n_books);
 int qpack_group_cb(const float* W, int64_t N, int64_t K, int bits, int group, const uint8_t* books,
                    int n_books, void* codes, void* meta, uint8_t* book_ids, hipStream_t stream);
 /* Decode GEMV y[b][n] = sum_k (s * e[book][q] / 2^(7-bits) + o) x[b][k],
- * fp32 accumulation; same arguments, limits and dtypes as qgemv_group plus
- * book_ids and books (device, entries <= 127 as qpack_group_cb checks).
- * Asynchronous. */
+ * fp32 accumulation; same arguments, limits, dtypes and alignment as
+ * qgemv_group (x 16-byte aligned) plus book_ids and books (device, entries
+ * <= 127 as qpack_group_cb checks).  Asynchronous. */
 int qgemv_group_cb(const void* codes, const void* meta, const uint8_t* book_ids, const uint8_t* books,
                    int n_books, int64_t N, int64_t K, int bits, int group, const void* x, int x_dtype,
                    int64_t B, void* y, int y_dtype, hipStream_t stream);

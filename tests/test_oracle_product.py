@@ -104,6 +104,28 @@ def test_sizes_against_page_figures():
     assert round(a / b) == ratio
 
 
+def test_layer_set_bytes():
+    """A layer's compressed bytes: with one width and group for all seven
+    matrices it is the layer's parameter count times b + 32/g bits; mixed
+    widths split the count into the attention and MLP parts; 80 layers at
+    4.5 bits (4-bit codes, groups of 64) plus 4.5-bit embeddings reproduce
+    the page's ~40 GB for a dense 70B at about 4.5 bpw."""
+    gold = json.load(open(GOLDEN))
+    per_layer, total = _llama70b_params()
+    uni = sizes.layer_set_bytes(LAYER_SHAPES, lambda n: 4, lambda n: 64)
+    assert uni * 8 == per_layer * 4.5
+    assert uni == 481_296_384
+    attn = sum(K * N for n, (K, N) in LAYER_SHAPES.items() if n in ("q", "k", "v", "o"))
+    mlp = per_layer - attn
+    hi = sizes.layer_set_bytes(LAYER_SHAPES, lambda n: 6 if n in ("q", "k", "v", "o") else 3, lambda n: 32)
+    assert hi * 8 == attn * (6 + 1) + mlp * (3 + 1)
+    lo = sizes.layer_set_bytes(LAYER_SHAPES, lambda n: 5 if n in ("q", "k", "v", "o") else 2, lambda n: 32)
+    assert lo * 8 == attn * (5 + 1) + mlp * (2 + 1)
+    g = gold["q4km_70b_GB"]
+    model = (80 * uni + (total - 80 * per_layer) * sizes.group_bpw(4, 64) / 8) / 1e9
+    assert abs(model - g["value"]) <= g["rel_tol"] * g["value"], model
+
+
 def test_sizes_formulas():
     assert sizes.group_bytes(28672, 8192, 4, 64) == 132_120_576
     assert sizes.group_bytes(512, 512, 4, 32) == 163_840
