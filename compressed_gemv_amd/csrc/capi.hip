@@ -518,7 +518,7 @@ int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes) {
   if (w->format == Q_FMT_BINLR) {
     const int st = qbinlr_sizes(w->N, w->K, w->r, 1, nullptr, nullptr, nullptr);
     if (st != Q_OK) return st;
-    *ws_bytes = (size_t)(M * padded_words(w->r) * 32 * 2);
+    *ws_bytes = (size_t)qg::gemm_binlr_ws_bytes(M, w->K, w->r);
     return Q_OK;
   }
   return Q_EINVAL;
@@ -560,8 +560,7 @@ int qgemm_prefill(const qweight* w, const void* X, int x_dtype, int64_t M, void*
   if (!aligned(ws, 16) || !aligned(w->ubits, 4) || !aligned(w->vtbits, 4)) return Q_EALIGN;
   return hip_status(qg::launch_gemm_binlr(
       static_cast<const uint32_t*>(w->ubits), static_cast<const uint32_t*>(w->vtbits), w->s1,
-      w->s2, w->N, w->K, w->r, static_cast<const uint16_t*>(X), M, Y, y_dtype,
-      static_cast<uint16_t*>(ws), stream));
+      w->s2, w->N, w->K, w->r, static_cast<const uint16_t*>(X), M, Y, y_dtype, ws, stream));
 }
 
 }  // extern "C"

@@ -11,6 +11,8 @@ static hipError_t gemm_group_cb_t(const uint32_t* codes, const uint32_t* meta, c
                                   const uint8_t* books, int nb, int64_t N, int64_t K, const uint16_t* X,
                                   int64_t M, void* Y, int y_bf16, hipStream_t s) {
   DecCB<BITS, G> dec{codes, meta, ids, books, nb, (int)N, (int)(K / 32), nullptr, CbConst{}};
+  if (K < kSplitBelowK)
+    return gemm_run<DecCB<BITS, G>, 0, false, false, true>(X, K, M, K, dec, N, nullptr, nullptr, Y, N, y_bf16, s);
   return gemm_run<DecCB<BITS, G>, 0, false>(X, K, M, K, dec, N, nullptr, nullptr, Y, N, y_bf16, s);
 }
 

@@ -12,6 +12,8 @@ static hipError_t gemm_group_outl_t(const uint32_t* codes, const uint32_t* meta,
                                     const uint16_t* X, int64_t M, void* Y, int y_bf16, hipStream_t s,
                                     SideCols sc) {
   DecRTN<BITS, G> dec{codes, meta, (int)N, (int)(K / 32)};
+  if (K < kSplitBelowK)
+    return gemm_run<DecRTN<BITS, G>, 0, false, true, true>(X, K, M, K, dec, N, nullptr, nullptr, Y, N, y_bf16, s, sc);
   return gemm_run<DecRTN<BITS, G>, 0, false, true>(X, K, M, K, dec, N, nullptr, nullptr, Y, N, y_bf16, s, sc);
 }
 

@@ -23,6 +23,10 @@
 //     in that XCD's L2.
 // The binary format runs two passes ("70B en 4GB de VRAM...", section 1):
 // T = bf16((X (.) s2) V) into the workspace, then Y = (T U^T) (.) s1.
+// Short reductions (K < 512) take a split-precision variant in which the
+// operand that is not exact in bf16 enters as bf16 hi + lo (weights; X s2 and
+// an fp32 T for the binary passes), so every output meets the same error
+// bound as the long ones.
 #pragma once
 
 #include "codebook.hpp"
@@ -50,7 +54,9 @@ struct DecRTN {
     buf_load_unit<BITS, 0>(crs, co, 0u, r.w);
     r.m = __builtin_amdgcn_raw_buffer_load_b32(mrs, mo, 0u, 0);
   }
-  __device__ __forceinline__ void decode(const Raw& r, uint32_t (&outp)[16]) const {
+  static constexpr bool kExact = false;    // w_hat needs more bits than bf16
+  // the 32 weights fl32(s q + o) (exact) in k order
+  __device__ __forceinline__ void decode_f32(const Raw& r, float (&wv)[32]) const {
     using UN = UnitH<BITS>;
     uint32_t pr[16];
     decode_unit_h<BITS>(r.w, pr);
@@ -58,7 +64,6 @@ struct DecRTN {
     float sp[UN::NCLS];
 #pragma unroll
     for (int c = 0; c < UN::NCLS; ++c) sp[c] = s * (float)(1 << (24 - BITS * c));
-    float wv[32];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const PairInfo pi = UN::pair(k);
@@ -66,6 +71,10 @@ struct DecRTN {
       wv[pi.ca] = __builtin_fmaf(f16_lo(pr[k]), sp[c], o);
       wv[pi.cb] = __builtin_fmaf(f16_hi(pr[k]), sp[c], o);
     }
+  }
+  __device__ __forceinline__ void decode(const Raw& r, uint32_t (&outp)[16]) const {
+    float wv[32];
+    decode_f32(r, wv);
 #pragma unroll
     for (int i = 0; i < 16; ++i) outp[i] = cvt_pk_bf16(wv[2 * i], wv[2 * i + 1]);
   }
@@ -73,6 +82,7 @@ struct DecRTN {
 
 struct DecBIN {
   static constexpr int kDictWords = 0;
+  static constexpr bool kExact = true;     // +-1 is exact in bf16
   const uint32_t* bits; int N; int Wn;   // rows, words per stored row
   struct Raw { uint32_t w; };
   __device__ __forceinline__ void load(int n, int u, Raw& r) const {
@@ -123,7 +133,9 @@ struct DecCB {
     r.m = __builtin_amdgcn_raw_buffer_load_b32(mrs, go * 4, 0u, 0);
     r.k = __builtin_amdgcn_raw_buffer_load_b8(krs, go, 0u, 0);
   }
-  __device__ __forceinline__ void decode(const Raw& r, uint32_t (&outp)[16]) const {
+  static constexpr bool kExact = false;
+  // the 32 weights fl32(s e[q] 2^(BITS-7) + o) (exact) in k order
+  __device__ __forceinline__ void decode_f32(const Raw& r, float (&wv)[32]) const {
     uint32_t T[4] = {0u, 0u, 0u, 0u};
     const uint32_t* tp = lds_dict + ((r.k & 15u) << BITS) / 4;   // ids < 16 (packer)
 #pragma unroll
@@ -132,13 +144,16 @@ struct DecCB {
     decode_unit_cb<BITS>(r.w, T, pr, kc);
     const float s = f16_bits_to_f32(r.m & 0xFFFFu) * (1.0f / (float)(1 << (7 - BITS)));
     const float o = f16_bits_to_f32(r.m >> 16);
-    float wv[32];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const PairInfo pi = Unit<BITS>::pair(k);
       wv[pi.ca] = __builtin_fmaf(bf16_lo_to_f32(pr[k]) - 128.0f, s, o);
       wv[pi.cb] = __builtin_fmaf(bf16_hi_to_f32(pr[k]) - 128.0f, s, o);
     }
+  }
+  __device__ __forceinline__ void decode(const Raw& r, uint32_t (&outp)[16]) const {
+    float wv[32];
+    decode_f32(r, wv);
 #pragma unroll
     for (int i = 0; i < 16; ++i) outp[i] = cvt_pk_bf16(wv[2 * i], wv[2 * i + 1]);
   }
@@ -156,26 +171,44 @@ struct TileSmall { static constexpr int TM = 128, TN = 256, TK = 64, WM = 2, WN 
 #define QG_BIG_VPM 3
 #endif
 struct TileBig   { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 2, WN = 2, VPM = QG_BIG_VPM; };   // 4 waves, 128 x 128
+// Split precision (short reductions): one operand is carried as bf16 hi + lo
+// tiles, so the LDS holds three tiles per buffer; a smaller block keeps them
+// within the LDS.
+struct TileSplit { static constexpr int TM = 64, TN = 128, TK = 64, WM = 2, WN = 2, VPM = 6; };      // 4 waves, 32 x 64
 
-// AMODE 0: A = X (bf16).  AMODE 1: A = bf16(X * s2[k]).  KMASK: Kact % 8 != 0.
+// AMODE 0: A = X (bf16).  AMODE 1: A = X * s2[k] (fp32, exact), rounded to
+// bf16.  AMODE 2: A fp32 (the binary path's T in split precision; SPLIT
+// only).  KMASK: Kact % 8 != 0.
 // oscale: per-column fp16 scale or null.  nbn: tiles along N.
 // OUTL: outlier side columns (fp16 side[N][n_out] at input channels oidx[],
 // 1 <= n_out <= TK) enter as one more K-step after the main loop, with A =
-// X[m][oidx_j] and B = bf16(side[n][j]) (zero past n_out): the same bf16
-// weight tiles as every other step.
-template <typename Dec, int AMODE, bool KMASK, typename Cfg, bool OUTL>
+// X[m][oidx_j] and B = side[n][j] (zero past n_out), rounded as the weight
+// tiles of every other step.
+// SPLIT: the inexact operand enters the matrix cores as bf16 hi + lo =
+// bf16(v - hi) (2^-16 relative residual), two MFMAs per fragment pair:
+// the fp32 A of AMODE 1 and 2, or, with AMODE 0, decoded weights that are
+// not exact in bf16.  Used for short reductions, where one bf16 rounding of
+// an operand (up to 2^-8 of sum |w||x|) could exceed the error budget.
+template <typename Dec, int AMODE, bool KMASK, typename Cfg, bool OUTL, bool SPLIT>
 __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, int M, int Kact, Dec dec, int N,
+    const void* __restrict__ A, int64_t lda, int M, int Kact, Dec dec, int N,
     const uint16_t* __restrict__ kscale, const uint16_t* __restrict__ oscale,
     void* __restrict__ Y, int64_t ldy, int y_bf16, int nbn,
     const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out) {
+  static_assert(AMODE != 2 || SPLIT, "fp32 A comes with split precision");
+  constexpr bool SPA = SPLIT && AMODE != 0;                  // A as hi + lo
+  constexpr bool SPB = SPLIT && AMODE == 0 && !Dec::kExact;  // weights as hi + lo
+  constexpr int ESZ = AMODE == 2 ? 4 : 2;                    // bytes per A element
   constexpr int TM = Cfg::TM, TN = Cfg::TN, TK = Cfg::TK, LP = TK + 8, UPR = TK / 32;
   constexpr int NT = 64 * Cfg::WM * Cfg::WN;         // threads
   constexpr int FI = TM / Cfg::WM / 32, FJ = TN / Cfg::WN / 32;   // 32x32 tiles per wave
-  constexpr int AC = TM * (TK / 8) / NT;              // 16-byte X chunks per thread and step
+  constexpr int AC = TM * (TK / 8) / NT;              // 8-element X chunks per thread and step
   constexpr int WU = TN * UPR / NT;                   // weight units per thread and step
   static_assert(AC >= 1 && WU >= 1 && NT % (TK / 8) == 0, "tile configuration");
-  __shared__ __align__(16) uint16_t lds[2][(TM + TN) * LP];
+  // per LDS buffer: A tile [, A lo tile], B tile [, B lo tile]
+  constexpr int AOFF_LO = TM * LP, BOFF = (SPA ? 2 : 1) * TM * LP, BOFF_LO = BOFF + TN * LP;
+  constexpr int BUF = BOFF + (SPB ? 2 : 1) * TN * LP;
+  __shared__ __align__(16) uint16_t lds[2][BUF];
   __shared__ __align__(16) uint32_t dict_lds[Dec::kDictWords > 0 ? Dec::kDictWords : 1];
   const int tid = threadIdx.x;
   if constexpr (Dec::kDictWords > 0) dec.bind(dict_lds, tid, NT);   // staged before the first decode
@@ -194,23 +227,29 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   constexpr int AROWS = NT / (TK / 8);                // X rows covered per chunk round
-  const int ar = tid / (TK / 8), ac = (tid % (TK / 8)) * 8;   // X: rows ar + AROWS i, 8 bf16 at ac
+  const int ar = tid / (TK / 8), ac = (tid % (TK / 8)) * 8;   // X: rows ar + AROWS i, 8 elements at ac
   const int nsteps = (Kact + TK - 1) / TK;
   // Branch-free loads through buffer resources based at this tile's first
   // row: rows past M are out of range and read 0, a chunk at or past Kact
   // gets an out-of-range offset.  (A chunk straddling Kact occurs only when
   // Kact % 8 != 0; KMASK then zeroes its tail after the load.)
   const int mrows = min(TM, M - m0);
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + (size_t)m0 * lda, (uint32_t)((size_t)mrows * lda * 2));
+  const __amdgpu_buffer_rsrc_t ars =
+      make_rsrc(static_cast<const char*>(A) + (size_t)m0 * lda * ESZ, (uint32_t)((size_t)mrows * lda * ESZ));
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(kscale, (uint32_t)(AMODE == 1 ? (size_t)Kact * 2 : 0));
-  struct Stage { u32x4_t a[AC]; u32x4_t sc; typename Dec::Raw w[WU]; };
+  // a: 8 bf16 (AMODE 0, 1) or the first 4 of 8 fp32 (AMODE 2, a2 the rest)
+  struct Stage { u32x4_t a[AC]; u32x4_t a2[AMODE == 2 ? AC : 1]; u32x4_t sc; typename Dec::Raw w[WU]; };
   auto gload = [&](int step, Stage& st) {
     const int k = step * TK + ac;
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
-      const uint32_t off = k < Kact ? (uint32_t)(((size_t)(ar + AROWS * i) * lda + k) * 2) : 0xFFFFFFF0u;
+      const uint32_t off = k < Kact ? (uint32_t)(((size_t)(ar + AROWS * i) * lda + k) * ESZ) : 0xFFFFFFE0u;
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0);
       st.a[i] = u32x4_t{v[0], v[1], v[2], v[3]};
+      if constexpr (AMODE == 2) {
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b128(ars, off + 16u, 0, 0);
+        st.a2[i] = u32x4_t{v2[0], v2[1], v2[2], v2[3]};
+      }
     }
     if constexpr (AMODE == 1) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(srs, k < Kact ? (uint32_t)k * 2 : 0xFFFFFFF0u, 0, 0);
@@ -225,54 +264,104 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   // scale (AMODE 1), decode and store one K-step into an LDS buffer
   auto lstore = [&](int step, Stage& st, int buf) {
     uint16_t* As = lds[buf];
-    uint16_t* Bs = lds[buf] + TM * LP;
+    uint16_t* Bs = lds[buf] + BOFF;
     if constexpr (KMASK) {
       const int k = step * TK + ac;
+      if constexpr (AMODE == 2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t keep = (k + 2 * e + 1 < Kact) ? 0xFFFFFFFFu : ((k + 2 * e < Kact) ? 0x0000FFFFu : 0u);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t k0 = (k + e < Kact) ? 0xFFFFFFFFu : 0u, k1 = (k + 4 + e < Kact) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int i = 0; i < AC; ++i) st.a[i][e] &= keep;
+          for (int i = 0; i < AC; ++i) { st.a[i][e] &= k0; st.a2[i][e] &= k1; }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t keep = (k + 2 * e + 1 < Kact) ? 0xFFFFFFFFu : ((k + 2 * e < Kact) ? 0x0000FFFFu : 0u);
+#pragma unroll
+          for (int i = 0; i < AC; ++i) st.a[i][e] &= keep;
+        }
       }
     }
-    if constexpr (AMODE == 1) {
-      // A = bf16(X * s2[k]), re-rounded to nearest even
+    if constexpr (AMODE == 0) {
 #pragma unroll
       for (int i = 0; i < AC; ++i)
+        *reinterpret_cast<u32x4_t*>(As + (ar + AROWS * i) * LP + ac) = st.a[i];
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          st.a[i][e] = cvt_pk_bf16(bf16_lo_to_f32(st.a[i][e]) * f16_bits_to_f32(st.sc[e] & 0xFFFFu),
-                                   bf16_hi_to_f32(st.a[i][e]) * f16_bits_to_f32(st.sc[e] >> 16));
+      for (int i = 0; i < AC; ++i) {
+        // the 8 fp32 values of the chunk: X * s2 (exact: 8 x 11 significant
+        // bits) or T; hi = bf16 (nearest even), lo = bf16(v - hi)
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (AMODE == 1) {
+            v[2 * e] = bf16_lo_to_f32(st.a[i][e]) * f16_bits_to_f32(st.sc[e] & 0xFFFFu);
+            v[2 * e + 1] = bf16_hi_to_f32(st.a[i][e]) * f16_bits_to_f32(st.sc[e] >> 16);
+          } else {
+            v[e] = __uint_as_float(st.a[i][e]);
+            v[4 + e] = __uint_as_float(st.a2[i][e]);
+          }
+        }
+        u32x4_t hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = cvt_pk_bf16(v[2 * e], v[2 * e + 1]);
+          if constexpr (SPA) lo[e] = cvt_pk_bf16(v[2 * e] - bf16_lo_to_f32(hi[e]), v[2 * e + 1] - bf16_hi_to_f32(hi[e]));
+        }
+        *reinterpret_cast<u32x4_t*>(As + (ar + AROWS * i) * LP + ac) = hi;
+        if constexpr (SPA) *reinterpret_cast<u32x4_t*>(As + AOFF_LO + (ar + AROWS * i) * LP + ac) = lo;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < AC; ++i)
-      *reinterpret_cast<u32x4_t*>(As + (ar + AROWS * i) * LP + ac) = st.a[i];
 #pragma unroll
     for (int j = 0; j < WU; ++j) {
       const int idx = tid + NT * j;
-      uint32_t v[16];
-      dec.decode(st.w[j], v);
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(Bs + (idx / UPR) * LP + (idx % UPR) * 32);
+      if constexpr (SPB) {
+        float wv[32];
+        dec.decode_f32(st.w[j], wv);
+        u32x4_t* dlo = reinterpret_cast<u32x4_t*>(lds[buf] + BOFF_LO + (idx / UPR) * LP + (idx % UPR) * 32);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+        for (int i = 0; i < 4; ++i) {
+          u32x4_t hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float w0 = wv[8 * i + 2 * e], w1 = wv[8 * i + 2 * e + 1];
+            hi[e] = cvt_pk_bf16(w0, w1);
+            lo[e] = cvt_pk_bf16(w0 - bf16_lo_to_f32(hi[e]), w1 - bf16_hi_to_f32(hi[e]));
+          }
+          dst[i] = hi;
+          dlo[i] = lo;
+        }
+      } else {
+        uint32_t v[16];
+        dec.decode(st.w[j], v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+      }
     }
   };
   // v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 and k = 8 (l / 32) .. +7
   // of each 32 x 16 operand; it sustains near-peak rate with few chains.
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   constexpr int WTM = TM / Cfg::WM, WTN = TN / Cfg::WN;
+  constexpr int NA = SPA ? 2 : 1, NB = SPB ? 2 : 1;   // A and B tiles (hi [, lo])
   auto mfma_step = [&](int buf) {
     const uint16_t* As = lds[buf];
-    const uint16_t* Bs = lds[buf] + TM * LP;
+    const uint16_t* Bs = lds[buf] + BOFF;
     // fragments of k-slice s+1 are read before the MFMAs of slice s
-    bf16x8_t af[2][FI], bfr[2][FJ];
-    auto rd = [&](int kk, bf16x8_t (&a)[FI], bf16x8_t (&b)[FJ]) {
+    bf16x8_t af[2][NA][FI], bfr[2][NB][FJ];
+    auto rd = [&](int kk, bf16x8_t (&a)[NA][FI], bf16x8_t (&b)[NB][FJ]) {
 #pragma unroll
-      for (int i = 0; i < FI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WTM + i * 32 + fr) * LP + kk + fk);
+      for (int h = 0; h < NA; ++h)
 #pragma unroll
-      for (int j = 0; j < FJ; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WTN + j * 32 + fr) * LP + kk + fk);
+        for (int i = 0; i < FI; ++i)
+          a[h][i] = *reinterpret_cast<const bf16x8_t*>(As + h * AOFF_LO + (wm * WTM + i * 32 + fr) * LP + kk + fk);
+#pragma unroll
+      for (int h = 0; h < NB; ++h)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          b[h][j] = *reinterpret_cast<const bf16x8_t*>(Bs + h * TN * LP + (wn * WTN + j * 32 + fr) * LP + kk + fk);
     };
     rd(0, af[0], bfr[0]);
 #pragma unroll
@@ -281,8 +370,15 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
 #pragma unroll
       for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < FJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FJ; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0][i], bfr[ks & 1][0][j], acc[i][j], 0, 0, 0);
+          if constexpr (SPA)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][NA - 1][i], bfr[ks & 1][0][j], acc[i][j], 0,
+                                                                0, 0);
+          if constexpr (SPB)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0][i], bfr[ks & 1][NB - 1][j], acc[i][j], 0,
+                                                                0, 0);
+        }
     }
   };
   // one half-iteration, a single basic block: issue the raw loads of step
@@ -295,7 +391,7 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
     mfma_step(cur);
     lstore(step + 1, st, cur ^ 1);
 #pragma unroll
-    for (int i = 0; i < FI * FJ * (TK / 16); ++i) {
+    for (int i = 0; i < FI * FJ * (TK / 16) * (SPLIT ? 2 : 1); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, Cfg::VPM, 0);   // VALU
     }
@@ -317,19 +413,23 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   }
   if constexpr (OUTL) {
     // the outlier K-step; the main loop is done with LDS (its last step
-    // ended at a barrier)
+    // ended at a barrier).  X is bf16 here (AMODE 0).
+    static_assert(AMODE == 0, "outlier columns come with the group format");
+    const uint16_t* X = static_cast<const uint16_t*>(A);
     uint16_t* As = lds[0];
-    uint16_t* Bs = lds[0] + TM * LP;
+    uint16_t* Bs = lds[0] + BOFF;
     for (int t = tid; t < TM * TK; t += NT) {
       const int r = t / TK, c = t % TK, m = m0 + r;
-      As[r * LP + c] = (c < n_out && m < M) ? A[(size_t)m * lda + oidx[c]] : (uint16_t)0;
+      As[r * LP + c] = (c < n_out && m < M) ? X[(size_t)m * lda + oidx[c]] : (uint16_t)0;
     }
     for (int t = tid; t < TN * TK; t += NT) {
       const int r = t / TK, c = t % TK, n = n0 + r;
-      As[TM * LP + r * LP + c] = (c < n_out && n < N)
-          ? (uint16_t)f32_to_bf16_rne(f16_bits_to_f32(side[(size_t)n * n_out + c])) : (uint16_t)0;
+      const float sv = (c < n_out && n < N) ? f16_bits_to_f32(side[(size_t)n * n_out + c]) : 0.f;
+      const uint32_t hi = f32_to_bf16_rne(sv);
+      Bs[r * LP + c] = (uint16_t)hi;
+      // fp16 -> bf16 hi keeps 8 of 11 significant bits; lo holds the rest exactly
+      if constexpr (SPB) Bs[TN * LP + r * LP + c] = (uint16_t)f32_to_bf16_rne(sv - bf16_bits_to_f32(hi));
     }
-    (void)Bs;
     __syncthreads();
     mfma_step(0);
   }
@@ -357,16 +457,23 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
 
 struct SideCols { const uint16_t* vals; const int32_t* idx; int n; };   // outlier columns (n = 0: none)
 
-template <typename Dec, int AMODE, bool KMASK, typename Cfg, bool OUTL = false>
-static hipError_t gemm_launch(const uint16_t* A, int64_t lda, int64_t M, int64_t Kact, Dec dec, int64_t N,
+template <typename Dec, int AMODE, bool KMASK, typename Cfg, bool OUTL = false, bool SPLIT = false>
+static hipError_t gemm_launch(const void* A, int64_t lda, int64_t M, int64_t Kact, Dec dec, int64_t N,
                               const uint16_t* kscale, const uint16_t* oscale, void* Y, int64_t ldy,
                               int y_bf16, hipStream_t s, SideCols sc) {
   const int nbn = (int)((N + Cfg::TN - 1) / Cfg::TN);
   const dim3 grid((unsigned)(((M + Cfg::TM - 1) / Cfg::TM) * nbn));
-  hipLaunchKernelGGL((gemm_kernel<Dec, AMODE, KMASK, Cfg, OUTL>), grid, dim3(64 * Cfg::WM * Cfg::WN), 0, s, A,
-                     lda, (int)M, (int)Kact, dec, (int)N, kscale, oscale, Y, ldy, y_bf16, nbn, sc.vals, sc.idx, sc.n);
+  hipLaunchKernelGGL((gemm_kernel<Dec, AMODE, KMASK, Cfg, OUTL, SPLIT>), grid, dim3(64 * Cfg::WM * Cfg::WN), 0, s,
+                     A, lda, (int)M, (int)Kact, dec, (int)N, kscale, oscale, Y, ldy, y_bf16, nbn, sc.vals, sc.idx,
+                     sc.n);
   return hipGetLastError();
 }
+
+// Reductions shorter than this take the split-precision kernel: with one
+// bf16 rounding of an operand, the error of an output is a sum of K terms
+// of up to 2^-8 |w||x| each that cancel like a random walk for long K
+// (~2^-8 / sqrt(3K) of sum |w||x|) but can reach 2^-8 for short ones.
+constexpr int64_t kSplitBelowK = 512;
 
 // Either tile runs one workgroup per CU, and a 256 x 256 tile takes about
 // 7/4 the time of a 128 x 256 one (fewer LDS reads and barriers per MFMA),
@@ -388,15 +495,20 @@ static bool use_big_tile(int64_t M, int64_t N) {
   return 7 * ((nbig + cus - 1) / cus) <= 4 * ((nsmall + cus - 1) / cus);
 }
 
-template <typename Dec, int AMODE, bool KMASK, bool OUTL = false>
-static hipError_t gemm_run(const uint16_t* A, int64_t lda, int64_t M, int64_t Kact, Dec dec, int64_t N,
+template <typename Dec, int AMODE, bool KMASK, bool OUTL = false, bool SPLIT = false>
+static hipError_t gemm_run(const void* A, int64_t lda, int64_t M, int64_t Kact, Dec dec, int64_t N,
                            const uint16_t* kscale, const uint16_t* oscale, void* Y, int64_t ldy,
                            int y_bf16, hipStream_t s, SideCols sc = SideCols{nullptr, nullptr, 0}) {
-  if (use_big_tile(M, N))
-    return gemm_launch<Dec, AMODE, KMASK, TileBig, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
-                                                         s, sc);
-  return gemm_launch<Dec, AMODE, KMASK, TileSmall, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
-                                                         s, sc);
+  if constexpr (SPLIT) {
+    return gemm_launch<Dec, AMODE, KMASK, TileSplit, OUTL, true>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy,
+                                                                 y_bf16, s, sc);
+  } else {
+    if (use_big_tile(M, N))
+      return gemm_launch<Dec, AMODE, KMASK, TileBig, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
+                                                           s, sc);
+    return gemm_launch<Dec, AMODE, KMASK, TileSmall, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
+                                                           s, sc);
+  }
 }
 
 }  // namespace qg

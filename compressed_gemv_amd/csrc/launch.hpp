@@ -88,6 +88,8 @@ hipError_t launch_gemm_group_outlier(const uint32_t* codes, const uint32_t* meta
 hipError_t launch_gemm_binlr(const uint32_t* ubits, const uint32_t* vtbits,
                              const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
                              int64_t r, const uint16_t* X, int64_t M, void* Y, int y_dtype,
-                             uint16_t* T_ws, hipStream_t s);
+                             void* T_ws, hipStream_t s);
+// Bytes of the binary prefill workspace (T) for M token rows.
+int64_t gemm_binlr_ws_bytes(int64_t M, int64_t K, int64_t r);
 
 }  // namespace qg

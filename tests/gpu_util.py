@@ -8,15 +8,11 @@ import torch
 import oracle
 
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+# The error bound of every fp32 output: max |y - y_ref| / sum |w_hat| |x|.
 TOL = 2e-3
-# Prefill feeds the matrix cores bf16 tiles (unit roundoff 2^-8).  RTN: each
-# weight is rounded once, so |y - y_ref| <= 2^-8 sum|w_hat||x| plus the fp32
-# accumulation; on the configs' reductions (K >= 512) the errors concentrate
-# near 1e-4, far inside 2e-3, but a short reduction can approach 2^-8.
-PREFILL_RTN_BOUND = 2.0 ** -8 + 2.0 ** -14
-# Binary prefill rounds s2*x and t = (s2*x) V to bf16: against the factored
-# magnitude |s1| r sum|s2 x| the error is <= 2 * 2^-8 (1 + 2^-8).
-PREFILL_BINLR_FACT_BOUND = 2.0 ** -7 * (1 + 2.0 ** -8) + 2.0 ** -14
+# bf16 has 8 significant bits: rounding to nearest even moves a value v by
+# at most 2^-8 |v| (unit roundoff), and by at most 2^-8 of the rounded value.
+BF16_U = 2.0 ** -8
 
 
 def say(msg):
@@ -50,4 +46,21 @@ def group_reference(W, bits, group):
 def check_err(y, y_ref, D, tol=TOL):
     err = oracle.product.normalized_error(y, y_ref, D)
     assert err <= tol, f"normalized error {err:.3e} > {tol}"
+    return err
+
+
+def check_bf16_out(y16, y32, y_ref, D):
+    """A bf16 output (y16) against the fp32 output of the same call (y32) and
+    the oracle: y16 must be y32 rounded to nearest even, bit for bit, and
+    |y16 - y_ref| <= 2e-3 D + 2^-8 |y16| element-wise (the bound of the fp32
+    result plus the output type's own rounding)."""
+    from workloads import f32_to_bf16_bits
+    y16 = np.asarray(y16, dtype=np.float64)
+    y32 = np.asarray(y32, dtype=np.float32)
+    want = oracle.product.bf16_to_f64(f32_to_bf16_bits(y32))
+    assert np.array_equal(y16, want), "bf16 output is not the fp32 result rounded to nearest even"
+    check_err(y32, y_ref, D)
+    excess = np.abs(y16 - y_ref) - BF16_U * np.abs(y16)
+    err = np.max(np.where(D > 0, excess / np.where(D > 0, D, 1.0), np.where(excess > 0, np.inf, 0.0)))
+    assert err <= TOL, f"bf16 output error beyond its rounding {err:.3e} > {TOL}"
     return err

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import DEV, TOL, check_err, dev, dev_bf16, group_reference, host, say
+from gpu_util import DEV, TOL, check_bf16_out, check_err, dev, dev_bf16, group_reference, host, say
 from workloads import (LAYER_SHAPES, config1_inputs, f32_to_bf16_bits, gen_weights, gen_x_bf16, gen_x_f32, layer_weights,
                        layer_x, rng_for)
 
@@ -170,10 +170,11 @@ def test_gemv_bf16_output(gpu):
     W = gen_weights(N, K, rng_for(55, 0), outliers=False)
     _, _, _, words, meta, W_hat = group_reference(W, 4, 64)
     xb = gen_x_bf16(1, K, rng_for(55, 1))
-    y = gpu.qgemv_group(dev(words.view(np.uint8).reshape(-1)), dev(meta.view(np.int32).reshape(-1)),
-                        N, K, 4, 64, dev_bf16(xb), y_dtype=torch.bfloat16)
+    cd, md = dev(words.view(np.uint8).reshape(-1)), dev(meta.view(np.int32).reshape(-1))
+    y16 = gpu.qgemv_group(cd, md, N, K, 4, 64, dev_bf16(xb), y_dtype=torch.bfloat16)
+    y32 = gpu.qgemv_group(cd, md, N, K, 4, 64, dev_bf16(xb))
     xv = oracle.product.bf16_to_f64(xb)
-    check_err(host(y), oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv), tol=2 ** -8)
+    check_bf16_out(host(y16), host(y32), oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
 
 
 def test_config1_end_to_end(gpu):

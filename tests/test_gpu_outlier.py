@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import check_err, dev, dev_bf16, host, say
+from gpu_util import check_bf16_out, check_err, dev, dev_bf16, host, say
 from workloads import gen_x_bf16, gen_x_f32, layer_weights, layer_x, rng_for
 
 pytestmark = pytest.mark.gpu
@@ -101,9 +101,11 @@ def test_gemv_long_rows_split_k(gpu):
     check_err(y, oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
 
 
-@pytest.mark.parametrize("M,N,K", [(40, 257, 512), (4000, 7900, 1024)])
+@pytest.mark.parametrize("M,N,K", [(40, 257, 512), (4000, 7900, 1024), (70, 200, 384)])
 def test_prefill(gpu, M, N, K):
-    """Both tile shapes (the second shape takes the 256 x 256 tile)."""
+    """Every tile shape: 128 x 256, 256 x 256 (M = 4000) and the
+    split-precision kernel of short reductions (K = 384), whose outlier step
+    carries the side columns as bf16 hi + lo too."""
     say(f"outlier prefill M={M} N={N} K={K}")
     W = _planted(N, K, [1, K // 2 - 1, K // 2], 11)
     words, meta, side, idx, W_hat = _oracle(W, 4, 64, 3)
@@ -124,12 +126,11 @@ def test_prefill_bf16_output(gpu):
     words, meta, side, idx, W_hat = _oracle(W, 3, 32, 2)
     X = gen_x_bf16(M, K, rng_for(325, 0))
     c, m, sd, ix = gpu.qpack_group_outlier(dev(W), 3, 32, 2)
-    Y = host(gpu.qgemm_prefill(gpu.make_qweight_group(c, m, N, K, 3, 32, side=sd, idx=ix), dev_bf16(X),
-                               y_dtype=torch.bfloat16))
+    w = gpu.make_qweight_group(c, m, N, K, 3, 32, side=sd, idx=ix)
+    Y16 = host(gpu.qgemm_prefill(w, dev_bf16(X), y_dtype=torch.bfloat16))
+    Y32 = host(gpu.qgemm_prefill(w, dev_bf16(X)))
     Xv = oracle.product.bf16_to_f64(X)
-    # bf16 weight tiles plus one bf16 rounding of y
-    check_err(Y, oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv),
-              2.0 ** -8 + 2.0 ** -14 + 2.0 ** -8)
+    check_bf16_out(Y16, Y32, oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv))
 
 
 def test_full_gate_shape(gpu):

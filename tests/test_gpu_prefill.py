@@ -65,38 +65,54 @@ def test_binlr_integer_exact(gpu):
     assert np.array_equal(Y, (Xi.astype(np.int64) @ C.T).astype(np.float64))
 
 
-@pytest.mark.parametrize("M", [512])
+def _sample_cols(N, n, seed):
+    """The first and last output and n more, sorted."""
+    return np.unique(np.concatenate([[0, N - 1], np.random.default_rng(seed).choice(N, n, replace=False)]))
+
+
+@pytest.mark.parametrize("M", [512, 4096])
 def test_full_rtn(gpu, M):
+    """Config 5, group RTN: the 8192 x 28672 gate matrix (4-bit g64, with its
+    outlier channels) against M = 512 and 4096 tokens, in the launch the
+    benchmark times.  Every token row is checked on 64 sampled outputs."""
     say(f"prefill full RTN M={M}")
     W = layer_weights("gate")
     N, K = W.shape
     codes, meta = gpu.qpack_group(dev(W), 4, 64)
     X = layer_x(K, M, config=5)
     Y = gpu.qgemm_prefill(gpu.make_qweight_group(codes, meta, N, K, 4, 64), dev_bf16(X))
-    rows = np.random.default_rng(5).choice(M, 12, replace=False)
-    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(6).choice(N, 60, replace=False)]))
-    Ys = host(Y)[np.ix_(rows, cols)]
+    cols = _sample_cols(N, 62, 6 + M)
+    Ys = host(Y)[:, cols]
     _, _, _, _, _, W_hat = group_reference(W[cols], 4, 64)
-    Xv = oracle.product.bf16_to_f64(X[rows])
+    Xv = oracle.product.bf16_to_f64(X)
     err = check_err(Ys, oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv))
     say(f"  err={err:.3e}")
 
 
-def test_full_binlr(gpu):
+@pytest.fixture(scope="module")
+def binlr_full(gpu):
     K, N, r = 8192, 28672, 4096
-    say("prefill full binary M=512")
     U, V, s1, s2 = binlr_factors(K, N, r)
     ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
-    M = 512
+    w = gpu.make_qweight_binlr(ubd, vbd, dev(s1.view(np.int16)), dev(s2.view(np.int16)), N, K, r)
+    return U, V, s1, s2, w
+
+
+@pytest.mark.parametrize("M", [512, 4096])
+def test_full_binlr(gpu, binlr_full, M):
+    """Config 5, binary: the r = 4096 factors of 8192 x 28672 against M = 512
+    and 4096 tokens; every token row checked on 42 sampled outputs."""
+    K, N, r = 8192, 28672, 4096
+    say(f"prefill full binary M={M}")
+    U, V, s1, s2, w = binlr_full
     X = layer_x(K, M, config=5)
-    Y = gpu.qgemm_prefill(gpu.make_qweight_binlr(ubd, vbd, dev(s1.view(np.int16)), dev(s2.view(np.int16)), N, K, r),
-                          dev_bf16(X))
-    rows = np.random.default_rng(7).choice(M, 8, replace=False)
-    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(8).choice(N, 40, replace=False)]))
-    Ys = host(Y)[np.ix_(rows, cols)]
+    Y = gpu.qgemm_prefill(w, dev_bf16(X))
+    cols = _sample_cols(N, 40, 8 + M)
+    Ys = host(Y)[:, cols]
     W = oracle.binlr.reconstruct(U[cols], V, s1[cols], s2)
-    Xv = oracle.product.bf16_to_f64(X[rows])
-    err = check_err(Ys, oracle.product.matmul_ref(W, Xv), oracle.product.abs_denominator(W, Xv))
+    Xv = oracle.product.bf16_to_f64(X)
+    err = check_err(Ys, oracle.product.matmul_ref(W, Xv),
+                    oracle.product.binlr_abs_denominator(U[cols], V, s1[cols], s2, Xv))
     say(f"  err={err:.3e}")
 
 

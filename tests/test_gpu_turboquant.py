@@ -3,10 +3,13 @@
 TurboQuant) against the CPU oracle: codes, signs and fp16 norms bit-exact;
 logits within the bound of one bf16 rounding of the rotated query operands.
 
-Logit error bound: Pi q and S Pi q are rounded once to bf16 (relative
-<= 2^-9 per element) and the products accumulate in fp32, so against
+Logit error bound: Pi q and S Pi q are formed in fp32 and rounded once to
+bf16, which has 8 significant bits, so each element moves by at most 2^-8
+of itself (round to nearest even, unit roundoff 2^-8); codebook values and
+signs are exact and the products accumulate in fp32.  Against
 D = |x| (sum |c||Pi q| + gamma sqrt(pi/2)/128 sum |S Pi q|) the error is
-<= 2^-9 D plus fp32 accumulation; the tests use 2^-8."""
+therefore <= 2^-8 D, plus the fp32 formation and accumulation of 128-term
+sums (below 2^-16 D): the tests hold every logit to 2^-8 + 2^-14."""
 import math
 
 import numpy as np
@@ -19,7 +22,7 @@ from workloads import rng_for
 
 pytestmark = pytest.mark.gpu
 tq = oracle.turboquant
-TOL = 2.0 ** -8
+TOL = 2.0 ** -8 + 2.0 ** -14
 
 
 def _setup(bits, seed):
@@ -196,9 +199,11 @@ def test_value_encoder_bit_exact(gpu, bits):
                                        (3, 2, 1), (2, 1, 5)])
 def test_attend(gpu, bits, nq, n):
     """Attention output over quantized values against the oracle's fp64
-    sum; fp32 sums over the values in the rotated domain, so the error is a
-    small multiple of 2^-24 of sum |P| |v_hat|; tested at 1e-4 of its largest
-    coordinate."""
+    sum, element by element.  The kernel sums over the values in the rotated
+    domain (weights p |v| as bf16 hi + lo, 2^-16 relative; fp32 sums) and
+    then applies Pi^T, so the error of output coordinate c is bounded by the
+    relative error of the rotated sums times
+    D[c] = sum_d |Pi[d][c]| sum_j |p_j| |v_j| |c_j[d]|; tested at 1e-4."""
     Pi, delta, table, cv = _value_setup(bits, 40 + nq)
     H = 3
     V = _keys(H * n, 50 + bits)
@@ -212,7 +217,9 @@ def test_attend(gpu, bits, nq, n):
     for h in range(H):
         sl = slice(h * n, (h + 1) * n)
         ref = tq.attend_values(P[h], codes[sl], n16[sl], Pi, cv)
-        Vh = tq.dequantize_mse(codes[sl], n16[sl].astype(np.float64), Pi, cv)
-        D = np.abs(P[h]).astype(np.float64) @ np.abs(Vh)
-        err = np.max(np.abs(out[h] - ref) / D.max(axis=1, keepdims=True))
+        # rotated-domain magnitudes |p_j| |v_j| |c_j[d]|, mapped through |Pi|
+        rot = np.abs(cv[codes[sl]]) * n16[sl].astype(np.float64)[:, None]
+        D = (np.abs(P[h]).astype(np.float64) @ rot) @ np.abs(Pi)
+        assert np.all(D > 0)
+        err = np.max(np.abs(out[h] - ref) / D)
         assert err <= 1e-4, (h, err)
