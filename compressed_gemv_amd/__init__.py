@@ -21,7 +21,7 @@ __all__ = [
     "qgroup_outlier_ws", "qpack_group_outlier", "qgemv_group_outlier", "qgemv_group_multi",
     "qcodebook_default", "qpack_group_cb", "qgemv_group_cb",
     "qtq_centroids", "qtq_rotation", "qtq_quant_keys", "qtq_project", "qtq_logits", "qtq_quant_values", "qtq_attend",
-    "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr",
+    "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr", "qgemv_binlr_noalloc",
     "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
 ]
 
@@ -99,6 +99,7 @@ def load() -> ctypes.CDLL:
         "qpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
         "qunpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
         "qgemv_binlr": (I32, [P, P, P, P, I64, I64, I64, P, I32, I64, P, I32, P, ctypes.c_size_t, P]),
+        "qgemv_binlr_noalloc": (I32, [P, P, P, P, I64, I64, I64, P, I32, I64, P, I32, P]),
         "qgemm_prefill_ws": (I32, [ctypes.POINTER(qweight), I64, SZ]),
         "qgemm_prefill": (I32, [ctypes.POINTER(qweight), P, I32, I64, P, I32, P, ctypes.c_size_t, P]),
     }
@@ -552,6 +553,27 @@ def qgemv_binlr(ubits, vtbits, s1, s2, N: int, K: int, r: int, x: torch.Tensor,
     _check(load().qgemv_binlr(_ptr(ubits), _ptr(vtbits), _ptr(s1), _ptr(s2), N, K, r, _ptr(x),
                               _dtype_code(x), B, _ptr(y), _dtype_code(y), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "qgemv_binlr")
+    return y
+
+
+def qgemv_binlr_noalloc(ubits, vtbits, s1, s2, N: int, K: int, r: int, x: torch.Tensor,
+                        y: Optional[torch.Tensor] = None, y_dtype=torch.float32, stream=None):
+    """qgemv_binlr with the library's per-device scratch array as workspace
+    (no workspace argument; the C call allocates nothing).  Pass y to keep
+    the whole call free of allocations."""
+    B = _batch(x, K)
+    ub, vb, _ = qbinlr_sizes(N, K, r, B)
+    _need_bytes(ubits, ub, "ubits")
+    _need_bytes(vtbits, vb, "vtbits")
+    _need_numel(s1, N, "s1", _H16, exact=False)
+    _need_numel(s2, K, "s2", _H16, exact=False)
+    if y is None:
+        y = torch.empty((B, N), dtype=y_dtype, device=x.device)
+    _need_numel(y, B * N, "y", _OUT)
+    _need_cuda(ubits, vtbits, s1, s2, x, y)
+    _check(load().qgemv_binlr_noalloc(_ptr(ubits), _ptr(vtbits), _ptr(s1), _ptr(s2), N, K, r, _ptr(x),
+                                      _dtype_code(x), B, _ptr(y), _dtype_code(y), _stream(stream)),
+           "qgemv_binlr_noalloc")
     return y
 
 

@@ -507,6 +507,26 @@ int qgemv_binlr(const void* ubits, const void* vtbits, const uint16_t* s1, const
       x, x_dtype, B, y, y_dtype, ws, stream));
 }
 
+int qgemv_binlr_noalloc(const void* ubits, const void* vtbits, const uint16_t* s1, const uint16_t* s2,
+                        int64_t N, int64_t K, int64_t r, const void* x, int x_dtype, int64_t B, void* y,
+                        int y_dtype, hipStream_t stream) {
+  size_t need = 0;
+  const int st = qbinlr_sizes(N, K, r, B, nullptr, nullptr, &need);
+  if (st != Q_OK) return st;
+  if (!ubits || !vtbits || !s1 || !s2 || !x || !y) return Q_EINVAL;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return Q_EINVAL;
+  if (!aligned(ubits, 16) || !aligned(vtbits, 16) || !aligned(x, 4) || !aligned(y, 4) || !aligned(s1, 2) ||
+      !aligned(s2, 2))
+    return Q_EALIGN;
+  if (need > Q_BINLR_NOALLOC_MAX_WS) return Q_EUNSUPPORTED;
+  hipError_t e;
+  void* ws = qg::binlr_scratch_ptr(&e);
+  if (!ws) return Q_EHIP;
+  return hip_status(qg::launch_gemv_binlr(
+      static_cast<const uint32_t*>(ubits), static_cast<const uint32_t*>(vtbits), s1, s2, N, K, r,
+      x, x_dtype, B, y, y_dtype, ws, stream));
+}
+
 int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes) {
   if (!w || !ws_bytes || M < 1 || M > kMaxDim) return Q_EINVAL;
   if (w->format == Q_FMT_GROUP) {

@@ -35,6 +35,9 @@
 // sums meet in LDS.
 #include "common.hpp"
 #include "launch.hpp"
+#include "qgemv.h"
+
+#include <mutex>
 
 namespace qg {
 
@@ -457,6 +460,30 @@ hipError_t bin_gemv_t(const uint32_t* bits, int64_t R, int64_t Wn, int64_t Lk, c
 int64_t pw(int64_t n) { return ((n + 31) / 32 + 3) / 4 * 4; }
 
 }  // namespace
+
+// Scratch for callers that cannot allocate (qgemv_binlr_noalloc): the
+// binary GEMV's workspace as one device array per GPU, alive until the
+// process ends.  Host code uses the address hipGetSymbolAddress returns for
+// the current device, never the array's name.
+static __device__ __align__(256) uint8_t scratch[Q_BINLR_NOALLOC_MAX_WS];
+
+void* binlr_scratch_ptr(hipError_t* err) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) { *err = hipErrorInvalidDevice; return nullptr; }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  *err = hipSuccess;
+  return ptrs[dev];
+}
 
 int64_t binlr_ws_bytes_per_batch(int64_t r) {
   // stage-2 table (4 bytes per entry, whole 512-entry steps) + (C, V) partials

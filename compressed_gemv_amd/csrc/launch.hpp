@@ -73,6 +73,9 @@ hipError_t launch_gemv_group_cb(const uint32_t* codes, const uint32_t* meta, con
 // Workspace bytes per batch row of qgemv_binlr: the stage-2 table and the
 // stage-1 partial sums.
 int64_t binlr_ws_bytes_per_batch(int64_t r);
+// The per-device scratch array of qgemv_binlr_noalloc (Q_BINLR_NOALLOC_MAX_WS
+// bytes): its device address on the current device, looked up once.
+void* binlr_scratch_ptr(hipError_t* err);
 hipError_t launch_gemv_binlr(const uint32_t* ubits, const uint32_t* vtbits,
                              const uint16_t* s1, const uint16_t* s2, int64_t N, int64_t K,
                              int64_t r, const void* x, int x_dtype, int64_t B, void* y,

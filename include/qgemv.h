@@ -294,6 +294,23 @@ int qgemv_binlr(const void* ubits, const void* vtbits, const uint16_t* s1,
                 const void* x, int x_dtype, int64_t B, void* y, int y_dtype,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* qgemv_binlr without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream/graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a static
+ * device array of Q_BINLR_NOALLOC_MAX_WS bytes that the library holds on
+ * each GPU it runs on until the process ends; the call allocates nothing.
+ * Same arguments, limits and results as qgemv_binlr; Q_EUNSUPPORTED when
+ * the workspace qbinlr_sizes reports for (N, K, r, B) exceeds
+ * Q_BINLR_NOALLOC_MAX_WS (e.g. r <= 16384 fits at B = 16).  Every call on
+ * one GPU uses that GPU's array: calls that may overlap on one GPU (other
+ * streams, other host threads) race and must be serialized by the caller.
+ * No state carries from one call to the next. */
+#define Q_BINLR_NOALLOC_MAX_WS ((size_t)2 << 20)
+int qgemv_binlr_noalloc(const void* ubits, const void* vtbits, const uint16_t* s1,
+                        const uint16_t* s2, int64_t N, int64_t K, int64_t r,
+                        const void* x, int x_dtype, int64_t B, void* y, int y_dtype,
+                        hipStream_t stream);
+
 /* --------------------------------------------------------------- prefill */
 typedef struct qweight {
   int format;                 /* Q_FMT_GROUP or Q_FMT_BINLR */

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 30, names
+    assert len(names) == 31, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -58,6 +58,9 @@ def test_size_queries(lib):
     assert ub == 10 * 16 and vb == 3 * 16 and ws == 2 * (2048 + 16)
     w = cg.qweight(cg.Q_FMT_BINLR, 28672, 8192, 0, 0, None, None, 4096, None, None, None, None)
     assert cg.qgemm_prefill_ws(w, 512) == 512 * 4096 * 2
+    # short reductions keep T in fp32 (split-precision passes)
+    w = cg.qweight(cg.Q_FMT_BINLR, 1000, 256, 0, 0, None, None, 300, None, None, None, None)
+    assert cg.qgemm_prefill_ws(w, 70) == 70 * 384 * 4
     w = cg.qweight(cg.Q_FMT_GROUP, 28672, 8192, 4, 64, None, None, 0, None, None, None, None)
     assert cg.qgemm_prefill_ws(w, 512) == 0
 
@@ -98,6 +101,15 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemv_binlr(good, good, good, good, 64, 128, 16, good, cg.Q_BF16, 1, good, cg.Q_F32,
                            P(0), 1 << 20, s) == cg.Q_EWORKSPACE
     assert lib.qpack_binlr(good, good, 64, 128, 0, good, good, s) == cg.Q_EINVAL
+    # binary without a workspace argument: the scratch array's limit, nulls, alignment
+    assert lib.qgemv_binlr_noalloc(good, good, good, good, 64, 128, 65536, good, cg.Q_BF16, 16, good, cg.Q_F32,
+                                   s) == cg.Q_EUNSUPPORTED
+    assert lib.qgemv_binlr_noalloc(good, P(0), good, good, 64, 128, 16, good, cg.Q_BF16, 1, good, cg.Q_F32,
+                                   s) == cg.Q_EINVAL
+    assert lib.qgemv_binlr_noalloc(odd, good, good, good, 64, 128, 16, good, cg.Q_BF16, 1, good, cg.Q_F32,
+                                   s) == cg.Q_EALIGN
+    assert lib.qgemv_binlr_noalloc(good, good, good, good, 64, 128, 16, good, cg.Q_BF16, 17, good, cg.Q_F32,
+                                   s) == cg.Q_EINVAL
     # grouped GEMV: count and per-matrix checks
     mats = (cg.qgroup_mat * 5)(*[cg.qgroup_mat(0x10000, 0x10000, 64, 0x10000) for _ in range(5)])
     assert lib.qgemv_group_multi(mats, 5, 128, 4, 32, good, cg.Q_BF16, 1, cg.Q_F32, s) == cg.Q_EINVAL
