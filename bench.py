@@ -73,6 +73,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one plain 1 GiB device copy (pmc calibration)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated substrings: measure only the rows whose names contain one (profiling)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read reference")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -119,29 +122,31 @@ def main():
     def time_launches(fn, steps, warmup, period=None):
         """(wall seconds, event seconds) over exactly `steps` launches after `warmup`.
 
-        The launches are captured into a HIP graph of `period` steps (one per
-        rotating-pool copy) replayed steps // period times, plus a graph of
-        the remaining steps % period, so the host's per-call cost (Python
-        binding, two launches for the binary path) never starves the GPU;
-        every replayed kernel still streams its own copy.  Events are
-        recorded on the stream the kernels run on.
+        The `steps` launches (launch i on rotating-pool copy i) are captured
+        into one HIP graph and replayed once inside the timed region, so the
+        host's per-call cost (Python binding, two launches for the binary
+        path) never starves the GPU and the region holds a single graph
+        launch; past 4096 steps, a graph of `period` launches is replayed
+        several times plus one of the remainder.  The capture is replayed
+        once untimed.  Events are recorded on the stream the kernels run on.
         """
-        period = min(period or 1, steps)
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
-        g = capture(fn, range(period))
-        reps, rem = divmod(steps, period)
-        tail = capture(fn, range(rem)) if rem else None
+        if steps <= 4096:
+            graphs = [capture(fn, range(steps))]
+        else:
+            period = min(period or 1, steps)
+            reps, rem = divmod(steps, period)
+            g = capture(fn, range(period))
+            graphs = [g] * reps + ([capture(fn, range(rem))] if rem else [])
         stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record(stream)
-        for _ in range(reps):
+        for g in graphs:
             g.replay()
-        if tail is not None:
-            tail.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -179,12 +184,15 @@ def main():
 
     rows = {}
     if not args.no_rows:
+        only = [o for o in args.only.split(",") if o]
         rows = measure_rows(cg, torch, np, dev, W, to_dev, bf16, pool_of, time_launches, log,
-                            LAYER_SHAPES, MIXED_SETS, N_LAYERS, ATTN, layer_weights, layer_x, binlr_factors)
+                            LAYER_SHAPES, MIXED_SETS, N_LAYERS, ATTN, layer_weights, layer_x, binlr_factors,
+                            lambda name: not only or any(o in name for o in only))
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(np, W, bits, group, log)
+    ceiling = None if args.no_ceiling else stream_ceiling(cg, torch, dev, time_launches, log)
 
     traffic = committed_traffic()
     out = {
@@ -207,6 +215,7 @@ def main():
             "compressed_bytes_per_step": nbytes,
             "rotating_pool_copies": max(2, int(args.pool_gib * (1 << 30) // nbytes) + 1),
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "timed_region": "one HIP graph of all steps, replayed once between two torch.cuda.synchronize()",
             "tok_s_equivalent_80_layers_4b_g64": round(value * 1e9 / (N_LAYERS * layer_bytes(4, 64, 4, 64)), 1),
         },
         "roofline": {
@@ -218,6 +227,11 @@ def main():
             "traffic": traffic,
             "kernel": "gemv_b1_kernel<4,64,bf16>",
             "per_launch_us": round(ev / args.steps * 1e6, 3),
+            "timing": "achieved = algorithmic bytes / per_launch_us, per_launch_us = HIP-event time of the "
+                      "timed region (graph of all steps, on the launch stream) / steps; value uses the "
+                      "wall-clock time of the same region",
+            "streaming_read_ceiling": ceiling,
+            "frac_of_measured_ceiling": (round(achieved / ceiling["read_132MB_GBps"], 4) if ceiling else None),
             "kernel_source_sha": kernel_source_sha(),
         },
         "cpu_baseline": cpu,
@@ -242,7 +256,8 @@ def layer_bytes(attn_bits, attn_group, mlp_bits, mlp_group):
 
 
 def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launches, log,
-                 LAYER_SHAPES, MIXED_SETS, N_LAYERS, ATTN, layer_weights, layer_x, binlr_factors):
+                 LAYER_SHAPES, MIXED_SETS, N_LAYERS, ATTN, layer_weights, layer_x, binlr_factors, want):
+    """Every other row of the hot path; want(name) selects rows (all by default)."""
     rows = {}
     steps, warm = 200, 20
 
@@ -265,10 +280,13 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
                 "pct_hbm_peak": round(100 * gbs / 8000.0, 2), "bytes": nbytes}
 
     # batch 16 on the headline shape
-    rows["gemv_4b_g64_gate_B16"] = gemv_row("gate", W_gate, 4, 64, 16)
-    log("B16:", rows["gemv_4b_g64_gate_B16"])
+    if want("gemv_4b_g64_gate_B16"):
+        rows["gemv_4b_g64_gate_B16"] = gemv_row("gate", W_gate, 4, 64, 16)
+        log("B16:", rows["gemv_4b_g64_gate_B16"])
     # whole 4-bit layer set at batch 1, and the mixed-width sets
     for label, spec in [("4b_g64", {"attn_bits": 4, "mlp_bits": 4, "group": 64})] + list(MIXED_SETS.items()):
+        if not (want(f"layer_set_{label}_B1") or (label == "4b_g64" and want("layer_set_4b_g64_B1_grouped"))):
+            continue
         per = {}
         t_layer = 0.0
         for name in ["q", "k", "v", "o", "gate", "up", "down"]:
@@ -304,18 +322,19 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         torch.cuda.empty_cache()
         return {"us": round(ev / steps * 1e6, 3), "GB/s": round(nbytes * steps / ev / 1e9, 1), "bytes": nbytes}
 
-    g_qkv = grouped_row([(n, layer_weights(n)) for n in ("q", "k", "v")], 4, 64)
-    g_gu = grouped_row([("gate", W_gate), ("up", W_gate)], 4, 64)
-    per = rows["layer_set_4b_g64_B1"]["per_matrix"]
-    t_layer = g_qkv["us"] + per["o"]["us"] + g_gu["us"] + per["down"]["us"]
-    layer_b = g_qkv["bytes"] + per["o"]["bytes"] + g_gu["bytes"] + per["down"]["bytes"]
-    rows["layer_set_4b_g64_B1_grouped"] = {
-        "sum_kernel_us_per_layer": round(t_layer, 2),
-        "GB/s": round(layer_b / (t_layer * 1e-6) / 1e9, 1),
-        "tok_s_equivalent_80_layers": round(1.0 / (N_LAYERS * t_layer * 1e-6), 1),
-        "launches": {"qkv": g_qkv, "o": per["o"], "gate_up": g_gu, "down": per["down"]},
-    }
-    log("grouped layer set:", rows["layer_set_4b_g64_B1_grouped"]["GB/s"], "GB/s")
+    if want("layer_set_4b_g64_B1_grouped"):
+        g_qkv = grouped_row([(n, layer_weights(n)) for n in ("q", "k", "v")], 4, 64)
+        g_gu = grouped_row([("gate", W_gate), ("up", W_gate)], 4, 64)
+        per = rows["layer_set_4b_g64_B1"]["per_matrix"]
+        t_layer = g_qkv["us"] + per["o"]["us"] + g_gu["us"] + per["down"]["us"]
+        layer_b = g_qkv["bytes"] + per["o"]["bytes"] + g_gu["bytes"] + per["down"]["bytes"]
+        rows["layer_set_4b_g64_B1_grouped"] = {
+            "sum_kernel_us_per_layer": round(t_layer, 2),
+            "GB/s": round(layer_b / (t_layer * 1e-6) / 1e9, 1),
+            "tok_s_equivalent_80_layers": round(1.0 / (N_LAYERS * t_layer * 1e-6), 1),
+            "launches": {"qkv": g_qkv, "o": per["o"], "gate_up": g_gu, "down": per["down"]},
+        }
+        log("grouped layer set:", rows["layer_set_4b_g64_B1_grouped"]["GB/s"], "GB/s")
     # the headline shape with its outlier channels kept aside in fp16 (0.1 %
     # of K = 8 channels); bytes = codes + meta + side columns
     def outlier_row(W, bits, group, n_out, B):
@@ -343,6 +362,8 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
                 "plain_gemv_us_same_pool": round(ev_plain / steps * 1e6, 3)}
 
     for B in (1, 16):
+        if not want(f"gemv_4b_g64_gate_outlier8_B{B}"):
+            continue
         rows[f"gemv_4b_g64_gate_outlier8_B{B}"] = outlier_row(W_gate, 4, 64, 8, B)
         log(f"outlier B{B}:", rows[f"gemv_4b_g64_gate_outlier8_B{B}"])
     # the headline shape with per-group codebooks (default 8-book dictionary);
@@ -373,6 +394,8 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
                 "plain_gemv_us_same_pool": round(ev_plain / steps * 1e6, 3)}
 
     for bits, B in [(4, 1), (4, 16), (2, 1)]:
+        if not want(f"gemv_{bits}b_g64_gate_codebook_B{B}"):
+            continue
         rows[f"gemv_{bits}b_g64_gate_codebook_B{B}"] = codebook_row(W_gate, bits, 64, B)
         log(f"codebook {bits}b B{B}:", rows[f"gemv_{bits}b_g64_gate_codebook_B{B}"])
     # attention logits from quantized keys (random rotation + Lloyd-Max codes
@@ -426,6 +449,8 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
                 "speedup_vs_fp32": round(base["fp32"] / us, 2), "speedup_vs_bf16": round(base["bf16"] / us, 2)}
 
     for kb in (4, 3):
+        if not want(f"kv_logits_{kb}bit_h8_n131072_q4"):
+            continue
         rows[f"kv_logits_{kb}bit_h8_n131072_q4"] = kv_row(kb)
         log(f"kv logits {kb}-bit:", rows[f"kv_logits_{kb}bit_h8_n131072_q4"])
 
@@ -474,16 +499,21 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
                 "torch_bf16_values_us": base["bf16"], "torch_fp32_values_us": base["fp32"],
                 "speedup_vs_fp32": round(base["fp32"] / us, 2), "speedup_vs_bf16": round(base["bf16"] / us, 2)}
 
-    rows["kv_attend_3bit_h8_n131072_q4"] = kv_attend_row(3)
-    log("kv attend 3-bit:", rows["kv_attend_3bit_h8_n131072_q4"])
+    if want("kv_attend_3bit_h8_n131072_q4"):
+        rows["kv_attend_3bit_h8_n131072_q4"] = kv_attend_row(3)
+        log("kv attend 3-bit:", rows["kv_attend_3bit_h8_n131072_q4"])
     # mixed widths at batch 8 (MLP shape)
     for bits in (3, 2):
-        rows[f"gemv_{bits}b_g32_gate_B8"] = gemv_row("gate", W_gate, bits, 32, 8)
+        if want(f"gemv_{bits}b_g32_gate_B8"):
+            rows[f"gemv_{bits}b_g32_gate_B8"] = gemv_row("gate", W_gate, bits, 32, 8)
     for bits in (6, 5):
-        rows[f"gemv_{bits}b_g32_q_B8"] = gemv_row("q", layer_weights("q"), bits, 32, 8)
+        if want(f"gemv_{bits}b_g32_q_B8"):
+            rows[f"gemv_{bits}b_g32_q_B8"] = gemv_row("q", layer_weights("q"), bits, 32, 8)
 
     # binary low-rank GEMV
     for (K, N, r) in [(8192, 28672, 4096), (8192, 8192, 2048)]:
+        if not want(f"binlr_gemv_{K}x{N}_r{r}_B1"):
+            continue
         U, V, s1, s2 = binlr_factors(K, N, r)
         ub, vb = cg.qpack_binlr(to_dev(U), to_dev(V))
         nbytes = (r * (N + K)) // 8 + 2 * (N + K)
@@ -508,6 +538,9 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         torch.cuda.empty_cache()
 
     # prefill GEMM, both formats
+    if not any(want(f"prefill_{lb}_M{M}") for lb in ("rtn_4b_g64", "binlr_r4096", "codebook_4b_g64")
+               for M in (512, 4096)):
+        return rows
     K, N = 8192, 28672
     codes, meta = cg.qpack_group(to_dev(W_gate), 4, 64)
     wq = cg.make_qweight_group(codes, meta, N, K, 4, 64)
@@ -523,6 +556,8 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
         for label, w, flops in [("rtn_4b_g64", wq, 2.0 * M * N * K), ("binlr_r4096", wb, 2.0 * M * 4096 * (K + N)),
                                 ("codebook_4b_g64", wcb, 2.0 * M * N * K)]:
+            if not want(f"prefill_{label}_M{M}"):
+                continue
             ws = None
             need = cg.qgemm_prefill_ws(w, M)
             if need:
@@ -538,46 +573,94 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
 
 def cpu_baseline(np, W, bits, group, log):
     """The oracle as it stands, on a bounded sample of rows of the same matrix:
-    unpack codes -> rebuild W_hat (fp64) -> multiply, as GB/s of compressed
-    bytes.  Offline quantize/pack of the sample is not timed."""
+    unpack codes -> rebuild W_hat (fp64) and the fp64 product, timed
+    separately, median of three runs, as GB/s of compressed bytes.  The
+    offline quantize/pack of the sample is not timed.  BLAS runs on every core
+    of this process's affinity set; the rebuild is numpy on one thread (as
+    the oracle is written)."""
     import oracle
     from workloads import layer_x
+    cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_limits, threadpool_info
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
+        limiter, blas = None, 1
     N, K = W.shape
     x = oracle.product.bf16_to_f64(layer_x(K, 1))
     per_row = K * bits // 8 + (K // group) * 4
 
-    def timed(R):
-        sub = W[:R]
-        q, s, o = oracle.rtn.quantize(sub, bits, group)       # offline: not timed
-        words = oracle.fmt.pack_codes(q, bits)
-        meta = oracle.fmt.pack_meta(s, o)
+    def packed(R):
+        q, s, o = oracle.rtn.quantize(W[:R], bits, group)       # offline: not timed
+        return oracle.fmt.pack_codes(q, bits), oracle.fmt.pack_meta(s, o)
+
+    def timed(R, words, meta):
         t0 = time.perf_counter()
         W_hat = oracle.product.what_group(words, meta, R, K, bits, group)
+        t1 = time.perf_counter()
         _ = oracle.product.matmul_ref(W_hat, x)
-        return time.perf_counter() - t0
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1
 
-    # probe a small sample, then size the measured sample to ~10 s of work
+    # probe a small sample, then size the sample to ~4 s per run (three runs)
     R0 = min(N, 1024)
-    t0 = timed(R0)
-    R = int(min(N, max(R0, R0 * 10.0 / max(t0, 1e-3))))
-    dt = timed(R) if R != R0 else t0
-    log(f"cpu oracle: {R} rows in {dt:.2f} s")
-    best = (R, dt)
-    R, dt = best
+    a0, b0 = timed(R0, *packed(R0))
+    R = int(min(N, max(R0, R0 * 4.0 / max(a0 + b0, 1e-3))))
+    words, meta = packed(R)
+    runs = [timed(R, words, meta) for _ in range(3)]
+    rec = sorted(r[0] for r in runs)[1]
+    mul = sorted(r[1] for r in runs)[1]
+    tot = sorted(r[0] + r[1] for r in runs)[1]
+    if limiter is not None:
+        limiter.restore_original_limits()
+    log(f"cpu oracle: {R} rows, rebuild {rec:.2f} s + product {mul:.2f} s (median of 3), {cores} cores, {cpu_model}")
     return {
-        "value": round(R * per_row / dt / 1e9, 4),
+        "value": round(R * per_row / tot / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": int(cores),
         "kind": "oracle",
-        "sample": f"{R} of {N} rows of the same 8192x28672 4-bit g64 matrix "
-                  f"({R * per_row} compressed bytes): unpack + rebuild W_hat in fp64 (numpy, one thread) "
-                  f"+ fp64 product (BLAS, {threads} threads), {dt:.2f} s",
+        "sample": f"{R} of {N} rows of the same 8192x28672 4-bit g64 matrix ({R * per_row} compressed bytes), "
+                  f"median of 3 runs: unpack + rebuild W_hat in fp64 {rec:.3f} s (numpy, one thread) + fp64 "
+                  f"product {mul:.3f} s (BLAS, {blas} threads)",
+        "cpu_model": cpu_model,
+        "affinity_cores": int(cores),
+        "blas_threads": int(blas),
+        "rebuild_s": round(rec, 4),
+        "product_s": round(mul, 4),
+        "rows": int(R),
     }
+
+
+def stream_ceiling(cg, torch, dev, time_launches, log):
+    """Read rate this GPU's HBM gives a plain read-only stream of 16-byte
+    nontemporal loads (the library's streaming-read kernel): 132 MB passes
+    (the headline launch's size) over a 2 GiB rotating pool, timed the same
+    way as the headline, and 4 GiB passes; the measured ceiling beside the
+    8 TB/s specification."""
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    n = 132_120_576
+    chunks = [buf[i * n:(i + 1) * n] for i in range((2 << 30) // n + 1)]
+    _, ev = time_launches(lambda i: cg.qstream_read(chunks[i % len(chunks)], sink), 400, 20, period=len(chunks))
+    small = n * 400 / ev / 1e9
+    _, ev = time_launches(lambda i: cg.qstream_read(buf, sink), 10, 2)
+    big = buf.numel() * 10 / ev / 1e9
+    del buf, chunks
+    torch.cuda.empty_cache()
+    log(f"streaming read: {small:.0f} GB/s per 132 MB pass, {big:.0f} GB/s over 4 GiB")
+    return {"read_132MB_GBps": round(small, 1), "read_4GiB_GBps": round(big, 1),
+            "method": "qstream_read (16-byte nontemporal loads, 1024x256 threads, nothing written), "
+                      "HIP events over one graph of back-to-back passes"}
 
 
 if __name__ == "__main__":

@@ -22,7 +22,7 @@ __all__ = [
     "qcodebook_default", "qpack_group_cb", "qgemv_group_cb",
     "qtq_centroids", "qtq_rotation", "qtq_quant_keys", "qtq_project", "qtq_logits", "qtq_quant_values", "qtq_attend",
     "qbinlr_sizes", "qpack_binlr", "qunpack_binlr", "qgemv_binlr", "qgemv_binlr_noalloc",
-    "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
+    "qstream_read", "qgemm_prefill_ws", "qgemm_prefill", "Q_F32", "Q_BF16", "Q_FMT_GROUP", "Q_FMT_BINLR",
 ]
 
 Q_OK, Q_EINVAL, Q_EALIGN, Q_EUNSUPPORTED, Q_ERANGE, Q_EWORKSPACE, Q_EHIP = 0, -1, -2, -3, -4, -5, -6
@@ -100,6 +100,7 @@ def load() -> ctypes.CDLL:
         "qunpack_binlr": (I32, [P, P, I64, I64, I64, P, P, P]),
         "qgemv_binlr": (I32, [P, P, P, P, I64, I64, I64, P, I32, I64, P, I32, P, ctypes.c_size_t, P]),
         "qgemv_binlr_noalloc": (I32, [P, P, P, P, I64, I64, I64, P, I32, I64, P, I32, P]),
+        "qstream_read": (I32, [P, ctypes.c_size_t, P, P]),
         "qgemm_prefill_ws": (I32, [ctypes.POINTER(qweight), I64, SZ]),
         "qgemm_prefill": (I32, [ctypes.POINTER(qweight), P, I32, I64, P, I32, P, ctypes.c_size_t, P]),
     }
@@ -575,6 +576,18 @@ def qgemv_binlr_noalloc(ubits, vtbits, s1, s2, N: int, K: int, r: int, x: torch.
                                       _dtype_code(x), B, _ptr(y), _dtype_code(y), _stream(stream)),
            "qgemv_binlr_noalloc")
     return y
+
+
+# -------------------------------------------------------------- measurement
+def qstream_read(buf: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """Read buf once as a plain 16-byte nontemporal stream (bandwidth
+    reference); out is a device int32 scratch word."""
+    nbytes = _nbytes(buf)
+    if nbytes % 16:
+        raise ValueError("buf: size not a multiple of 16 bytes")
+    _need_bytes(out, 4, "out")
+    _need_cuda(buf, out)
+    _check(load().qstream_read(_ptr(buf), nbytes, _ptr(out), _stream(stream)), "qstream_read")
 
 
 # ------------------------------------------------------------------ prefill

@@ -22,7 +22,7 @@ ARCH = os.environ.get("QGEMV_ARCH", "gfx950")
 
 SOURCES = ["capi.hip", "pack.hip", "gemv_group.hip", "gemv_binlr.hip", "gemm_prefill.hip", "gemm_prefill_outlier.hip",
            "gemv_codebook.hip", "gemm_prefill_codebook.hip",
-           "turboquant.hip"]
+           "turboquant.hip", "stream_read.hip"]
 
 CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

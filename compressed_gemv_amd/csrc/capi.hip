@@ -313,6 +313,9 @@ int qtq_rotation(int d, const double* G, double* Pi) {
 
 namespace {
 constexpr int kTqDim = 128;
+// one head's keys are addressed through 32-bit byte offsets (64 bytes of
+// fp32 input per key half-row, 256 bytes of slack): n below this bound
+constexpr int64_t kTqMaxKeys = (((int64_t)1 << 32) - 256) / 64;
 // bits = stored bits per coordinate; the table has 2^m entries, m = bits - 1
 // for keys (one sign bit) and m = bits for values
 int tq_table_ok(int m, float delta, const uint8_t* table) {
@@ -325,7 +328,7 @@ int tq_args_ok(int64_t n, int64_t heads, int bits, float delta, const uint8_t* t
   if (n < 1 || heads < 1 || bits < 3 || bits > 4 || !table) return Q_EINVAL;
   if (!(delta > 0.0f) || !isfinite(delta)) return Q_EINVAL;
   // keys of one head are addressed through 32-bit buffer offsets
-  if (n * 64 >= ((int64_t)1 << 32) - 256 || n * heads > INT32_MAX || heads > 65535) return Q_EUNSUPPORTED;
+  if (n >= kTqMaxKeys || heads > 65535 || n * heads > INT32_MAX) return Q_EUNSUPPORTED;
   const int L = 1 << (bits - 1);
   for (int k = 0; k < L; ++k)
     if (table[k] < 1 || table[k] > 127) return Q_EINVAL;
@@ -339,6 +342,7 @@ void tq_table_words(const uint8_t* t, int L, uint32_t* w4) {
 
 int qtq_sizes(int64_t n, int bits, size_t* codes_bytes, size_t* signs_bytes, size_t* norms_bytes) {
   if (n < 1 || bits < 3 || bits > 4) return Q_EINVAL;
+  if (n >= kTqMaxKeys) return Q_EUNSUPPORTED;
   if (codes_bytes) *codes_bytes = (size_t)(n * kTqDim * (bits - 1) / 8);
   if (signs_bytes) *signs_bytes = (size_t)(n * kTqDim / 8);
   if (norms_bytes) *norms_bytes = (size_t)(n * 4);
@@ -405,7 +409,7 @@ int qtq_quant_values(const float* V, int64_t n, int bits, const double* Pi, floa
   int st = tq_table_ok(bits, delta, table);
   if (st != Q_OK) return st;
   if (!V || !Pi || !codes || !norms) return Q_EINVAL;
-  if (n * 64 >= ((int64_t)1 << 32) - 256) return Q_EUNSUPPORTED;
+  if (n >= kTqMaxKeys) return Q_EUNSUPPORTED;
   if (!aligned(V, 4) || !aligned(Pi, 8) || !aligned(codes, 4) || !aligned(norms, 4)) return Q_EALIGN;
   uint32_t tw[4];
   tq_table_words(table, 1 << bits, tw);
@@ -424,6 +428,7 @@ int qtq_quant_values(const float* V, int64_t n, int bits, const double* Pi, floa
 
 int qtq_attend_ws(int64_t n, int64_t heads, int64_t nq, size_t* ws_bytes) {
   if (n < 1 || heads < 1 || heads > 65535 || nq < 1 || nq > 65535 || !ws_bytes) return Q_EINVAL;
+  if (n >= kTqMaxKeys) return Q_EUNSUPPORTED;
   *ws_bytes = (size_t)(heads * ((nq + 15) / 16) * qg::tq_attend_blocks(n, heads) * 16 * 129 * 4);
   return Q_OK;
 }
@@ -438,7 +443,7 @@ int qtq_attend(const void* codes, const uint32_t* norms, int64_t n, int64_t head
   if ((st = qtq_attend_ws(n, heads, nq, &need)) != Q_OK) return st;
   if (!codes || !norms || !Pi || !P || !out) return Q_EINVAL;
   if (!ws || ws_bytes < need) return Q_EWORKSPACE;
-  if (n * 64 >= ((int64_t)1 << 32) - 256 || n * heads > INT32_MAX) return Q_EUNSUPPORTED;
+  if (n * heads > INT32_MAX) return Q_EUNSUPPORTED;
   if (!aligned(codes, 4) || !aligned(norms, 4) || !aligned(Pi, 8) || !aligned(P, 4) || !aligned(out, 4) ||
       !aligned(ws, 16))
     return Q_EALIGN;
@@ -525,6 +530,12 @@ int qgemv_binlr_noalloc(const void* ubits, const void* vtbits, const uint16_t* s
   return hip_status(qg::launch_gemv_binlr(
       static_cast<const uint32_t*>(ubits), static_cast<const uint32_t*>(vtbits), s1, s2, N, K, r,
       x, x_dtype, B, y, y_dtype, ws, stream));
+}
+
+int qstream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream) {
+  if (!buf || !out || bytes == 0 || bytes % 16) return Q_EINVAL;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return Q_EALIGN;
+  return hip_status(qg::launch_stream_read(buf, (uint64_t)bytes, out, stream));
 }
 
 int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes) {

@@ -81,6 +81,9 @@ hipError_t launch_gemv_binlr(const uint32_t* ubits, const uint32_t* vtbits,
                              int64_t r, const void* x, int x_dtype, int64_t B, void* y,
                              int y_dtype, void* ws, hipStream_t s);
 
+// Read `bytes` (a multiple of 16) once with 16-byte nontemporal loads.
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* out, hipStream_t s);
+
 hipError_t launch_gemm_group(const uint32_t* codes, const uint32_t* meta, int64_t N,
                              int64_t K, int bits, int group, const uint16_t* X, int64_t M,
                              void* Y, int y_dtype, hipStream_t s,

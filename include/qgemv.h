@@ -225,7 +225,9 @@ int qtq_centroids(int d, int mbits, float* delta, uint8_t* table);
  * d); with G of i.i.d. N(0, 1) entries, a random rotation.  Q_ERANGE if G is
  * singular. */
 int qtq_rotation(int d, const double* G, double* Pi);
-/* Byte sizes of codes, signs and norms for n keys (host only). */
+/* Byte sizes of codes, signs and norms for n keys (host only).  Every
+ * key-cache call takes n < 67108860 per head (one head's data is addressed
+ * through 32-bit offsets) and returns Q_EUNSUPPORTED beyond. */
 int qtq_sizes(int64_t n, int bits, size_t* codes_bytes, size_t* signs_bytes, size_t* norms_bytes);
 /* Encode n keys K[n][128] (fp32, device): y = Pi x / |x|, each coordinate
  * to the nearest centroid (ties to the lower index), residual r = y - c,
@@ -257,7 +259,7 @@ int qtq_logits(const void* codes, const uint32_t* signs, const uint32_t* norms, 
  * order.  Synchronizes `stream`; Q_ERANGE as qtq_quant_keys. */
 int qtq_quant_values(const float* V, int64_t n, int bits, const double* Pi, float delta, const uint8_t* table,
                      void* codes, uint32_t* norms, hipStream_t stream);
-/* Workspace bytes of qtq_attend (host). */
+/* Workspace bytes of qtq_attend (host); Q_EUNSUPPORTED for n >= 67108860. */
 int qtq_attend_ws(int64_t n, int64_t heads, int64_t nq, size_t* ws_bytes);
 /* Attention output over quantized values: for head h, query i < nq and
  * weights P[h][i][n] (fp32, device; e.g. the softmax of qtq_logits),
@@ -310,6 +312,15 @@ int qgemv_binlr_noalloc(const void* ubits, const void* vtbits, const uint16_t* s
                         const uint16_t* s2, int64_t N, int64_t K, int64_t r,
                         const void* x, int x_dtype, int64_t B, void* y, int y_dtype,
                         hipStream_t stream);
+
+/* ------------------------------------------------------------ measurement
+ * Reference for the decode kernels' bandwidth ("AirLLM corre un modelo
+ * 70B...", "Por qué es lento": time per token ~ bytes / read speed): read
+ * buf (device, 16-byte aligned, bytes a multiple of 16) once with 16-byte
+ * nontemporal loads, as a plain read-only stream; *out (device, 4-byte
+ * aligned) is written only in the unlikely case that the xor of all words
+ * equals 0x9E3779B9, so callers pass a scratch word.  Asynchronous. */
+int qstream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream);
 
 /* --------------------------------------------------------------- prefill */
 typedef struct qweight {

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 31, names
+    assert len(names) == 32, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -101,6 +101,9 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemv_binlr(good, good, good, good, 64, 128, 16, good, cg.Q_BF16, 1, good, cg.Q_F32,
                            P(0), 1 << 20, s) == cg.Q_EWORKSPACE
     assert lib.qpack_binlr(good, good, 64, 128, 0, good, good, s) == cg.Q_EINVAL
+    # streaming-read reference: sizes and alignment
+    assert lib.qstream_read(good, 100, good, s) == cg.Q_EINVAL
+    assert lib.qstream_read(odd, 128, good, s) == cg.Q_EALIGN
     # binary without a workspace argument: the scratch array's limit, nulls, alignment
     assert lib.qgemv_binlr_noalloc(good, good, good, good, 64, 128, 65536, good, cg.Q_BF16, 16, good, cg.Q_F32,
                                    s) == cg.Q_EUNSUPPORTED
