@@ -659,7 +659,7 @@ def stream_ceiling(cg, torch, dev, time_launches, log):
     torch.cuda.empty_cache()
     log(f"streaming read: {small:.0f} GB/s per 132 MB pass, {big:.0f} GB/s over 4 GiB")
     return {"read_132MB_GBps": round(small, 1), "read_4GiB_GBps": round(big, 1),
-            "method": "qstream_read (16-byte nontemporal loads, 1024x256 threads, nothing written), "
+            "method": "qstream_read (16-byte nontemporal loads, grid-stride, 2048x256 threads, nothing written), "
                       "HIP events over one graph of back-to-back passes"}
 
 
