@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void tq_prep_kernel(const float* __restrict__ 
 #define TQ_DEPTH 4    // key steps in flight per wave
 #endif
 
-template <int M>
+template <int M, bool FULLN>
 __global__ __launch_bounds__(256) void tq_logits_kernel(const uint32_t* __restrict__ codes,
                                                         const uint32_t* __restrict__ signs,
                                                         const uint32_t* __restrict__ norms, int n, int nq,
@@ -208,7 +208,6 @@ __global__ __launch_bounds__(256) void tq_logits_kernel(const uint32_t* __restri
   asm volatile("" : "+v"(smask), "+v"(sone));
   const float gk = 1.2533141373155003f / 128.0f;        // sqrt(pi/2) / d
   const float bias = 192.0f * qsum;
-  const bool vec_out = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   const size_t hk = (size_t)h * n;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes + hk * 4 * M, (uint32_t)((size_t)n * 16 * M));
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(signs + hk * 4, (uint32_t)((size_t)n * 16));
@@ -222,10 +221,13 @@ __global__ __launch_bounds__(256) void tq_logits_kernel(const uint32_t* __restri
     buf_load_unit<M>(crs, ok ? u * (M * 4) : 0xFFFFFF00u, 0u, rw.c);
     rw.s = buf_load_u32(srs, ok ? u * 4 : 0xFFFFFF00u, 0u);
     // the norms of keys 4 kg .. 4 kg + 3 (the rows of D this lane holds): one
-    // 16-byte load when all four are present, per key in a partial last group
+    // 16-byte load when the key count is a multiple of 4 (a group is then
+    // whole or wholly past n), else one load per key.  The form is fixed per
+    // instance, never chosen per lane, so every step issues the same number
+    // of loads and the waits before a step's decode cover exactly its loads.
     const int k0 = base + 4 * kg;
-    if (k0 + 3 < n) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(nrs, (uint32_t)k0 * 4, 0u, kNT);
+    if constexpr (FULLN) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(nrs, k0 < n ? (uint32_t)k0 * 4 : 0xFFFFFF00u, 0u, kNT);
       rw.nm[0] = v[0]; rw.nm[1] = v[1]; rw.nm[2] = v[2]; rw.nm[3] = v[3];
     } else {
 #pragma unroll
@@ -263,8 +265,8 @@ __global__ __launch_bounds__(256) void tq_logits_kernel(const uint32_t* __restri
         const float nrm = f16_bits_to_f32(rw.nm[i] & 0xFFFFu), g = f16_bits_to_f32(rw.nm[i] >> 16) * gk;
         v[i] = nrm * (delta * (dm[i] - bias) + g * ds[i]);
       }
-      if (vec_out && k0 + 3 < n) {   // rows 16-byte aligned (n % 4 == 0): one store of 4 keys
-        *reinterpret_cast<f32x4_t*>(orow + k0) = f32x4_t{v[0], v[1], v[2], v[3]};
+      if constexpr (FULLN) {   // rows 16-byte aligned (n % 4 == 0, out aligned): one store of 4 keys
+        if (k0 < n) *reinterpret_cast<f32x4_t*>(orow + k0) = f32x4_t{v[0], v[1], v[2], v[3]};
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -309,7 +311,7 @@ constexpr int kTqPart = 129;             // floats per (workgroup, query): 128 s
 constexpr int kTqVPitch = 20;            // u16 per coordinate row of a wave's value tile (8-byte aligned rows)
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-template <int M>
+template <int M, bool FULLN>
 __global__ __launch_bounds__(256) void tq_attend_kernel(const uint32_t* __restrict__ codes,
                                                         const uint32_t* __restrict__ norms, int n, int nq,
                                                         const float* __restrict__ P, uint4 tab,
@@ -337,11 +339,14 @@ __global__ __launch_bounds__(256) void tq_attend_kernel(const uint32_t* __restri
     const uint32_t u = (uint32_t)key * 4 + (uint32_t)kg;
     buf_load_unit<M>(crs, key < n ? u * (M * 4) : 0xFFFFFF00u, 0u, rw.c);
     // norms and weights of values 4 kg .. 4 kg + 3: one 16-byte load each when
-    // all four are present, per value in a partial last group
+    // the value count is a multiple of 4 (a group is then whole or wholly
+    // past n), else one load per value; fixed per instance, so every step
+    // issues the same number of loads.
     const int k0 = base + 4 * kg;
-    if (k0 + 3 < n) {
-      const auto vn = __builtin_amdgcn_raw_buffer_load_b128(nrs, (uint32_t)k0 * 4, 0u, kNT);
-      const auto vp = __builtin_amdgcn_raw_buffer_load_b128(prs, (uint32_t)k0 * 4, 0u, 0);
+    if constexpr (FULLN) {
+      const uint32_t off = k0 < n ? (uint32_t)k0 * 4 : 0xFFFFFF00u;
+      const auto vn = __builtin_amdgcn_raw_buffer_load_b128(nrs, off, 0u, kNT);
+      const auto vp = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0u, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) { rw.nm[i] = vn[i]; rw.p[i] = vp[i]; }
     } else {
@@ -482,14 +487,23 @@ hipError_t launch_tq_attend(const uint32_t* codes, const uint32_t* norms, int64_
   const int64_t nb = tq_attend_blocks(n, heads), nch = (nq + 15) / 16;
   const dim3 grid((unsigned)nb, (unsigned)heads, (unsigned)nch);
   const uint4 t4{tab[0], tab[1], tab[2], tab[3]};
-  if (mbits == 2)
-    hipLaunchKernelGGL((tq_attend_kernel<2>), grid, dim3(256), 0, s, codes, norms, (int)n, (int)nq, P, t4, part);
-  else if (mbits == 3)
-    hipLaunchKernelGGL((tq_attend_kernel<3>), grid, dim3(256), 0, s, codes, norms, (int)n, (int)nq, P, t4, part);
-  else if (mbits == 4)
-    hipLaunchKernelGGL((tq_attend_kernel<4>), grid, dim3(256), 0, s, codes, norms, (int)n, (int)nq, P, t4, part);
-  else
+  // weight rows 16-byte aligned when n % 4 == 0 and P is
+  const bool full = n % 4 == 0 && (reinterpret_cast<uintptr_t>(P) & 15) == 0;
+#define TQA(MB, F) \
+  hipLaunchKernelGGL((tq_attend_kernel<MB, F>), grid, dim3(256), 0, s, codes, norms, (int)n, (int)nq, P, t4, part)
+  if (mbits == 2) {
+    if (full) TQA(2, true);
+    else TQA(2, false);
+  } else if (mbits == 3) {
+    if (full) TQA(3, true);
+    else TQA(3, false);
+  } else if (mbits == 4) {
+    if (full) TQA(4, true);
+    else TQA(4, false);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef TQA
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tq_attend_finish_kernel, dim3((unsigned)heads, (unsigned)nq), dim3(256), 0, s, part, (int)nb,
@@ -518,12 +532,18 @@ hipError_t launch_tq_logits(const uint32_t* codes, const uint32_t* signs, const 
   if (per_head > need) per_head = need;
   if (per_head < 1) per_head = 1;
   const dim3 grid((unsigned)per_head, (unsigned)heads, (unsigned)((nq + 15) / 16));
-  if (mbits == 2)
-    hipLaunchKernelGGL((tq_logits_kernel<2>), grid, dim3(256), 0, s, codes, signs, norms, (int)n, (int)nq, delta,
-                       tab_lo, tab_hi, ws, out);
-  else
-    hipLaunchKernelGGL((tq_logits_kernel<3>), grid, dim3(256), 0, s, codes, signs, norms, (int)n, (int)nq, delta,
-                       tab_lo, tab_hi, ws, out);
+  const bool full = n % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+#define TQL(MB, F)                                                                                             \
+  hipLaunchKernelGGL((tq_logits_kernel<MB, F>), grid, dim3(256), 0, s, codes, signs, norms, (int)n, (int)nq, delta, \
+                     tab_lo, tab_hi, ws, out)
+  if (mbits == 2) {
+    if (full) TQL(2, true);
+    else TQL(2, false);
+  } else {
+    if (full) TQL(3, true);
+    else TQL(3, false);
+  }
+#undef TQL
   return hipGetLastError();
 }
 

@@ -143,6 +143,22 @@ def summarize(trace_dir, fetch_dir, write_dir, kernel, alg_bytes, skip=0, take=0
     return out
 
 
+def counter_table(counter_dirs, kernel, grid=None, skip=0, take=0):
+    """{counter: median per dispatch} over dispatches [skip, skip + take) of
+    `kernel` (all after `skip` when take is 0), from one or more counter runs."""
+    out = {}
+    for d in counter_dirs:
+        rows = _csv(os.path.join(d, "**", "*counter_collection.csv"))
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
+        by = {}
+        for r in rows:
+            if kernel in r["Kernel_Name"] and (grid is None or _grid(r) == grid):
+                by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for name, vals in by.items():
+            out[name] = statistics.median(_window(vals, skip, take))
+    return out
+
+
 def _kernel_spec(spec):
     """NAME=BYTES[@GRID][+SKIP][:TAKE] -> (name, bytes, grid, skip, take)."""
     name, rest = spec.rsplit("=", 1)
@@ -168,6 +184,8 @@ def main():
     ap.add_argument("--kernel", action="append", default=[],
                     help="NAME=BYTES[@GRID][+SKIP][:TAKE]: substring of the kernel name, algorithmic bytes per "
                          "dispatch, optional grid (total work-items, e.g. 262144), dispatches skipped and taken (the timed region)")
+    ap.add_argument("--counters", action="append", default=[],
+                    help="rocprofv3 --pmc output directory with other counters (median per dispatch is reported)")
     ap.add_argument("--sha", default="")
     ap.add_argument("--title", default="")
     ap.add_argument("--commands", default="", help="text block with the rocprofv3 commands")
@@ -199,6 +217,9 @@ def main():
                   f"- algorithmic bytes per launch: {int(nbytes)}",
                   f"- achieved (algorithmic bytes / mean duration): {s['achieved_gbs']:.1f} GB/s "
                   f"(median: {s['achieved_gbs_median']:.1f} GB/s)"]
+        if a.counters:
+            ct = counter_table(a.counters, name, grid, skip, take)
+            lines += [f"- {k} (median per dispatch): {v:.6g}" for k, v in sorted(ct.items())]
         if "traffic_bytes" in s:
             lines += [f"- FETCH_SIZE median per dispatch: {s['fetch_kib']:.1f} KiB; 1 GiB copy reads "
                       f"{s['copy_fetch_kib']:.1f} KiB -> scale {s['fetch_scale']:.5f} bytes/KiB-unit",

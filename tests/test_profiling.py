@@ -70,3 +70,9 @@ def test_kernel_spec():
     assert pf._kernel_spec("gemv_b1_kernel<4, 64=132120576@1024+25:20") == (
         "gemv_b1_kernel<4, 64", 132120576.0, "1024", 25, 20)
     assert pf._kernel_spec("bin_mfma_kernel<2=100") == ("bin_mfma_kernel<2", 100.0, None, 0, 0)
+
+
+def test_counter_table(tmp_path):
+    _counters(str(tmp_path / "c"), 100.0, 1.0)
+    t = pf.counter_table([str(tmp_path / "c")], "A<4, 64>", grid="64", skip=1, take=3)
+    assert t == {"C": 102.0}
