@@ -86,6 +86,9 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemv_group(good, good, 64, 128, 4, 32, good, cg.Q_BF16, 17, good, cg.Q_F32, s) == cg.Q_EINVAL
     # misaligned codes
     assert lib.qgemv_group(odd, good, 64, 128, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EALIGN
+    # x must be 16-byte aligned (the header's rule); y 4-byte aligned is enough
+    assert lib.qgemv_group(good, good, 64, 128, 4, 32, odd, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EALIGN
+    assert lib.qgemv_group(good, good, 64, 128, 4, 32, P(0x10008), cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EALIGN
     # unsupported: fp32 activations with B > 1, K beyond the register-resident limit
     assert lib.qgemv_group(good, good, 64, 128, 4, 32, good, cg.Q_F32, 2, good, cg.Q_F32, s) == cg.Q_EUNSUPPORTED
     assert lib.qgemv_group(good, good, 64, 131072, 4, 32, good, cg.Q_BF16, 1, good, cg.Q_F32, s) == cg.Q_EUNSUPPORTED
