@@ -378,7 +378,7 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 // staged in LDS first).
 // CB: codes read through per-group books; the pairs of decode_unit_cb give
 // e[q] exactly and one fma per weight gives fl32(s 2^(b-7) e[q] + o).
-template <int BITS, int G, int RT, int WPB, bool OUT, bool CB = false>
+template <int BITS, int G, int RT, int WPB, bool OUT, bool CB = false, bool SPLITW = true>
 __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
     const uint16_t* __restrict__ x, int B, void* __restrict__ yout, int y_bf16,
@@ -472,18 +472,20 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // w_hat = hi + lo, both bf16 (2^-16 relative residual): two MFMAs
+        // SPLITW: w_hat = hi + lo, both bf16 (2^-16 relative residual), two
+        // MFMAs; else w_hat rounded once to bf16 (nearest even), one MFMA
         u32x4_t hi, lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float w0 = wv[8 * j + 2 * e], w1 = wv[8 * j + 2 * e + 1];
           hi[e] = cvt_pk_bf16(w0, w1);
-          lo[e] = cvt_pk_bf16(w0 - bf16_lo_to_f32(hi[e]), w1 - bf16_hi_to_f32(hi[e]));
+          if constexpr (SPLITW) lo[e] = cvt_pk_bf16(w0 - bf16_lo_to_f32(hi[e]), w1 - bf16_hi_to_f32(hi[e]));
         }
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
                                                          __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo),
-                                                         __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
+        if constexpr (SPLITW)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo),
+                                                           __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
       }
     }
   };
@@ -581,26 +583,43 @@ static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t
   return hipGetLastError();
 }
 
+// Reductions of at least this many inputs take the weights as one bf16
+// operand; shorter ones as bf16 hi + lo (the error argument is given with
+// the tile choice below).
+constexpr int64_t kGemvSplitBelowK = 512;
+
 template <int BITS, int G, int RT, int WPB, bool CB = false>
 static hipError_t gemv_mfma_launch(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
                                    const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s, Side sd,
                                    Books bk = Books{nullptr, nullptr, 0}) {
   const int64_t tiles = (N + 16 * RT - 1) / (16 * RT);
-  if constexpr (CB)
-    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, false, true>), dim3((unsigned)tiles), dim3(64 * WPB), 0,
-                       s, codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16, nullptr, nullptr, 0, bk);
-  else if (sd.n > 0)
-    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, true>), dim3((unsigned)tiles), dim3(64 * WPB), 0, s,
-                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16, sd.vals, sd.idx, sd.n, bk);
-  else
-    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, false>), dim3((unsigned)tiles), dim3(64 * WPB), 0, s,
-                       codes, meta, (int)N, (int)K, x, (int)B, y, y_bf16, nullptr, nullptr, 0, bk);
+  const dim3 grid((unsigned)tiles), block(64 * WPB);
+#define MF(O, C, S, SV, SI, SN)                                                                               \
+  hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, O, C, S>), grid, block, 0, s, codes, meta, (int)N, (int)K, \
+                     x, (int)B, y, y_bf16, SV, SI, SN, bk)
+  const bool split = K < kGemvSplitBelowK;
+  if constexpr (CB) {
+    if (split) MF(false, true, true, nullptr, nullptr, 0);
+    else MF(false, true, false, nullptr, nullptr, 0);
+  } else if (sd.n > 0) {
+    if (split) MF(true, false, true, sd.vals, sd.idx, sd.n);
+    else MF(true, false, false, sd.vals, sd.idx, sd.n);
+  } else {
+    if (split) MF(false, false, true, nullptr, nullptr, 0);
+    else MF(false, false, false, nullptr, nullptr, 0);
+  }
+#undef MF
   return hipGetLastError();
 }
 
 // Tile choice, measured on MI355X at B = 2..16: row tiles per wave (reuse of
 // the activation fragments) RT = 4 for N >= 16384, 2 for N >= 4096, else 1;
 // 4 waves split K.  QG_MB_RT / QG_MB_WPB force one choice.
+// Weight operand: rounding w_hat once to bf16 (unit roundoff 2^-8) moves a
+// product by at most 2^-8 sum |w_hat||x| in the worst case, and by about
+// 2^-8 / sqrt(3K) of it when the rounding errors are independent (below
+// 1e-4 of the bound at K >= 512); for K < 512 the hi + lo split keeps every
+// shape far inside the 2e-3 budget.
 #ifndef QG_MB_RT
 #define QG_MB_RT 0
 #endif
