@@ -173,13 +173,14 @@ struct TileSmall { static constexpr int TM = 128, TN = 256, TK = 64, WM = 2, WN 
 // 8 waves of 64 x 128: two waves per SIMD, so one wave's MFMAs run while the
 // other waits at the step barrier or on its LDS reads (measured on MI355X
 // against 4 waves of 128 x 128, 2 x 4 waves and 2-6 VALU per MFMA: ~10 %
-// faster at M = 512 and 4096 for RTN and binary weights, although each step
-// reads 50 % more LDS fragments).
+// faster at M = 512 and 4096 for RTN, binary and codebook weights, although
+// each step reads 50 % more LDS fragments).  At 3 VALU per MFMA the plain,
+// binary and codebook decoders fit the 256 registers a wave has at two waves
+// per SIMD (4 made the codebook decoder spill).
 struct TileBig   { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 4, WN = 2, VPM = QG_BIG_VPM; };   // 8 waves, 64 x 128
-// The same block on 4 waves of 128 x 128 (one per SIMD), for decoders whose
-// lookups do not fit the 256 registers of a wave at two waves per SIMD (the
-// codebook decoder would spill).
-struct TileBig4  { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 2, WN = 2, VPM = 3; };   // 4 waves, 128 x 128
+// The outlier instances (one more K-step for the side columns) fit their
+// registers at 4 VALU per MFMA (3 made the 5- and 6-bit ones spill).
+struct TileBigO  { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 4, WN = 2, VPM = 4; };
 // Split precision (short reductions): one operand is carried as bf16 hi + lo
 // tiles, so the LDS holds three tiles per buffer; a smaller block keeps them
 // within the LDS.
@@ -513,8 +514,8 @@ static hipError_t gemm_run(const void* A, int64_t lda, int64_t M, int64_t Kact, 
                                                                  y_bf16, s, sc);
   } else {
     if (use_big_tile(M, N)) {
-      if constexpr (Dec::kDictWords > 0)
-        return gemm_launch<Dec, AMODE, KMASK, TileBig4, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
+      if constexpr (OUTL)
+        return gemm_launch<Dec, AMODE, KMASK, TileBigO, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
                                                               s, sc);
       else
         return gemm_launch<Dec, AMODE, KMASK, TileBig, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
