@@ -485,24 +485,36 @@ static hipError_t gemm_launch(const void* A, int64_t lda, int64_t M, int64_t Kac
 // (~2^-8 / sqrt(3K) of sum |w||x|) but can reach 2^-8 for short ones.
 constexpr int64_t kSplitBelowK = 512;
 
-// Either tile runs one workgroup per CU, and a 256 x 256 tile takes about
-// 7/4 the time of a 128 x 256 one (fewer LDS reads and barriers per MFMA),
-// so the choice compares whole rounds of workgroups over the CUs: the big
-// tile wins once it has enough tiles to fill the GPU, the small one when
-// its extra parallelism saves a round (short M, or the narrow first pass of
-// the binary path).
+// The two larger tiles run one workgroup per CU, the 64 x 128 tile two (its
+// LDS allows two).  Counting a round as one tile per CU, a round of
+// 256 x 256 tiles takes about 7/4 the time of a round of 128 x 256 ones and
+// 7/2 that of a round of 64 x 128 ones (fewer LDS reads and barriers per
+// MFMA in the larger tiles), so the choice compares whole rounds of tiles
+// over the CUs: the big tile wins once
+// it has enough tiles to fill the GPU, the smaller ones when their extra
+// parallelism saves rounds (short M, narrow N such as k/v projections, the
+// narrow first pass of the binary path).  Measured on MI355X over M = 64,
+// 512, 4096 and N = 1024, 8192, 28672 (K = 8192): the model picks the
+// fastest tile or one within 4 % of it; at equal cost the 64 x 128 tile
+// measured faster than the 128 x 256 one.
 #ifndef QG_GEMM_TILE
-#define QG_GEMM_TILE 0    // 0 = by cost, 1 = small, 2 = big
+#define QG_GEMM_TILE 0    // 0 = by cost, 1 = small, 2 = big, 3 = 64 x 128
 #endif
-static bool use_big_tile(int64_t M, int64_t N) {
-  if (QG_GEMM_TILE) return QG_GEMM_TILE == 2;
+#ifndef QG_TINY_COST
+#define QG_TINY_COST 2    // time of one round of 64 x 128 tiles, in the units of the model below
+#endif
+enum class TileChoice { Small, Big, Tiny };
+static TileChoice pick_tile(int64_t M, int64_t N) {
+  if (QG_GEMM_TILE) return QG_GEMM_TILE == 2 ? TileChoice::Big : (QG_GEMM_TILE == 3 ? TileChoice::Tiny : TileChoice::Small);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  const int64_t nbig = ((M + TileBig::TM - 1) / TileBig::TM) * ((N + TileBig::TN - 1) / TileBig::TN);
-  const int64_t nsmall = ((M + TileSmall::TM - 1) / TileSmall::TM) * ((N + TileSmall::TN - 1) / TileSmall::TN);
-  return 7 * ((nbig + cus - 1) / cus) <= 4 * ((nsmall + cus - 1) / cus);
+  auto rounds = [&](int tm, int tn) { return (((M + tm - 1) / tm) * ((N + tn - 1) / tn) + cus - 1) / cus; };
+  const int64_t cbig = 7 * rounds(TileBig::TM, TileBig::TN), csmall = 4 * rounds(TileSmall::TM, TileSmall::TN);
+  const int64_t ctiny = QG_TINY_COST * rounds(TileSplit::TM, TileSplit::TN);
+  if (cbig <= csmall && cbig <= ctiny) return TileChoice::Big;
+  return csmall < ctiny ? TileChoice::Small : TileChoice::Tiny;
 }
 
 template <typename Dec, int AMODE, bool KMASK, bool OUTL = false, bool SPLIT = false>
@@ -513,7 +525,8 @@ static hipError_t gemm_run(const void* A, int64_t lda, int64_t M, int64_t Kact, 
     return gemm_launch<Dec, AMODE, KMASK, TileSplit, OUTL, true>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy,
                                                                  y_bf16, s, sc);
   } else {
-    if (use_big_tile(M, N)) {
+    const TileChoice tc = pick_tile(M, N);
+    if (tc == TileChoice::Big) {
       if constexpr (OUTL)
         return gemm_launch<Dec, AMODE, KMASK, TileBigO, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
                                                               s, sc);
@@ -521,6 +534,9 @@ static hipError_t gemm_run(const void* A, int64_t lda, int64_t M, int64_t Kact, 
         return gemm_launch<Dec, AMODE, KMASK, TileBig, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
                                                              s, sc);
     }
+    if (tc == TileChoice::Tiny)
+      return gemm_launch<Dec, AMODE, KMASK, TileSplit, OUTL, false>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy,
+                                                                    y_bf16, s, sc);
     return gemm_launch<Dec, AMODE, KMASK, TileSmall, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
                                                            s, sc);
   }

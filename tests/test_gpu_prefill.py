@@ -137,7 +137,7 @@ def test_big_tile_rtn_ragged(gpu):
 
 def test_big_tile_binlr_ragged(gpu):
     """The second pass (M x N) takes the 256 x 256 tile with its masked K
-    tail (r % 8 != 0); the first (M x r) takes the 128 x 256 one."""
+    tail (r % 8 != 0); the first (M x r) takes the 64 x 128 one."""
     M, N, K, r = 4000, 7900, 3000, 1001
     say(f"prefill big-tile binary M={M} N={N} K={K} r={r}")
     U, V, s1, s2 = gen_binlr(N, K, r, rng_for(78, 0))
@@ -151,4 +151,39 @@ def test_big_tile_binlr_ragged(gpu):
     Xv = oracle.product.bf16_to_f64(X[rows])
     err = check_err(Y[np.ix_(rows, cols)], oracle.product.matmul_ref(W, Xv),
                     oracle.product.binlr_abs_denominator(U[cols], V, s1[cols], s2, Xv))
+    say(f"  err={err:.3e}")
+
+
+def test_small_tile_rtn_ragged(gpu):
+    """With 256 CUs this shape takes the 128 x 256 tile (218 tiles in one
+    round, against 109 slower 256 x 256 tiles or four rounds of 64 x 128
+    ones), with ragged M and N."""
+    M, N, K = 250, 27900, 1024
+    say(f"prefill small-tile RTN M={M} N={N} K={K}")
+    W = gen_weights(N, K, rng_for(80, 0), outliers=True)
+    codes, meta = gpu.qpack_group(dev(W), 4, 64)
+    X = gen_x_bf16(M, K, rng_for(81, 0))
+    Y = host(gpu.qgemm_prefill(gpu.make_qweight_group(codes, meta, N, K, 4, 64), dev_bf16(X)))
+    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], np.random.default_rng(13).choice(M, 12, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, N - 1], np.random.default_rng(14).choice(N, 40, replace=False)]))
+    _, _, _, _, _, W_hat = group_reference(W[cols], 4, 64)
+    Xv = oracle.product.bf16_to_f64(X[rows])
+    err = check_err(Y[np.ix_(rows, cols)], oracle.product.matmul_ref(W_hat, Xv),
+                    oracle.product.abs_denominator(W_hat, Xv))
+    say(f"  err={err:.3e}")
+
+
+def test_tiny_tile_rtn_half_step(gpu):
+    """Short M and narrow N take the 64 x 128 tile; K = 1056 (single bf16
+    weights) ends on half a 64-wide step, one 32-code unit per row.  Every
+    output is checked."""
+    M, N, K = 100, 1000, 1056
+    say(f"prefill tiny-tile RTN M={M} N={N} K={K}")
+    W = gen_weights(N, K, rng_for(82, 0), outliers=True)
+    codes, meta = gpu.qpack_group(dev(W), 5, 32)
+    X = gen_x_bf16(M, K, rng_for(83, 0))
+    Y = host(gpu.qgemm_prefill(gpu.make_qweight_group(codes, meta, N, K, 5, 32), dev_bf16(X)))
+    _, _, _, _, _, W_hat = group_reference(W, 5, 32)
+    Xv = oracle.product.bf16_to_f64(X)
+    err = check_err(Y, oracle.product.matmul_ref(W_hat, Xv), oracle.product.abs_denominator(W_hat, Xv))
     say(f"  err={err:.3e}")
