@@ -4,20 +4,22 @@
 // Prefill multiplies many token rows by the same weights, so unlike decode it
 // is a dense contraction (arithmetic intensity of thousands of flops per
 // weight byte) and belongs on the matrix cores.  A workgroup owns a TM x TN
-// (tokens x outputs) tile, 128 x 256 with 8 waves or 256 x 256 with 4 waves,
-// and walks K in steps of TK = 64:
-//   * the X tile (bf16, optionally scaled by s2 and re-rounded) and the
-//     decoded weight tile (bf16) are staged in LDS with a padded row pitch of
-//     TK + 8 elements, so the 16-byte fragment reads of consecutive rows hit
-//     distinct banks; two LDS buffers and two register stages: while the
-//     matrix cores work on step i, the raw loads of step i+2 are in flight
-//     and step i+1 is decoded and stored into the other LDS buffer, one
-//     barrier per step;
+// (tokens x outputs) tile, 256 x 256 or 128 x 256 with 8 waves or 64 x 128
+// with 4, and walks K in steps of TK = 64:
+//   * the decoded weight tile (bf16) is staged in LDS with a padded row pitch
+//     of TK + 8 elements, so the 16-byte fragment reads of consecutive rows
+//     hit distinct banks; a plain bf16 X tile goes from memory straight into
+//     LDS (unpadded rows, chunks placed by an XOR of the row so reads stay
+//     conflict-free), an X tile scaled by s2 (binary first pass) or split
+//     into hi + lo passes through registers; two LDS buffers: while the
+//     matrix cores work on step i, the raw weight loads of a later step are
+//     in flight and step i+1 is decoded and stored into the other buffer,
+//     one barrier per step;
 //   * every thread decodes one or two 32-weight units per step: group RTN
 //     unit -> fp16 subnormal q*2^(p-24) -> v_fma_mix_f32 s*q + o -> bf16
 //     (round to nearest even); binary word -> +-1 (exact);
-//   * each wave runs a 64 x 64 or 128 x 128 block of v_mfma_f32_32x32x16_bf16
-//     tiles per 16-wide k slice, fp32 accumulation;
+//   * each wave runs a 32 x 64, 64 x 64 or 64 x 128 block of
+//     v_mfma_f32_32x32x16_bf16 tiles per 16-wide k slice, fp32 accumulation;
 //   * workgroups are numbered so that the 8 XCDs each take a contiguous run
 //     of tiles, N fastest: the concurrent tiles of one XCD share their X rows
 //     in that XCD's L2.
@@ -167,6 +169,9 @@ struct TileSmall { static constexpr int TM = 128, TN = 256, TK = 64, WM = 2, WN 
 #ifndef QG_BIG_TK
 #define QG_BIG_TK 64
 #endif
+#ifndef QG_DIRECT_A
+#define QG_DIRECT_A 1     // bf16 X tiles loaded straight into LDS
+#endif
 #ifndef QG_BIG_VPM
 #define QG_BIG_VPM 3
 #endif
@@ -181,6 +186,14 @@ struct TileBig   { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM =
 // The outlier instances (one more K-step for the side columns) fit their
 // registers at 4 VALU per MFMA (3 made the 5- and 6-bit ones spill).
 struct TileBigO  { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 4, WN = 2, VPM = 4; };
+// The codebook decoder's byte-permute lookups are longer VALU chains: 6 VALU
+// per MFMA (registers to spare once the X tile skips the registers) measured
+// ~5 % faster than 3 at M = 512 and 4096; the other decoders gain nothing
+// from more.
+#ifndef QG_BIGC_VPM
+#define QG_BIGC_VPM 6
+#endif
+struct TileBigC  { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 4, WN = 2, VPM = QG_BIGC_VPM; };
 // Split precision (short reductions): one operand is carried as bf16 hi + lo
 // tiles, so the LDS holds three tiles per buffer; a smaller block keeps them
 // within the LDS.
@@ -215,10 +228,21 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   constexpr int AC = TM * (TK / 8) / NT;              // 8-element X chunks per thread and step
   constexpr int WU = TN * UPR / NT;                   // weight units per thread and step
   static_assert(AC >= 1 && WU >= 1 && NT % (TK / 8) == 0, "tile configuration");
-  // per LDS buffer: A tile [, A lo tile], B tile [, B lo tile]
-  constexpr int AOFF_LO = TM * LP, BOFF = (SPA ? 2 : 1) * TM * LP, BOFF_LO = BOFF + TN * LP;
-  constexpr int BUF = BOFF + (SPB ? 2 : 1) * TN * LP;
-  __shared__ __align__(16) uint16_t lds[2][BUF];
+  // DIRECT: the bf16 X tile goes from memory straight into LDS (buffer
+  // loads with the LDS flag, no trip through registers), in unpadded rows of
+  // TK elements whose 16-byte chunk c sits at slot c ^ (row % 8), so the
+  // fragment reads below stay free of bank conflicts.
+  constexpr bool DIRECT = QG_DIRECT_A && AMODE == 0 && !KMASK && !SPLIT && !OUTL;
+  constexpr int AP = DIRECT ? TK : LP;                       // A row pitch
+  // per buffer: A tile [, A lo tile] and B tile [, B lo tile], A and B in
+  // separate arrays (the compiler then knows that reads of one buffer do not
+  // wait on direct loads into the other)
+  constexpr int AOFF_LO = TM * AP, ABUF = (SPA ? 2 : 1) * TM * AP;
+  constexpr int BOFF_LO = TN * LP, BBUF = (SPB ? 2 : 1) * TN * LP;
+  __shared__ __align__(16) uint16_t lds_a0[ABUF];
+  __shared__ __align__(16) uint16_t lds_a1[ABUF];
+  __shared__ __align__(16) uint16_t lds_b[2][BBUF];
+  static_assert(!DIRECT || (TK == 64 && AC * (NT / 64) * 8 == TM), "direct X tiles: 1 KB (8 rows) per load");
   __shared__ __align__(16) uint32_t dict_lds[Dec::kDictWords > 0 ? Dec::kDictWords : 1];
   const int tid = threadIdx.x;
   if constexpr (Dec::kDictWords > 0) dec.bind(dict_lds, tid, NT);   // staged before the first decode
@@ -252,7 +276,7 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   auto gload = [&](int step, Stage& st) {
     const int k = step * TK + ac;
 #pragma unroll
-    for (int i = 0; i < AC; ++i) {
+    for (int i = 0; i < (DIRECT ? 0 : AC); ++i) {
       const uint32_t off = k < Kact ? (uint32_t)(((size_t)(ar + AROWS * i) * lda + k) * ESZ) : 0xFFFFFFE0u;
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0);
       st.a[i] = u32x4_t{v[0], v[1], v[2], v[3]};
@@ -273,8 +297,8 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   };
   // scale (AMODE 1), decode and store one K-step into an LDS buffer
   auto lstore = [&](int step, Stage& st, int buf) {
-    uint16_t* As = lds[buf];
-    uint16_t* Bs = lds[buf] + BOFF;
+    uint16_t* As = buf ? lds_a1 : lds_a0;
+    uint16_t* Bs = lds_b[buf];
     if constexpr (KMASK) {
       const int k = step * TK + ac;
       if constexpr (AMODE == 2) {
@@ -294,9 +318,10 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
       }
     }
     if constexpr (AMODE == 0) {
+      if constexpr (!DIRECT)
 #pragma unroll
-      for (int i = 0; i < AC; ++i)
-        *reinterpret_cast<u32x4_t*>(As + (ar + AROWS * i) * LP + ac) = st.a[i];
+        for (int i = 0; i < AC; ++i)
+          *reinterpret_cast<u32x4_t*>(As + (ar + AROWS * i) * LP + ac) = st.a[i];
     } else {
 #pragma unroll
       for (int i = 0; i < AC; ++i) {
@@ -330,7 +355,7 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
       if constexpr (SPB) {
         float wv[32];
         dec.decode_f32(st.w[j], wv);
-        u32x4_t* dlo = reinterpret_cast<u32x4_t*>(lds[buf] + BOFF_LO + (idx / UPR) * LP + (idx % UPR) * 32);
+        u32x4_t* dlo = reinterpret_cast<u32x4_t*>(lds_b[buf] + BOFF_LO + (idx / UPR) * LP + (idx % UPR) * 32);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           u32x4_t hi, lo;
@@ -357,16 +382,21 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   constexpr int WTM = TM / Cfg::WM, WTN = TN / Cfg::WN;
   constexpr int NA = SPA ? 2 : 1, NB = SPB ? 2 : 1;   // A and B tiles (hi [, lo])
   auto mfma_step = [&](int buf) {
-    const uint16_t* As = lds[buf];
-    const uint16_t* Bs = lds[buf] + BOFF;
+    const uint16_t* As = buf ? lds_a1 : lds_a0;
+    const uint16_t* Bs = lds_b[buf];
     // fragments of k-slice s+1 are read before the MFMAs of slice s
     bf16x8_t af[2][NA][FI], bfr[2][NB][FJ];
     auto rd = [&](int kk, bf16x8_t (&a)[NA][FI], bf16x8_t (&b)[NB][FJ]) {
 #pragma unroll
       for (int h = 0; h < NA; ++h)
 #pragma unroll
-        for (int i = 0; i < FI; ++i)
-          a[h][i] = *reinterpret_cast<const bf16x8_t*>(As + h * AOFF_LO + (wm * WTM + i * 32 + fr) * LP + kk + fk);
+        for (int i = 0; i < FI; ++i) {
+          const int row = wm * WTM + i * 32 + fr;
+          if constexpr (DIRECT)
+            a[h][i] = *reinterpret_cast<const bf16x8_t*>(As + row * TK + 8 * (((kk + fk) >> 3) ^ (fr & 7)));
+          else
+            a[h][i] = *reinterpret_cast<const bf16x8_t*>(As + h * AOFF_LO + row * LP + kk + fk);
+        }
 #pragma unroll
       for (int h = 0; h < NB; ++h)
 #pragma unroll
@@ -396,8 +426,35 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
   // store step s+1 (loaded one step earlier) into the other buffer, with the
   // decode interleaved between the MFMAs.  Steps past the end load zeros and
   // store into a buffer nobody reads.
+  // DIRECT: the X tile of one step into an A buffer.  Wave w's load i
+  // fills 1 KB of it, rows 8 (w AC + i) .. +7; lane l takes row l / 8 of
+  // those and slot l % 8, i.e. chunk (l % 8) ^ (row % 8) of that row.
+  // Rows past M and chunks at or past Kact read 0 (out-of-range offsets).
+  auto adirect = [&](int step, int buf) {
+    if constexpr (DIRECT) {
+      uint16_t* base = buf ? lds_a1 : lds_a0;
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+      for (int i = 0; i < AC; ++i) {
+        const int blk = wv * AC + i, r = blk * 8 + (lane >> 3);
+        const int k = step * TK + 8 * ((lane & 7) ^ (r & 7));
+        const uint32_t off = k < Kact ? (uint32_t)(((size_t)r * lda + k) * 2) : 0xFFFFFFE0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (__attribute__((address_space(3))) void*)(base + blk * 512), 16,
+                                                 off, 0, 0, 0);
+      }
+    }
+  };
+  // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum): this
+  // wave's direct loads have landed in LDS before the barrier
+  auto adirect_wait = [&]() {
+    if constexpr (DIRECT) __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
   auto half = [&](int step, Stage& ld, Stage& st, int cur) {
+    adirect(step + 1, cur ^ 1);
     gload(step + 2, ld);
+    // DIRECT waits for every load before the barrier, so the raw loads of
+    // step s+2 go out first and have the whole step to arrive
+    if constexpr (DIRECT) __builtin_amdgcn_sched_barrier(0);
     mfma_step(cur);
     lstore(step + 1, st, cur ^ 1);
 #pragma unroll
@@ -405,14 +462,17 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, Cfg::VPM, 0);   // VALU
     }
+    adirect_wait();
     __syncthreads();
   };
 
   Stage s0, s1;
+  adirect(0, 0);
   gload(0, s0);
   gload(1, s1);
   if constexpr (Dec::kDictWords > 0) __syncthreads();   // dictionary staged
   lstore(0, s0, 0);
+  adirect_wait();
   __syncthreads();
   // Whole pairs of steps, so the loop has one exit: with an odd step count
   // the last half-step runs on a buffer of zeros (everything loaded past the
@@ -426,8 +486,8 @@ __global__ __launch_bounds__(64 * Cfg::WM * Cfg::WN) void gemm_kernel(
     // ended at a barrier).  X is bf16 here (AMODE 0).
     static_assert(AMODE == 0, "outlier columns come with the group format");
     const uint16_t* X = static_cast<const uint16_t*>(A);
-    uint16_t* As = lds[0];
-    uint16_t* Bs = lds[0] + BOFF;
+    uint16_t* As = lds_a0;
+    uint16_t* Bs = lds_b[0];
     for (int t = tid; t < TM * TK; t += NT) {
       const int r = t / TK, c = t % TK, m = m0 + r;
       As[r * LP + c] = (c < n_out && m < M) ? X[(size_t)m * lda + oidx[c]] : (uint16_t)0;
@@ -529,6 +589,9 @@ static hipError_t gemm_run(const void* A, int64_t lda, int64_t M, int64_t Kact, 
     if (tc == TileChoice::Big) {
       if constexpr (OUTL)
         return gemm_launch<Dec, AMODE, KMASK, TileBigO, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
+                                                              s, sc);
+      else if constexpr (Dec::kDictWords > 0)
+        return gemm_launch<Dec, AMODE, KMASK, TileBigC, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
                                                               s, sc);
       else
         return gemm_launch<Dec, AMODE, KMASK, TileBig, OUTL>(A, lda, M, Kact, dec, N, kscale, oscale, Y, ldy, y_bf16,
