@@ -137,11 +137,13 @@ def test_full_gate_shape(gpu, bits):
 
 
 @pytest.mark.parametrize("bits,M,N,K", [(4, 40, 257, 512), (3, 64, 300, 1024), (2, 40, 257, 512),
-                                        (4, 4000, 7900, 1024), (4, 70, 200, 256), (3, 33, 65, 128)])
+                                        (4, 4000, 7900, 1024), (4, 250, 27900, 1024), (4, 70, 200, 256),
+                                        (3, 33, 65, 128)])
 def test_prefill(gpu, bits, M, N, K):
-    """Every tile shape: the 256 x 256 tile (M = 4000), the 128 x 256 one and
-    the split-precision kernel of short reductions (K < 512); sampled rows
-    and columns at the large size."""
+    """Every tile shape (with 256 CUs): the 256 x 256 tile (M = 4000), the
+    128 x 256 one (M = 250, N = 27900), the 64 x 128 one (the short and
+    narrow shapes) and the split-precision kernel of short reductions
+    (K < 512); sampled rows and columns."""
     say(f"codebook prefill b={bits} M={M} N={N} K={K}")
     books = _random_books(bits, 40 + bits)
     W = gen_weights(N, K, rng_for(377, M + bits), outliers=True)

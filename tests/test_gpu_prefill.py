@@ -135,10 +135,13 @@ def test_big_tile_rtn_ragged(gpu):
     say(f"  err={err:.3e}")
 
 
-def test_big_tile_binlr_ragged(gpu):
-    """The second pass (M x N) takes the 256 x 256 tile with its masked K
-    tail (r % 8 != 0); the first (M x r) takes the 64 x 128 one."""
-    M, N, K, r = 4000, 7900, 3000, 1001
+@pytest.mark.parametrize("r", [1001, 1000])
+def test_big_tile_binlr_ragged(gpu, r):
+    """The second pass (M x N) takes the 256 x 256 tile: with r % 8 != 0 its
+    masked K tail (T staged through registers), with r = 1000 the X tile
+    loaded straight into LDS, K ending mid-step; the first (M x r) takes the
+    64 x 128 one."""
+    M, N, K = 4000, 7900, 3000
     say(f"prefill big-tile binary M={M} N={N} K={K} r={r}")
     U, V, s1, s2 = gen_binlr(N, K, r, rng_for(78, 0))
     ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
