@@ -164,7 +164,8 @@ struct DecCB {
 // Tile configurations: block tile TM x TN, WM x WN waves, each wave
 // (TM/WM) x (TN/WN) on 32x32x16 MFMAs; VPM VALU instructions are interleaved
 // after each MFMA of a step.
-// TK is the K step (a multiple of 32); LDS rows are TK + 8 bf16 apart.
+// TK is the K step (a multiple of 32); weight-tile LDS rows are TK + 8 bf16
+// apart (a directly loaded X tile is unpadded, see DIRECT below).
 struct TileSmall { static constexpr int TM = 128, TN = 256, TK = 64, WM = 2, WN = 4, VPM = 6; };   // 8 waves, 64 x 64
 #ifndef QG_BIG_TK
 #define QG_BIG_TK 64
@@ -179,9 +180,9 @@ struct TileSmall { static constexpr int TM = 128, TN = 256, TK = 64, WM = 2, WN 
 // other waits at the step barrier or on its LDS reads (measured on MI355X
 // against 4 waves of 128 x 128, 2 x 4 waves and 2-6 VALU per MFMA: ~10 %
 // faster at M = 512 and 4096 for RTN, binary and codebook weights, although
-// each step reads 50 % more LDS fragments).  At 3 VALU per MFMA the plain,
-// binary and codebook decoders fit the 256 registers a wave has at two waves
-// per SIMD (4 made the codebook decoder spill).
+// each step reads 50 % more LDS fragments).  Every instance fits the 256
+// registers a wave has at two waves per SIMD; the plain and binary decoders
+// run best at 3 VALU per MFMA (4-6 measured no faster).
 struct TileBig   { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 4, WN = 2, VPM = QG_BIG_VPM; };   // 8 waves, 64 x 128
 // The outlier instances (one more K-step for the side columns) fit their
 // registers at 4 VALU per MFMA (3 made the 5- and 6-bit ones spill).
@@ -194,9 +195,10 @@ struct TileBigO  { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM =
 #define QG_BIGC_VPM 6
 #endif
 struct TileBigC  { static constexpr int TM = 256, TN = 256, TK = QG_BIG_TK, WM = 4, WN = 2, VPM = QG_BIGC_VPM; };
-// Split precision (short reductions): one operand is carried as bf16 hi + lo
-// tiles, so the LDS holds three tiles per buffer; a smaller block keeps them
-// within the LDS.
+// 64 x 128 with 4 waves: the split-precision kernel of short reductions (one
+// operand carried as bf16 hi + lo tiles, three tiles per LDS buffer, which a
+// smaller block keeps within the LDS), and the plain kernel of launches too
+// small to fill the GPU with the larger tiles (two workgroups per CU).
 struct TileSplit { static constexpr int TM = 64, TN = 128, TK = 64, WM = 2, WN = 2, VPM = 6; };      // 4 waves, 32 x 64
 
 // AMODE 0: A = X (bf16).  AMODE 1: A = X * s2[k] (fp32, exact), rounded to
