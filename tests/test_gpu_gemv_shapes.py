@@ -1,0 +1,104 @@
+"""GPU parity of the decode GEMVs on seeded random shapes: group RTN (batch
+1 with fp32 or bf16 x, batch 2..16 with bf16 x), binary low-rank and
+codebook codes, against the CPU oracle on sampled outputs.
+
+Each launcher derives its geometry from the shape (how far a row's units
+are split over waves, rows per stream or row tiles per workgroup, one bf16
+weight operand or hi + lo below 512 inputs, the binary stages' steps per
+wave and their full or general variants); random N, K, r and batch sizes
+with ragged tails reach those branches without naming them.  The shapes are
+drawn once from a fixed seed.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check_err, dev, dev_bf16, host, say
+from workloads import gen_binlr, gen_weights, gen_x_bf16, gen_x_f32, rng_for
+
+pytestmark = pytest.mark.gpu
+
+_R = np.random.default_rng(31337)
+
+
+def _dim(lo, hi, i):
+    # even cases log-uniform, odd cases uniform
+    if i % 2 == 0:
+        return int(np.exp(_R.uniform(np.log(lo), np.log(hi))))
+    return int(_R.integers(lo, hi + 1))
+
+
+GROUP_CASES = []
+for i in range(12):
+    bits, group = int(_R.integers(2, 7)), int(_R.choice([32, 64]))
+    B = 1 if i % 3 == 0 else int(_R.integers(1, 17))
+    xkind = "f32" if (B == 1 and i % 2 == 0) else "bf16"
+    GROUP_CASES.append((bits, group, B, xkind, _dim(1, 30000, i), group * _dim(1, 12000 // group, i)))
+BIN_CASES = [(int(_R.integers(1, 17)) if i % 2 else 1, _dim(1, 30000, i), _dim(1, 9000, i), _dim(1, 3000, i))
+             for i in range(8)]
+CB_CASES = []
+for i in range(6):
+    bits, group = int(_R.integers(2, 5)), int(_R.choice([32, 64]))
+    B = 1 if i % 2 == 0 else int(_R.integers(2, 17))
+    CB_CASES.append((bits, group, B, _dim(1, 30000, i), group * _dim(1, 12000 // group, i)))
+
+
+def _x(B, K, xkind, rng):
+    if xkind == "f32":
+        xh = gen_x_f32(B, K, rng)
+        return xh.astype(np.float64), dev(xh)
+    xb = gen_x_bf16(B, K, rng)
+    return oracle.product.bf16_to_f64(xb), dev_bf16(xb)
+
+
+def _cols(N, seed):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, N - 1], r.choice(N, min(N, 48), replace=False)]))
+
+
+@pytest.mark.parametrize("bits,group,B,xkind,N,K", GROUP_CASES)
+def test_group_random_shape(gpu, bits, group, B, xkind, N, K):
+    say(f"gemv group b={bits} g={group} B={B} x={xkind} N={N} K={K}")
+    seed = N * 7 + K * 3 + B
+    W = gen_weights(N, K, rng_for(610, seed), outliers=True)
+    codes, meta = gpu.qpack_group(dev(W), bits, group)
+    xv, xd = _x(B, K, xkind, rng_for(611, seed))
+    y = host(gpu.qgemv_group(codes, meta, N, K, bits, group, xd)).reshape(B, N)
+    cols = _cols(N, seed)
+    q, s, o = oracle.rtn.quantize(W[cols], bits, group)
+    W_hat = oracle.rtn.dequantize(q, s, o, group)
+    err = check_err(y[:, cols], oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
+    say(f"  err={err:.2e}")
+
+
+@pytest.mark.parametrize("B,N,K,r", BIN_CASES)
+def test_binlr_random_shape(gpu, B, N, K, r):
+    say(f"gemv binlr B={B} N={N} K={K} r={r}")
+    seed = N * 7 + K * 3 + r + B
+    U, V, s1, s2 = gen_binlr(N, K, r, rng_for(612, seed))
+    ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
+    xv, xd = _x(B, K, "bf16", rng_for(613, seed))
+    y = host(gpu.qgemv_binlr(ubd, vbd, dev(s1.view(np.int16)), dev(s2.view(np.int16)), N, K, r, xd)).reshape(B, N)
+    cols = _cols(N, seed)
+    W = oracle.binlr.reconstruct(U[cols], V, s1[cols], s2)
+    err = check_err(y[:, cols], oracle.product.matmul_ref(W, xv),
+                    oracle.product.binlr_abs_denominator(U[cols], V, s1[cols], s2, xv))
+    say(f"  err={err:.2e}")
+
+
+@pytest.mark.parametrize("bits,group,B,N,K", CB_CASES)
+def test_codebook_random_shape(gpu, bits, group, B, N, K):
+    say(f"gemv codebook b={bits} g={group} B={B} N={N} K={K}")
+    seed = N * 7 + K * 3 + B
+    books = rng_for(614, seed).integers(0, 128, size=(8, 1 << bits)).astype(np.uint8)
+    W = gen_weights(N, K, rng_for(615, seed), outliers=True)
+    bd = dev(books)
+    c, m, k = gpu.qpack_group_cb(dev(W), bits, group, bd)
+    xv, xd = _x(B, K, "bf16", rng_for(616, seed))
+    y = host(gpu.qgemv_group_cb(c, m, k, bd, N, K, bits, group, xd)).reshape(B, N)
+    cols = _cols(N, seed)
+    q, s, o, ids = oracle.codebook.quantize(W[cols], bits, group, books)
+    assert np.array_equal(host(k)[cols], ids)
+    W_hat = oracle.codebook.dequantize(q, s, o, ids, books, bits, group)
+    err = check_err(y[:, cols], oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
+    say(f"  err={err:.2e}")
