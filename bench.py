@@ -255,11 +255,18 @@ def layer_bytes(attn_bits, attn_group, mlp_bits, mlp_group):
     return tot
 
 
+KV_STEPS = 1000          # key-cache rows: 1000 calls (tens of ms), as the GEMV rows
+STREAM_PASSES = 2000     # streaming-read reference: 132 MB passes per timed region
+
+
 def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launches, log,
                  LAYER_SHAPES, MIXED_SETS, N_LAYERS, ATTN, layer_weights, layer_x, binlr_factors, want):
     """Every other row of the hot path; want(name) selects rows (all by default)."""
     rows = {}
-    steps, warm = 200, 20
+    # 2000 launches per row (tens of ms): a sustained HBM stream runs ~10 %
+    # faster for its first ~2 ms and then dips while the chip's power
+    # management settles, so windows of a few ms mix in that transient
+    steps, warm = 2000, 20
 
     def gemv_row(name, W, bits, group, B):
         N, K = W.shape
@@ -419,10 +426,10 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         def f(i):
             a, b_, m_ = pool[i % len(pool)]
             cg.qtq_logits(a, b_, m_, n, H, bits, delta, table, Pi, SPi, Qv, out=out, ws=ws)
-        wall, ev = time_launches(f, 100, 10, period=len(pool))
+        wall, ev = time_launches(f, KV_STEPS, 10, period=len(pool))
         del pool
         torch.cuda.empty_cache()
-        us = ev / 100 * 1e6
+        us = ev / KV_STEPS * 1e6
         base = {}
         Kh = Kf.view(H, n, 128)
         for label, dt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
@@ -472,10 +479,10 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         def f(i):
             a, m_ = pool[i % len(pool)]
             cg.qtq_attend(a, m_, n, H, bits, delta, table, Pi, Pw, out=out, ws=ws)
-        wall, ev = time_launches(f, 100, 10, period=len(pool))
+        wall, ev = time_launches(f, KV_STEPS, 10, period=len(pool))
         del pool
         torch.cuda.empty_cache()
-        us = ev / 100 * 1e6
+        us = ev / KV_STEPS * 1e6
         base = {}
         for label, dt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
             vd = Vf.view(H, n, 128).to(dt).contiguous()
@@ -651,10 +658,11 @@ def stream_ceiling(cg, torch, dev, time_launches, log):
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     n = 132_120_576
     chunks = [buf[i * n:(i + 1) * n] for i in range((2 << 30) // n + 1)]
-    _, ev = time_launches(lambda i: cg.qstream_read(chunks[i % len(chunks)], sink), 400, 20, period=len(chunks))
-    small = n * 400 / ev / 1e9
-    _, ev = time_launches(lambda i: cg.qstream_read(buf, sink), 10, 2)
-    big = buf.numel() * 10 / ev / 1e9
+    _, ev = time_launches(lambda i: cg.qstream_read(chunks[i % len(chunks)], sink), STREAM_PASSES, 20,
+                          period=len(chunks))
+    small = n * STREAM_PASSES / ev / 1e9
+    _, ev = time_launches(lambda i: cg.qstream_read(buf, sink), 40, 2)
+    big = buf.numel() * 40 / ev / 1e9
     del buf, chunks
     torch.cuda.empty_cache()
     log(f"streaming read: {small:.0f} GB/s per 132 MB pass, {big:.0f} GB/s over 4 GiB")
