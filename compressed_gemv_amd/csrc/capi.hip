@@ -37,6 +37,21 @@ int dtype_ok(int d) { return d == Q_F32 || d == Q_BF16; }
 // 2 for fp32 activations).
 int64_t gemv_b1_max_k(int x_dtype) { return x_dtype == Q_F32 ? 8 * 64 * 2 * 32 : 8 * 64 * 4 * 32; }
 
+// The batched GEMV addresses a lane's activation slice as (row * K + unit
+// * 32) * 2 bytes in 32-bit signed arithmetic: B * K * 2 must stay below
+// 2^31.
+int batched_x_ok(int64_t B, int64_t K) { return B > 1 && B * K * 2 >= ((int64_t)1 << 31) ? Q_EUNSUPPORTED : Q_OK; }
+
+// Prefill tile loads address X (and the binary path's T) through 32-bit
+// offsets from the tile's first row: 256 rows of K bf16 inputs, and of the
+// padded rank in fp32 for T, must fit; the grid of 64 x 128 tiles must fit
+// a signed 32-bit workgroup index.
+int prefill_dims_ok(int64_t M, int64_t N, int64_t K, int64_t rp) {
+  if (K * 256 * 2 >= ((int64_t)1 << 32) || rp * 256 * 4 >= ((int64_t)1 << 32)) return Q_EUNSUPPORTED;
+  if (((M + 63) / 64) * ((N + 127) / 128) >= ((int64_t)1 << 31)) return Q_EUNSUPPORTED;
+  return Q_OK;
+}
+
 // codebooks: 2..4-bit codes, 1..16 books
 int cb_args_ok(int64_t N, int64_t K, int bits, int group, const uint8_t* books, int n_books) {
   const int st = group_args_ok(N, K, bits, group);
@@ -116,6 +131,7 @@ int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K, int b
   if (!aligned(codes, 16) || !aligned(meta, 16) || !aligned(x, 16) || !aligned(y, 4))
     return Q_EALIGN;
   if (B == 1 && K > gemv_b1_max_k(x_dtype)) return Q_EUNSUPPORTED;
+  if (batched_x_ok(B, K) != Q_OK) return Q_EUNSUPPORTED;
   if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
   if (N > INT32_MAX || K > INT32_MAX) return Q_EUNSUPPORTED;
   return hip_status(qg::launch_gemv_group(static_cast<const uint32_t*>(codes),
@@ -138,6 +154,7 @@ int qgemv_group_multi(const qgroup_mat* mats, int count, int64_t K, int bits, in
   }
   if (!aligned(x, 16)) return Q_EALIGN;
   if (B == 1 && K > gemv_b1_max_k(x_dtype)) return Q_EUNSUPPORTED;
+  if (batched_x_ok(B, K) != Q_OK) return Q_EUNSUPPORTED;
   if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
   if (total > INT32_MAX || K > INT32_MAX) return Q_EUNSUPPORTED;
   if (B > 1) {
@@ -216,6 +233,7 @@ int qgemv_group_outlier(const void* codes, const void* meta, const uint16_t* sid
   if (!aligned(codes, 16) || !aligned(meta, 16) || !aligned(x, 16) || !aligned(y, 4))
     return Q_EALIGN;
   if (B == 1 && K > gemv_b1_max_k(x_dtype)) return Q_EUNSUPPORTED;
+  if (batched_x_ok(B, K) != Q_OK) return Q_EUNSUPPORTED;
   if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
   if (N > INT32_MAX || K > INT32_MAX || N * n_out > INT32_MAX) return Q_EUNSUPPORTED;
   return hip_status(qg::launch_gemv_group(static_cast<const uint32_t*>(codes),
@@ -279,6 +297,7 @@ int qgemv_group_cb(const void* codes, const void* meta, const uint8_t* book_ids,
   if (!aligned(codes, 16) || !aligned(meta, 16) || !aligned(x, 16) || !aligned(y, 4))
     return Q_EALIGN;
   if (B == 1 && K > gemv_b1_max_k(x_dtype)) return Q_EUNSUPPORTED;
+  if (batched_x_ok(B, K) != Q_OK) return Q_EUNSUPPORTED;
   if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
   if (N > INT32_MAX || K > INT32_MAX) return Q_EUNSUPPORTED;
   return hip_status(qg::launch_gemv_group_cb(static_cast<const uint32_t*>(codes),
@@ -565,6 +584,8 @@ int qgemm_prefill(const qweight* w, const void* X, int x_dtype, int64_t M, void*
   if (!dtype_ok(y_dtype)) return Q_EINVAL;
   if (!aligned(X, 16) || !aligned(Y, 4)) return Q_EALIGN;
   if (M > INT32_MAX) return Q_EUNSUPPORTED;
+  if (prefill_dims_ok(M, w->N, w->K, w->format == Q_FMT_BINLR ? padded_words(w->r) * 32 : 0) != Q_OK)
+    return Q_EUNSUPPORTED;
   if (w->format == Q_FMT_GROUP) {
     if (!w->codes || !w->meta) return Q_EINVAL;
     if (outlier_args_ok(w->K, w->n_out) != Q_OK || (w->n_out > 0 && (!w->side || !w->oidx))) return Q_EINVAL;

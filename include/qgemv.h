@@ -110,8 +110,8 @@ int qunpack_group(const void* codes, const void* meta, int64_t N, int64_t K,
  * accumulation in fp32.  1 <= B <= 16.  codes, meta and x must be 16-byte
  * aligned (the activations are read with 16-byte loads), y 4-byte aligned;
  * Q_EALIGN otherwise.  Batch 1 supports K <= 65536 (bf16 x) or 32768 (fp32
- * x); B > 1 takes bf16 x only (Q_EUNSUPPORTED otherwise).  Asynchronous on
- * `stream`. */
+ * x); B > 1 takes bf16 x only and B * K < 2^30 (activation offsets are
+ * 32-bit), Q_EUNSUPPORTED otherwise.  Asynchronous on `stream`. */
 int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K,
                 int bits, int group, const void* x, int x_dtype, int64_t B,
                 void* y, int y_dtype, hipStream_t stream);
@@ -353,7 +353,9 @@ int qgemm_prefill_ws(const qweight* w, int64_t M, size_t* ws_bytes);
  * accumulation.  Group RTN: one pass.  Binary: T = (X (.) s2) V into the
  * workspace as bf16, then Y = (T U^T) (.) s1 ("70B en 4GB de VRAM...",
  * section 1; the pages' GEMM kernels for this format).  y_dtype Q_F32 or
- * Q_BF16.  Asynchronous. */
+ * Q_BF16.  Tiles address X and T through 32-bit offsets: K < 2^23, the rank
+ * padded to 128 below 2^22, and ceil(M/64) * ceil(N/128) < 2^31, else
+ * Q_EUNSUPPORTED.  Asynchronous. */
 int qgemm_prefill(const qweight* w, const void* X, int x_dtype, int64_t M,
                   void* Y, int y_dtype, void* ws, size_t ws_bytes,
                   hipStream_t stream);

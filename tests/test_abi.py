@@ -153,6 +153,25 @@ def test_entry_points_validate_before_touching_the_gpu(lib):
     assert lib.qgemm_prefill(ctypes.byref(w), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
     wb = cg.qweight(cg.Q_FMT_BINLR, 64, 128, 0, 0, None, None, 16, 0x10000, 0x10000, 0x10000, 0x10000)
     assert lib.qgemm_prefill(ctypes.byref(wb), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EWORKSPACE
+    # 32-bit tile offsets: 256 rows of K bf16 inputs, 256 rows of the padded
+    # rank in fp32, and the tile count must fit
+    wk = cg.qweight(cg.Q_FMT_GROUP, 1, 1 << 23, 2, 32, 0x10000, 0x10000, 0, None, None, None, None)
+    assert lib.qgemm_prefill(ctypes.byref(wk), good, cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EUNSUPPORTED
+    wk.K = (1 << 23) - 32
+    assert lib.qgemm_prefill(ctypes.byref(wk), P(0), cg.Q_BF16, 16, good, cg.Q_F32, P(0), 0, s) == cg.Q_EINVAL
+    wr = cg.qweight(cg.Q_FMT_BINLR, 1, 64, 0, 0, None, None, 1 << 22, 0x10000, 0x10000, 0x10000, 0x10000)
+    assert lib.qgemm_prefill(ctypes.byref(wr), good, cg.Q_BF16, 16, good, cg.Q_F32, good, 1 << 40,
+                             s) == cg.Q_EUNSUPPORTED
+    wt = cg.qweight(cg.Q_FMT_GROUP, 32768, 32, 2, 32, 0x10000, 0x10000, 0, None, None, None, None)
+    assert lib.qgemm_prefill(ctypes.byref(wt), good, cg.Q_BF16, 1 << 30, good, cg.Q_F32, P(0), 0,
+                             s) == cg.Q_EUNSUPPORTED   # 2^24 x 256 tiles of 64 x 128
+    assert lib.qgemm_prefill(ctypes.byref(wt), P(0), cg.Q_BF16, 1 << 20, good, cg.Q_F32, P(0), 0,
+                             s) == cg.Q_EINVAL         # 2^14 x 256 tiles: past the size checks
+    # batched GEMV: B * K * 2 bytes of activations addressed in 32 bits
+    assert lib.qgemv_group(good, good, 1, 1 << 26, 2, 32, good, cg.Q_BF16, 16, good, cg.Q_F32,
+                           s) == cg.Q_EUNSUPPORTED
+    assert lib.qgemv_group(good, good, 1, 1 << 26, 2, 32, good, cg.Q_BF16, 1, good, cg.Q_F32,
+                           s) == cg.Q_EUNSUPPORTED   # batch 1: K past its own limit
     # codebook prefill: ids present, no outlier columns with books, widths 2..4
     wc = cg.qweight(cg.Q_FMT_GROUP, 64, 128, 4, 32, 0x10000, 0x10000, 0, None, None, None, None, None, None, 0,
                     None, 0x10000, 8)
