@@ -50,6 +50,13 @@
 
 namespace qg {
 
+template <bool C, typename A, typename B> struct Pick { using T = A; };
+template <typename A, typename B> struct Pick<false, A, B> { using T = B; };
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
 // ------------------------------------------------------------------ B = 1
 // OUT: outlier side columns (fp16 side[N][n_out] at input channels oidx[],
 // n_out <= 64): lane j < n_out of K-slice 0 adds side[row][j] * x[oidx[j]]
@@ -370,20 +377,31 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 // matching 8-wide slices of x[b].  Dequantization: each code is decoded as
 // the fp16 subnormal q*2^(p-24) (common.hpp, UnitH), and one v_fma_mix_f32
 // per weight gives fl32(s*q + o); the MFMA takes it as bf16 hi + lo (two
-// MFMAs, 2^-16 relative residual), so the rounding of the weight operand
-// stays far below the error budget at any K.  Partial sums of the WPB waves
+// MFMAs, 2^-16 relative residual; SPLITW), or, for reductions of at least
+// 512 inputs, rounded once to bf16 (one MFMA).  Partial sums of the WPB waves
 // meet in LDS.
+// PAIR (plain codes, one bf16 operand): a wave takes two quads (8 units) per
+// step, and each weight load instruction reads those 8 units from 8 rows
+// (lane (r, kg) of instruction h: row (r & 7) + 8h, unit kg + 4((r >> 3) ^ h))
+// instead of 4 units from 16 rows, i.e. half as many cache lines per
+// instruction, whole 128-byte lines for 4-bit codes.  The matrix-core layout
+// is restored in registers: quad 0 is instruction 0's word for r < 8 and
+// instruction 1's for r >= 8, quad 1 the other instruction's word 8 lanes
+// away (a row rotation by 8, DPP).  Group words: g32 as the codes; g64 one
+// load of the pair's 4 groups per row, spread by lane permutes.  The same
+// products in the same order, so the results equal the one-quad form's.
 // OUT: outlier side columns as in the B = 1 kernel, added to each output
 // in the final reduction (the activations of the outlier channels are
 // staged in LDS first).
 // CB: codes read through per-group books; the pairs of decode_unit_cb give
 // e[q] exactly and one fma per weight gives fl32(s 2^(b-7) e[q] + o).
-template <int BITS, int G, int RT, int WPB, bool OUT, bool CB = false, bool SPLITW = true>
+template <int BITS, int G, int RT, int WPB, bool OUT, bool CB = false, bool SPLITW = true, bool PAIR = false>
 __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
     const uint16_t* __restrict__ x, int B, void* __restrict__ yout, int y_bf16,
     const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out, Books bk) {
   static_assert(!(CB && OUT), "codebooks come without outlier columns");
+  static_assert(!(PAIR && (CB || SPLITW)), "pair loads: plain codes, one bf16 weight operand");
   __shared__ float red[WPB][RT * 4][64];
   __shared__ float xo[OUT ? 16 * 64 : 1];
   __shared__ __align__(16) uint32_t dict[CB ? 64 : 1];
@@ -405,7 +423,12 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  struct Buf { u32x4_t xb[4]; uint32_t w[RT][BITS]; uint32_t m[RT]; uint32_t k[RT]; };
+  // one quad per step, or (PAIR) two: codes as loaded (instruction h of tile
+  // t in w[t][h]) and meta as loaded (G = 32: as the codes; G = 64: one word)
+  struct Buf1 { u32x4_t xb[4]; uint32_t w[RT][BITS]; uint32_t m[RT]; uint32_t k[RT]; };
+  struct Buf2 { u32x4_t xb[2][4]; uint32_t w[RT][2][BITS]; uint32_t m[RT][2]; };
+  using Buf = typename Pick<PAIR, Buf2, Buf1>::T;
+  const bool lo8 = r < 8;
   // Branch-free loads through buffer resources.  Activations: a lane past B
   // reads a valid activation row (its column is never stored), a unit past K
   // gets an out-of-range offset and reads 0.  Weights: rows past N read 0
@@ -416,6 +439,38 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(bk.ids, CB ? (uint32_t)((size_t)N * GN) : 0u);
   auto load = [&](Buf& b, int qi) {
+    if constexpr (PAIR) {
+      // qi is a pair of quads: units 8 qi .. 8 qi + 7.  Load instruction h
+      // of tile t: lane (r, kg) takes row (r & 7) + 8 h of the tile and unit
+      // 8 qi + kg + 4 ((r >> 3) ^ h), so each instruction reads 8 units in a
+      // row from 8 rows (whole 128-byte lines for 4-bit codes).
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int u0 = 8 * qi + 4 * q + kg;
+        const uint32_t xo = u0 < U ? (uint32_t)((bc * K + u0 * 32) * 2) : 0xFFFFFF00u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * t, 0, 0);
+          b.xb[q][t] = u32x4_t{v[0], v[1], v[2], v[3]};
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t row = (uint32_t)(row_base + 16 * t + (r & 7) + 8 * h);
+          const uint32_t u = (uint32_t)(8 * qi + kg + 4 * ((r >> 3) ^ h));
+          buf_load_unit<BITS, 0>(crs, (row * (uint32_t)U + u) * (BITS * 4), 0u, b.w[t][h]);
+          if constexpr (G == 32) b.m[t][h] = __builtin_amdgcn_raw_buffer_load_b32(mrs, (row * (uint32_t)GN + u) * 4, 0u, 0);
+        }
+        if constexpr (G == 64) {
+          // the pair's 4 groups of row r: lane (r, kg) takes group 4 qi + kg
+          const uint32_t row = (uint32_t)(row_base + 16 * t + r);
+          b.m[t][0] = __builtin_amdgcn_raw_buffer_load_b32(mrs, (row * (uint32_t)GN + (uint32_t)(4 * qi + kg)) * 4, 0u, 0);
+          b.m[t][1] = 0u;
+        }
+      }
+    } else {
     const int u0 = 4 * qi + kg;
     const uint32_t xo = u0 < U ? (uint32_t)((bc * K + u0 * 32) * 2) : 0xFFFFFF00u;
 #pragma unroll
@@ -434,22 +489,26 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
       if constexpr (CB)
         b.k[t] = __builtin_amdgcn_raw_buffer_load_b8(krs, row * (uint32_t)GN + (uint32_t)((u0 * 32) / G), 0u, 0);
     }
+    }
   };
   using UN = UnitH<BITS>;
   CbConst kc{};
   if constexpr (CB) kc = cb_consts();
-  auto compute = [&](const Buf& b) {
+  // one quad: codes w, group words m, book ids kk (CB) of the RT tiles and
+  // the activation fragments xb
+  auto quad = [&](const uint32_t (&bw)[RT][BITS], const uint32_t (&bm)[RT], const uint32_t (&bk_)[RT],
+                  const u32x4_t (&bxb)[4]) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       uint32_t pr[16];
-      const float s = f16_bits_to_f32(b.m[t] & 0xFFFFu), o = f16_bits_to_f32(b.m[t] >> 16);
+      const float s = f16_bits_to_f32(bm[t] & 0xFFFFu), o = f16_bits_to_f32(bm[t] >> 16);
       float wv[32];
       if constexpr (CB) {
         uint32_t T[4] = {0u, 0u, 0u, 0u};
-        const uint32_t* tp = dict + ((b.k[t] & 15u) << BITS) / 4;   // ids < 16 (packer)
+        const uint32_t* tp = dict + ((bk_[t] & 15u) << BITS) / 4;   // ids < 16 (packer)
 #pragma unroll
         for (int i = 0; i < (1 << BITS) / 4; ++i) T[i] = tp[i];
-        decode_unit_cb<BITS>(b.w[t], T, pr, kc);
+        decode_unit_cb<BITS>(bw[t], T, pr, kc);
         const float sc = s * (1.0f / (float)(1 << (7 - BITS)));
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -458,7 +517,7 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
           wv[pi.cb] = __builtin_fmaf(bf16_hi_to_f32(pr[k]) - 128.0f, sc, o);
         }
       } else {
-        decode_unit_h<BITS>(b.w[t], pr);
+        decode_unit_h<BITS>(bw[t], pr);
         float sp[UN::NCLS];
 #pragma unroll
         for (int c = 0; c < UN::NCLS; ++c) sp[c] = s * (float)(1 << (24 - BITS * c));
@@ -482,16 +541,49 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
           if constexpr (SPLITW) lo[e] = cvt_pk_bf16(w0 - bf16_lo_to_f32(hi[e]), w1 - bf16_hi_to_f32(hi[e]));
         }
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
-                                                         __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
+                                                         __builtin_bit_cast(bf16x8_t, bxb[j]), acc[t], 0, 0, 0);
         if constexpr (SPLITW)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo),
-                                                           __builtin_bit_cast(bf16x8_t, b.xb[j]), acc[t], 0, 0, 0);
+                                                           __builtin_bit_cast(bf16x8_t, bxb[j]), acc[t], 0, 0, 0);
       }
     }
   };
 
-  const int nq = (U + 3) >> 2;
-  const int nit = wave < nq ? (nq - wave + WPB - 1) / WPB : 0;   // quads of this wave
+  auto compute = [&](const Buf& b) {
+    if constexpr (PAIR) {
+      // to the matrix-core layout: quad 0 of the pair (lane (r, kg): unit kg
+      // of row r) is instruction 0's word for r < 8 and instruction 1's for
+      // r >= 8; quad 1 (unit 4 + kg) sits 8 lanes away in the other
+      // instruction, brought over by a rotation by 8 inside each 16-lane row
+      uint32_t w0[RT][BITS], w1[RT][BITS], m0[RT], m1[RT], k0[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) {
+          const uint32_t a = b.w[t][0][i], c = b.w[t][1][i];
+          w0[t][i] = lo8 ? a : c;
+          w1[t][i] = dpp_u32<0x128>(lo8 ? c : a);   // row_ror:8
+        }
+        if constexpr (G == 32) {
+          m0[t] = lo8 ? b.m[t][0] : b.m[t][1];
+          m1[t] = dpp_u32<0x128>(lo8 ? b.m[t][1] : b.m[t][0]);
+        } else {
+          // group (unit / 2) of row r: lane (r, kg / 2) holds quad 0's,
+          // lane (r, 2 + kg / 2) quad 1's
+          m0[t] = (uint32_t)__builtin_amdgcn_ds_bpermute((r + 16 * (kg >> 1)) * 4, (int)b.m[t][0]);
+          m1[t] = (uint32_t)__builtin_amdgcn_ds_bpermute((r + 16 * (2 + (kg >> 1))) * 4, (int)b.m[t][0]);
+        }
+        k0[t] = 0u;
+      }
+      quad(w0, m0, k0, b.xb[0]);
+      quad(w1, m1, k0, b.xb[1]);
+    } else {
+      quad(b.w, b.m, b.k, b.xb);
+    }
+  };
+
+  const int nq = PAIR ? (((U + 3) >> 2) + 1) >> 1 : (U + 3) >> 2;   // quads, or pairs of quads
+  const int nit = wave < nq ? (nq - wave + WPB - 1) / WPB : 0;     // steps of this wave
   Buf b0, b1;
   if (nit > 0) load(b0, wave);
   if constexpr (CB) __syncthreads();   // dictionary staged before the first decode
@@ -583,6 +675,9 @@ static hipError_t gemv_b1_t(const uint32_t* codes, const uint32_t* meta, int64_t
   return hipGetLastError();
 }
 
+#ifndef QG_MB_PAIR
+#define QG_MB_PAIR 1      // plain codes, K >= 512: two quads per step, 8-row load instructions
+#endif
 // Reductions of at least this many inputs take the weights as one bf16
 // operand; shorter ones as bf16 hi + lo (the error argument is given with
 // the tile choice below).
@@ -597,18 +692,24 @@ static hipError_t gemv_mfma_launch(const uint32_t* codes, const uint32_t* meta, 
 #define MF(O, C, S, SV, SI, SN)                                                                               \
   hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, O, C, S>), grid, block, 0, s, codes, meta, (int)N, (int)K, \
                      x, (int)B, y, y_bf16, SV, SI, SN, bk)
+#define MFP(O, SV, SI, SN)                                                                                     \
+  hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, O, false, false, true>), grid, block, 0, s, codes, meta,   \
+                     (int)N, (int)K, x, (int)B, y, y_bf16, SV, SI, SN, bk)
   const bool split = K < kGemvSplitBelowK;
   if constexpr (CB) {
     if (split) MF(false, true, true, nullptr, nullptr, 0);
     else MF(false, true, false, nullptr, nullptr, 0);
   } else if (sd.n > 0) {
     if (split) MF(true, false, true, sd.vals, sd.idx, sd.n);
+    else if (QG_MB_PAIR) MFP(true, sd.vals, sd.idx, sd.n);
     else MF(true, false, false, sd.vals, sd.idx, sd.n);
   } else {
     if (split) MF(false, false, true, nullptr, nullptr, 0);
+    else if (QG_MB_PAIR) MFP(false, nullptr, nullptr, 0);
     else MF(false, false, false, nullptr, nullptr, 0);
   }
 #undef MF
+#undef MFP
   return hipGetLastError();
 }
 
