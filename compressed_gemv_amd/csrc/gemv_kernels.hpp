@@ -438,7 +438,7 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((size_t)N * U * BITS * 4));
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, (uint32_t)((size_t)N * GN * 4));
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(bk.ids, CB ? (uint32_t)((size_t)N * GN) : 0u);
-  auto load = [&](Buf& b, int qi) {
+  auto load = [&](Buf& b, int qi, bool even) {
     if constexpr (PAIR) {
       // qi is a pair of quads: units 8 qi .. 8 qi + 7.  Load instruction h
       // of tile t: lane (r, kg) takes row (r & 7) + 8 h of the tile and unit
@@ -464,10 +464,16 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
           if constexpr (G == 32) b.m[t][h] = __builtin_amdgcn_raw_buffer_load_b32(mrs, (row * (uint32_t)GN + u) * 4, 0u, 0);
         }
         if constexpr (G == 64) {
-          // the pair's 4 groups of row r: lane (r, kg) takes group 4 qi + kg
-          const uint32_t row = (uint32_t)(row_base + 16 * t + r);
-          b.m[t][0] = __builtin_amdgcn_raw_buffer_load_b32(mrs, (row * (uint32_t)GN + (uint32_t)(4 * qi + kg)) * 4, 0u, 0);
-          b.m[t][1] = 0u;
+          // even steps load the group words of both pairs of their block (8
+          // groups, 32 bytes of row r): lane (r, kg) takes groups
+          // 4 qi + 2 kg and 4 qi + 2 kg + 1
+          if (even) {
+            const uint32_t row = (uint32_t)(row_base + 16 * t + r);
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+                mrs, (row * (uint32_t)GN + (uint32_t)(4 * qi + 2 * kg)) * 4, 0u, 0);
+            b.m[t][0] = v[0];
+            b.m[t][1] = v[1];
+          }
         }
       }
     } else {
@@ -549,7 +555,8 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     }
   };
 
-  auto compute = [&](const Buf& b) {
+  // s: the step's place in its pair block (G = 64 group words in mc)
+  auto compute = [&](const Buf& b, int s_, const uint32_t (&mc)[RT][2]) {
     if constexpr (PAIR) {
       // to the matrix-core layout: quad 0 of the pair (lane (r, kg): unit kg
       // of row r) is instruction 0's word for r < 8 and instruction 1's for
@@ -568,10 +575,15 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
           m0[t] = lo8 ? b.m[t][0] : b.m[t][1];
           m1[t] = dpp_u32<0x128>(lo8 ? b.m[t][1] : b.m[t][0]);
         } else {
-          // group (unit / 2) of row r: lane (r, kg / 2) holds quad 0's,
-          // lane (r, 2 + kg / 2) quad 1's
-          m0[t] = (uint32_t)__builtin_amdgcn_ds_bpermute((r + 16 * (kg >> 1)) * 4, (int)b.m[t][0]);
-          m1[t] = (uint32_t)__builtin_amdgcn_ds_bpermute((r + 16 * (2 + (kg >> 1))) * 4, (int)b.m[t][0]);
+          // quad q of this step needs group 4 s + 2 q + kg / 2 of the block,
+          // word kg / 2 of lane (r, 2 s + q)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int src = (r + 16 * (2 * s_ + q)) * 4;
+            const uint32_t d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mc[t][0]);
+            const uint32_t d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mc[t][1]);
+            (q ? m1 : m0)[t] = (kg >> 1) ? d1 : d0;
+          }
         }
         k0[t] = 0u;
       }
@@ -582,28 +594,50 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
     }
   };
 
-  const int nq = PAIR ? (((U + 3) >> 2) + 1) >> 1 : (U + 3) >> 2;   // quads, or pairs of quads
-  const int nit = wave < nq ? (nq - wave + WPB - 1) / WPB : 0;     // steps of this wave
+  // Steps of a wave: quads w, w + WPB, ...; with PAIR, pairs w, w + WPB, ...,
+  // except for g64 groups (BLK), where wave w takes blocks of two adjacent
+  // pairs, w, w + WPB, ... (step it is pair 2 (w + WPB (it / 2)) + it % 2), so
+  // that b0 holds the even steps, which also load their block's group words,
+  // and b1 the odd ones; an odd step past the last pair loads zero
+  // activations.  (Blocks for g32 codes measured slower: the waves of a
+  // workgroup then read pairs 0, 2, 4, 6 together rather than 0, 1, 2, 3.)
+  constexpr bool BLK = PAIR && G == 64;
+  const int nq = (U + 3) >> 2, npair = (nq + 1) >> 1, nblk = (npair + 1) >> 1;
+  const int nunit = PAIR ? npair : nq;
+  const int nit = BLK ? (wave < nblk ? 2 * ((nblk - wave + WPB - 1) / WPB) : 0)
+                      : (wave < nunit ? (nunit - wave + WPB - 1) / WPB : 0);   // steps of this wave
+  auto idx = [&](int st) { return BLK ? 2 * (wave + WPB * (st >> 1)) + (st & 1) : wave + WPB * st; };
   Buf b0, b1;
-  if (nit > 0) load(b0, wave);
+  uint32_t mc[RT][2];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) mc[t][0] = mc[t][1] = 0u;
+  auto keep = [&](const Buf& b) {   // the block's group words, for its odd step
+    if constexpr (PAIR && G == 64)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) { mc[t][0] = b.m[t][0]; mc[t][1] = b.m[t][1]; }
+  };
+  if (nit > 0) load(b0, idx(0), true);
   if constexpr (CB) __syncthreads();   // dictionary staged before the first decode
   int it = 0;
   while (it + 2 < nit) {
-    load(b1, wave + WPB * (it + 1));
+    load(b1, idx(it + 1), false);
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(b0);
-    load(b0, wave + WPB * (it + 2));
+    keep(b0);
+    compute(b0, 0, mc);
+    load(b0, idx(it + 2), true);
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(b1);
+    compute(b1, 1, mc);
     it += 2;
   }
   if (it + 1 < nit) {
-    load(b1, wave + WPB * (it + 1));
+    load(b1, idx(it + 1), false);
     __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads issued here
-    compute(b0);
-    compute(b1);
+    keep(b0);
+    compute(b0, 0, mc);
+    compute(b1, 1, mc);
   } else if (it < nit) {
-    compute(b0);
+    keep(b0);
+    compute(b0, 0, mc);
   }
 #pragma unroll
   for (int t = 0; t < RT; ++t)
