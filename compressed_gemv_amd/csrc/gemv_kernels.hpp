@@ -747,9 +747,15 @@ static hipError_t gemv_mfma_launch(const uint32_t* codes, const uint32_t* meta, 
   return hipGetLastError();
 }
 
-// Tile choice, measured on MI355X at B = 2..16: row tiles per wave (reuse of
-// the activation fragments) RT = 4 for N >= 16384, 2 for N >= 4096, else 1;
-// 4 waves split K.  QG_MB_RT / QG_MB_WPB force one choice.
+// Tile choice, measured on MI355X at B = 2..16: 4 waves split K, and the
+// row tiles per workgroup (reuse of the activation fragments) are picked
+// from {1, 2, 4, 7} so that the workgroups spread evenly over the 256 CUs
+// (mfma_row_tiles).  At N = 28672 that is 7 tiles
+// (256 workgroups of 112 rows) instead of 4 (448 workgroups, so 192 CUs
+// held two and 64 one): 8192 x 28672 4-bit g64 at B = 16 41.9 -> 36.7 us
+// (with outlier columns 44.0 -> 39.6, codebooks 69.4 -> 62.8), 2-bit g32 at
+// B = 8 36.2 -> 31.9 us; 3-bit g32 at B = 8 measured 40.1 -> 41.4 us, so
+// 3-bit codes keep at most 4 tiles.  QG_MB_RT / QG_MB_WPB force one choice.
 // Weight operand: rounding w_hat once to bf16 (unit roundoff 2^-8) moves a
 // product by at most 2^-8 sum |w_hat||x| in the worst case, and by about
 // 2^-8 / sqrt(3K) of it when the rounding errors are independent (below
@@ -761,6 +767,24 @@ static hipError_t gemv_mfma_launch(const uint32_t* codes, const uint32_t* meta, 
 #ifndef QG_MB_WPB
 #define QG_MB_WPB 0
 #endif
+// Row tiles per workgroup of the B >= 2 kernel, among 1, 2, 4 and 7 (7 not
+// for 3-bit codes): the least work on the busiest CU (256 CUs), counted as
+// rounds of one workgroup per CU times (tiles + 1), the 1 standing for the
+// activation loads a workgroup shares among its tiles; the larger tile on
+// ties.
+static inline int mfma_row_tiles(int64_t N, bool allow7) {
+  constexpr int64_t kCUs = 256;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int rt : {1, 2, 4, 7}) {
+    if (rt == 7 && !allow7) continue;
+    const int64_t tiles = (N + 16 * rt - 1) / (16 * rt);
+    const int64_t cost = (tiles + kCUs - 1) / kCUs * (rt + 1);
+    if (cost <= best_cost) { best = rt; best_cost = cost; }
+  }
+  return best;
+}
+
 template <int BITS, int G, bool CB = false>
 static hipError_t gemv_mfma_t(const uint32_t* codes, const uint32_t* meta, int64_t N, int64_t K,
                               const uint16_t* x, int64_t B, void* y, int y_bf16, hipStream_t s, Side sd,
@@ -768,8 +792,10 @@ static hipError_t gemv_mfma_t(const uint32_t* codes, const uint32_t* meta, int64
 #if QG_MB_RT && QG_MB_WPB
   return gemv_mfma_launch<BITS, G, QG_MB_RT, QG_MB_WPB, CB>(codes, meta, N, K, x, B, y, y_bf16, s, sd, bk);
 #else
-  const int rt = N >= 16384 ? 4 : (N >= 4096 ? 2 : 1), wpb = 4;
+  constexpr bool kAllow7 = BITS != 3;
+  const int rt = mfma_row_tiles(N, kAllow7), wpb = 4;
 #define L(R, W) if (rt == R && wpb == W) return gemv_mfma_launch<BITS, G, R, W, CB>(codes, meta, N, K, x, B, y, y_bf16, s, sd, bk)
+  if constexpr (kAllow7) L(7, 4);
   L(4, 4); L(2, 4); L(1, 4);
 #undef L
   return hipErrorInvalidValue;

@@ -102,3 +102,51 @@ def test_codebook_random_shape(gpu, bits, group, B, N, K):
     W_hat = oracle.codebook.dequantize(q, s, o, ids, books, bits, group)
     err = check_err(y[:, cols], oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
     say(f"  err={err:.2e}")
+
+
+# Tall matrices whose batched launch takes seven 16-row tiles per workgroup
+# (N of about 20000 and more; 3-bit codes take four), with a ragged last
+# workgroup: plain codes with one bf16 weight operand (K >= 512) and with the
+# hi + lo split (K < 512), outlier columns and codebooks.
+RT7_CASES = [
+    ("plain", 4, 64, 16, 28632, 1024),
+    ("plain", 3, 32, 8, 27000, 576),
+    ("plain", 2, 32, 5, 28672, 448),
+    ("plain", 5, 64, 3, 25000, 640),
+    ("plain", 6, 32, 2, 25001, 512),
+    ("outlier", 4, 64, 16, 28600, 1024),
+    ("outlier", 3, 32, 9, 25003, 448),
+    ("codebook", 4, 64, 16, 28600, 512),
+    ("codebook", 3, 32, 7, 25001, 448),
+]
+
+
+@pytest.mark.parametrize("kind,bits,group,B,N,K", RT7_CASES)
+def test_batched_seven_tile_workgroups(gpu, kind, bits, group, B, N, K):
+    say(f"gemv {kind} b={bits} g={group} B={B} N={N} K={K} (seven-tile workgroups)")
+    seed = N * 5 + K + B
+    W = gen_weights(N, K, rng_for(617, seed), outliers=True)
+    xv, xd = _x(B, K, "bf16", rng_for(618, seed))
+    cols = _cols(N, seed)
+    if kind == "plain":
+        codes, meta = gpu.qpack_group(dev(W), bits, group)
+        y = gpu.qgemv_group(codes, meta, N, K, bits, group, xd)
+        q, s, o = oracle.rtn.quantize(W[cols], bits, group)
+        W_hat = oracle.rtn.dequantize(q, s, o, group)
+    elif kind == "outlier":
+        c, m, sd, ix = gpu.qpack_group_outlier(dev(W), bits, group, 6)
+        y = gpu.qgemv_group_outlier(c, m, sd, ix, N, K, bits, group, xd)
+        idx = oracle.outlier.outlier_channels(W, 6)
+        assert np.array_equal(host(ix), idx.astype(np.int32))
+        q, s, o, side = oracle.outlier.encode_with(W[cols], bits, group, idx)
+        W_hat = oracle.outlier.reconstruct(q, s, o, group, side, idx)
+    else:
+        books = rng_for(619, seed).integers(0, 128, size=(8, 1 << bits)).astype(np.uint8)
+        bd = dev(books)
+        c, m, k = gpu.qpack_group_cb(dev(W), bits, group, bd)
+        y = gpu.qgemv_group_cb(c, m, k, bd, N, K, bits, group, xd)
+        q, s, o, ids = oracle.codebook.quantize(W[cols], bits, group, books)
+        W_hat = oracle.codebook.dequantize(q, s, o, ids, books, bits, group)
+    y = host(y).reshape(B, N)
+    err = check_err(y[:, cols], oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
+    say(f"  err={err:.2e}")
