@@ -150,3 +150,31 @@ def test_batched_seven_tile_workgroups(gpu, kind, bits, group, B, N, K):
     y = host(y).reshape(B, N)
     err = check_err(y[:, cols], oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
     say(f"  err={err:.2e}")
+
+
+# Binary GEMV shapes with tall second stages (N of 16000 to 28672) and
+# ragged last workgroups, one or several K-steps per table chunk, full and
+# general kernels, batch 1 and more.
+BIN_RT_CASES = [
+    (1, 28600, 1024, 512),
+    (3, 25001, 640, 4100),
+    (4, 28672, 512, 1024),
+    (2, 16384, 512, 2048),
+    (1, 16000, 1000, 3000),
+    (5, 20003, 448, 700),
+]
+
+
+@pytest.mark.parametrize("B,N,K,r", BIN_RT_CASES)
+def test_binlr_tall_stage2(gpu, B, N, K, r):
+    say(f"gemv binlr B={B} N={N} K={K} r={r} (tall second stage)")
+    seed = N * 11 + K * 5 + r + B
+    U, V, s1, s2 = gen_binlr(N, K, r, rng_for(620, seed))
+    ubd, vbd = gpu.qpack_binlr(dev(U), dev(V))
+    xv, xd = _x(B, K, "bf16", rng_for(621, seed))
+    y = host(gpu.qgemv_binlr(ubd, vbd, dev(s1.view(np.int16)), dev(s2.view(np.int16)), N, K, r, xd)).reshape(B, N)
+    cols = _cols(N, seed)
+    W = oracle.binlr.reconstruct(U[cols], V, s1[cols], s2)
+    err = check_err(y[:, cols], oracle.product.matmul_ref(W, xv),
+                    oracle.product.binlr_abs_denominator(U[cols], V, s1[cols], s2, xv))
+    say(f"  err={err:.2e}")
