@@ -292,7 +292,7 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         log("B16:", rows["gemv_4b_g64_gate_B16"])
     # whole 4-bit layer set at batch 1, and the mixed-width sets
     for label, spec in [("4b_g64", {"attn_bits": 4, "mlp_bits": 4, "group": 64})] + list(MIXED_SETS.items()):
-        if not (want(f"layer_set_{label}_B1") or (label == "4b_g64" and want("layer_set_4b_g64_B1_grouped"))):
+        if not (want(f"layer_set_{label}_B1") or want(f"layer_set_{label}_B1_grouped")):
             continue
         per = {}
         t_layer = 0.0
@@ -310,7 +310,7 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
             "per_matrix": per,
         }
         log(label, rows[f"layer_set_{label}_B1"]["GB/s"], "GB/s")
-    # the 4-bit layer set with q/k/v in one launch and gate/up in one launch
+    # each layer set with q/k/v in one launch and gate/up in one launch
     def grouped_row(specs, bits, group):
         """specs: [(name, W)] sharing K; one grouped launch per step."""
         K = specs[0][1].shape[1]
@@ -329,19 +329,23 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         torch.cuda.empty_cache()
         return {"us": round(ev / steps * 1e6, 3), "GB/s": round(nbytes * steps / ev / 1e9, 1), "bytes": nbytes}
 
-    if want("layer_set_4b_g64_B1_grouped"):
-        g_qkv = grouped_row([(n, layer_weights(n)) for n in ("q", "k", "v")], 4, 64)
-        g_gu = grouped_row([("gate", W_gate), ("up", W_gate)], 4, 64)
-        per = rows["layer_set_4b_g64_B1"]["per_matrix"]
+    for label, spec in [("4b_g64", {"attn_bits": 4, "mlp_bits": 4, "group": 64})] + list(MIXED_SETS.items()):
+        name = f"layer_set_{label}_B1_grouped"
+        if not want(name) or f"layer_set_{label}_B1" not in rows:
+            continue
+        gsz = spec["group"]
+        g_qkv = grouped_row([(n, layer_weights(n)) for n in ("q", "k", "v")], spec["attn_bits"], gsz)
+        g_gu = grouped_row([("gate", W_gate), ("up", W_gate)], spec["mlp_bits"], gsz)
+        per = rows[f"layer_set_{label}_B1"]["per_matrix"]
         t_layer = g_qkv["us"] + per["o"]["us"] + g_gu["us"] + per["down"]["us"]
         layer_b = g_qkv["bytes"] + per["o"]["bytes"] + g_gu["bytes"] + per["down"]["bytes"]
-        rows["layer_set_4b_g64_B1_grouped"] = {
+        rows[name] = {
             "sum_kernel_us_per_layer": round(t_layer, 2),
             "GB/s": round(layer_b / (t_layer * 1e-6) / 1e9, 1),
             "tok_s_equivalent_80_layers": round(1.0 / (N_LAYERS * t_layer * 1e-6), 1),
             "launches": {"qkv": g_qkv, "o": per["o"], "gate_up": g_gu, "down": per["down"]},
         }
-        log("grouped layer set:", rows["layer_set_4b_g64_B1_grouped"]["GB/s"], "GB/s")
+        log(f"grouped layer set {label}:", rows[name]["GB/s"], "GB/s")
     # the headline shape with its outlier channels kept aside in fp16 (0.1 %
     # of K = 8 channels); bytes = codes + meta + side columns
     def outlier_row(W, bits, group, n_out, B):

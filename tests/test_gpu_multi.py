@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from gpu_util import check_bf16_out, check_err, dev, dev_bf16, group_reference, host, say
-from workloads import gen_weights, gen_x_bf16, gen_x_f32, rng_for
+from workloads import gen_weights, gen_x_bf16, gen_x_f32, layer_weights, rng_for
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,8 @@ def test_fused_equals_separate_calls(gpu):
         assert torch.equal(y, y1)
 
 
-@pytest.mark.parametrize("bits,group,xkind", [(4, 64, "bf16"), (3, 32, "bf16"), (6, 32, "f32"), (2, 64, "bf16")])
+@pytest.mark.parametrize("bits,group,xkind", [(4, 64, "bf16"), (3, 32, "bf16"), (6, 32, "f32"), (2, 64, "bf16"),
+                                              (6, 32, "bf16"), (5, 32, "bf16"), (2, 32, "bf16")])
 @pytest.mark.parametrize("shapes", [[45, 7, 300], [100], [64, 1, 33, 17]])
 def test_against_oracle(gpu, bits, group, xkind, shapes):
     K = 512
@@ -80,3 +81,28 @@ def test_long_rows_split_k(gpu):
     ys = gpu.qgemv_group_multi([(c, m, n) for c, m, n, _ in mats], K, bits, group, dev_bf16(xb))
     for (c, m, n, W_hat), y in zip(mats, ys):
         check_err(host(y), oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
+
+
+@pytest.mark.parametrize("bits,group", [(6, 32), (5, 32), (3, 32), (2, 32)])
+def test_mixed_width_layer_shapes(gpu, bits, group):
+    """The grouped launches of the mixed-width layer sets at their real shapes
+    (q/k/v 8192 x 8192, 1024, 1024 with attention widths; gate/up 28672 x 2
+    with MLP widths), each matrix on sampled rows against the oracle."""
+    K = 8192
+    names = ("q", "k", "v") if bits >= 5 else ("gate", "up")
+    if bits >= 5:
+        Ws = [layer_weights(n) for n in names]
+    else:
+        Wg = layer_weights("gate")      # gate and up share the shape (and here the weights)
+        Ws = [Wg, Wg]
+    packed = [gpu.qpack_group(dev(W), bits, group) for W in Ws]
+    xb = gen_x_bf16(1, K, rng_for(333, bits))
+    xv = oracle.product.bf16_to_f64(xb)
+    say(f"grouped {'/'.join(names)} b={bits} g={group}")
+    ys = gpu.qgemv_group_multi([(c, m, W.shape[0]) for (c, m), W in zip(packed, Ws)], K, bits, group, dev_bf16(xb))
+    for W, y in zip(Ws, ys):
+        N = W.shape[0]
+        rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(N + bits).choice(N, 48, replace=False)]))
+        q, s, o = oracle.rtn.quantize(W[rows], bits, group)
+        W_hat = oracle.rtn.dequantize(q, s, o, group)
+        check_err(host(y)[0, rows], oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
