@@ -310,6 +310,29 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
             "per_matrix": per,
         }
         log(label, rows[f"layer_set_{label}_B1"]["GB/s"], "GB/s")
+    # the layer sets at their batches above 1 (4-bit set at 16, the mixed
+    # widths at 8): every token of the batch shares one pass over the weights
+    for label, spec, B in ([("4b_g64", {"attn_bits": 4, "mlp_bits": 4, "group": 64}, 16)]
+                           + [(lb, sp, 8) for lb, sp in MIXED_SETS.items()]):
+        name = f"layer_set_{label}_B{B}"
+        if not want(name):
+            continue
+        per = {}
+        t_layer = 0.0
+        for mat in ["q", "k", "v", "o", "gate", "up", "down"]:
+            bits = spec["attn_bits"] if mat in ATTN else spec["mlp_bits"]
+            Wn = W_gate if mat in ("gate", "up") else layer_weights(mat)
+            per[mat] = gemv_row(mat, Wn, bits, spec["group"], B)
+            t_layer += per[mat]["us"]
+        layer_b = sum(v["bytes"] for v in per.values())
+        rows[name] = {
+            "sum_kernel_us_per_layer": round(t_layer, 2),
+            "GB/s": round(layer_b / (t_layer * 1e-6) / 1e9, 1),
+            "batch": B,
+            "tok_s_80_layers": round(B / (N_LAYERS * t_layer * 1e-6), 1),
+            "per_matrix": per,
+        }
+        log(name, rows[name]["GB/s"], "GB/s")
     # each layer set with q/k/v in one launch and gate/up in one launch
     def grouped_row(specs, bits, group):
         """specs: [(name, W)] sharing K; one grouped launch per step."""
