@@ -315,7 +315,7 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
     for label, spec, B in ([("4b_g64", {"attn_bits": 4, "mlp_bits": 4, "group": 64}, 16)]
                            + [(lb, sp, 8) for lb, sp in MIXED_SETS.items()]):
         name = f"layer_set_{label}_B{B}"
-        if not want(name):
+        if not (want(name) or want(name + "_grouped")):
             continue
         per = {}
         t_layer = 0.0
@@ -334,14 +334,14 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         }
         log(name, rows[name]["GB/s"], "GB/s")
     # each layer set with q/k/v in one launch and gate/up in one launch
-    def grouped_row(specs, bits, group):
+    def grouped_row(specs, bits, group, B=1):
         """specs: [(name, W)] sharing K; one grouped launch per step."""
         K = specs[0][1].shape[1]
         packed = [cg.qpack_group(to_dev(W), bits, group) + (W.shape[0],) for _, W in specs]
         nbytes = sum(c.numel() + m.numel() * 4 for c, m, _ in packed)
         pool = pool_of(tuple(t for c, m, _ in packed for t in (c, m)), nbytes)
-        x = bf16(layer_x(K, 1))
-        ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for _, _, n in packed]
+        x = bf16(layer_x(K, B))
+        ys = [torch.empty((B, n), dtype=torch.float32, device=dev) for _, _, n in packed]
 
         def f(i):
             p = pool[i % len(pool)]
@@ -352,20 +352,22 @@ def measure_rows(cg, torch, np, dev, W_gate, to_dev, bf16, pool_of, time_launche
         torch.cuda.empty_cache()
         return {"us": round(ev / steps * 1e6, 3), "GB/s": round(nbytes * steps / ev / 1e9, 1), "bytes": nbytes}
 
-    for label, spec in [("4b_g64", {"attn_bits": 4, "mlp_bits": 4, "group": 64})] + list(MIXED_SETS.items()):
-        name = f"layer_set_{label}_B1_grouped"
-        if not want(name) or f"layer_set_{label}_B1" not in rows:
+    sets = [("4b_g64", {"attn_bits": 4, "mlp_bits": 4, "group": 64})] + list(MIXED_SETS.items())
+    for (label, spec), B in [(st, 1) for st in sets] + [(sets[0], 16)] + [(st, 8) for st in sets[1:]]:
+        name = f"layer_set_{label}_B{B}_grouped"
+        if not want(name) or f"layer_set_{label}_B{B}" not in rows:
             continue
         gsz = spec["group"]
-        g_qkv = grouped_row([(n, layer_weights(n)) for n in ("q", "k", "v")], spec["attn_bits"], gsz)
-        g_gu = grouped_row([("gate", W_gate), ("up", W_gate)], spec["mlp_bits"], gsz)
-        per = rows[f"layer_set_{label}_B1"]["per_matrix"]
+        g_qkv = grouped_row([(n, layer_weights(n)) for n in ("q", "k", "v")], spec["attn_bits"], gsz, B)
+        g_gu = grouped_row([("gate", W_gate), ("up", W_gate)], spec["mlp_bits"], gsz, B)
+        per = rows[f"layer_set_{label}_B{B}"]["per_matrix"]
         t_layer = g_qkv["us"] + per["o"]["us"] + g_gu["us"] + per["down"]["us"]
         layer_b = g_qkv["bytes"] + per["o"]["bytes"] + g_gu["bytes"] + per["down"]["bytes"]
         rows[name] = {
             "sum_kernel_us_per_layer": round(t_layer, 2),
             "GB/s": round(layer_b / (t_layer * 1e-6) / 1e9, 1),
-            "tok_s_equivalent_80_layers": round(1.0 / (N_LAYERS * t_layer * 1e-6), 1),
+            ("tok_s_equivalent_80_layers" if B == 1 else "tok_s_80_layers"):
+                round(B / (N_LAYERS * t_layer * 1e-6), 1),
             "launches": {"qkv": g_qkv, "o": per["o"], "gate_up": g_gu, "down": per["down"]},
         }
         log(f"grouped layer set {label}:", rows[name]["GB/s"], "GB/s")

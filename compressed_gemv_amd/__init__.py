@@ -256,8 +256,8 @@ def qgemv_group(codes, meta, N: int, K: int, bits: int, group: int, x: torch.Ten
 
 def qgemv_group_multi(mats, K: int, bits: int, group: int, x: torch.Tensor, ys=None,
                       y_dtype=torch.float32, stream=None):
-    """[y_i] for mats = [(codes_i, meta_i, N_i)] sharing x, K, bits, group; one
-    launch for batch 1."""
+    """[y_i] for mats = [(codes_i, meta_i, N_i)] sharing x, K, bits, group, in
+    one launch."""
     B = _batch(x, K)
     if ys is None:
         ys = [torch.empty((B, n), dtype=y_dtype, device=x.device) for (_, _, n) in mats]

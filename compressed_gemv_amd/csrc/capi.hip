@@ -157,15 +157,6 @@ int qgemv_group_multi(const qgroup_mat* mats, int count, int64_t K, int bits, in
   if (batched_x_ok(B, K) != Q_OK) return Q_EUNSUPPORTED;
   if (B > 1 && x_dtype != Q_BF16) return Q_EUNSUPPORTED;
   if (total > INT32_MAX || K > INT32_MAX) return Q_EUNSUPPORTED;
-  if (B > 1) {
-    for (int i = 0; i < count; ++i) {
-      const hipError_t e = qg::launch_gemv_group(static_cast<const uint32_t*>(mats[i].codes),
-                                                 static_cast<const uint32_t*>(mats[i].meta), mats[i].N, K, bits,
-                                                 group, x, x_dtype, B, mats[i].y, y_dtype, stream);
-      if (e != hipSuccess) return Q_EHIP;
-    }
-    return Q_OK;
-  }
   qg::MultiSegs ms{};
   int start = 0;
   for (int i = 0; i < 4; ++i) {
@@ -179,7 +170,7 @@ int qgemv_group_multi(const qgroup_mat* mats, int count, int64_t K, int bits, in
     }
   }
   ms.nseg = count;
-  return hip_status(qg::launch_gemv_group_multi(ms, K, bits, group, x, x_dtype, mats[0].y, y_dtype, stream));
+  return hip_status(qg::launch_gemv_group_multi(ms, K, bits, group, x, x_dtype, B, mats[0].y, y_dtype, stream));
 }
 
 int outlier_args_ok(int64_t K, int64_t n_out) {

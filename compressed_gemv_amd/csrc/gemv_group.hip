@@ -43,8 +43,22 @@ hipError_t launch_gemv_group(const uint32_t* codes, const uint32_t* meta, int64_
 }
 
 hipError_t launch_gemv_group_multi(const MultiSegs& ms, int64_t K, int bits, int group, const void* x,
-                                   int x_dtype, void* y0, int y_dtype, hipStream_t s) {
+                                   int x_dtype, int64_t B, void* y0, int y_dtype, hipStream_t s) {
   const int yb = y_dtype == 1;
+  if (B > 1) {   // one matrix-core launch over the matrices' tiles
+    if (x_dtype != 1) return hipErrorInvalidValue;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+#define CALLB(b, g) gemv_mfma_multi_t<b, g>(ms, K, xb, B, yb, s)
+    switch (bits * 100 + group) {
+      case 232: return CALLB(2, 32); case 264: return CALLB(2, 64);
+      case 332: return CALLB(3, 32); case 364: return CALLB(3, 64);
+      case 432: return CALLB(4, 32); case 464: return CALLB(4, 64);
+      case 532: return CALLB(5, 32); case 564: return CALLB(5, 64);
+      case 632: return CALLB(6, 32); case 664: return CALLB(6, 64);
+      default: return hipErrorInvalidValue;
+    }
+#undef CALLB
+  }
   int64_t N = 0;
   for (int i = 0; i < ms.nseg; ++i) N += ms.nrows[i];
   const Side none{nullptr, nullptr, 0};

@@ -395,12 +395,33 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 // staged in LDS first).
 // CB: codes read through per-group books; the pairs of decode_unit_cb give
 // e[q] exactly and one fma per weight gives fl32(s 2^(b-7) e[q] + o).
-template <int BITS, int G, int RT, int WPB, bool OUT, bool CB = false, bool SPLITW = true, bool PAIR = false>
+// MULTI: up to four matrices sharing K, width, group and x in one launch
+// (a layer's q/k/v or gate/up): workgroup w belongs to matrix m with
+// segs.start[m] <= w < segs.start[m + 1] (starts counted in workgroups,
+// unused ones INT_MAX) and takes its tile w - segs.start[m]; the matrix's
+// codes, group words, rows and output are picked with scalar selects.
+template <int BITS, int G, int RT, int WPB, bool OUT, bool CB = false, bool SPLITW = true, bool PAIR = false,
+          bool MULTI = false>
 __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
-    const uint32_t* __restrict__ codes, const uint32_t* __restrict__ meta, int N, int K,
-    const uint16_t* __restrict__ x, int B, void* __restrict__ yout, int y_bf16,
-    const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out, Books bk) {
+    const uint32_t* __restrict__ codes_in, const uint32_t* __restrict__ meta_in, int N_in, int K,
+    const uint16_t* __restrict__ x, int B, void* __restrict__ yout_in, int y_bf16,
+    const uint16_t* __restrict__ side, const int32_t* __restrict__ oidx, int n_out, Books bk, MultiSegs segs) {
   static_assert(!(CB && OUT), "codebooks come without outlier columns");
+  static_assert(!(MULTI && (CB || OUT)), "grouped launches take plain codes");
+  const uint32_t* codes = codes_in;
+  const uint32_t* meta = meta_in;
+  int N = N_in;
+  void* yout = yout_in;
+  int tile = blockIdx.x;
+  if constexpr (MULTI) {
+    const uint32_t w = blockIdx.x;
+    const int mi = (w >= (uint32_t)segs.start[1]) + (w >= (uint32_t)segs.start[2]) + (w >= (uint32_t)segs.start[3]);
+    codes = static_cast<const uint32_t*>(mi == 0 ? segs.codes[0] : (mi == 1 ? segs.codes[1] : (mi == 2 ? segs.codes[2] : segs.codes[3])));
+    meta = static_cast<const uint32_t*>(mi == 0 ? segs.meta[0] : (mi == 1 ? segs.meta[1] : (mi == 2 ? segs.meta[2] : segs.meta[3])));
+    yout = mi == 0 ? segs.y[0] : (mi == 1 ? segs.y[1] : (mi == 2 ? segs.y[2] : segs.y[3]));
+    N = (int)(mi == 0 ? segs.nrows[0] : (mi == 1 ? segs.nrows[1] : (mi == 2 ? segs.nrows[2] : segs.nrows[3])));
+    tile = (int)w - (mi == 0 ? segs.start[0] : (mi == 1 ? segs.start[1] : (mi == 2 ? segs.start[2] : segs.start[3])));
+  }
   static_assert(!(PAIR && (CB || SPLITW)), "pair loads: plain codes, one bf16 weight operand");
   __shared__ float red[WPB][RT * 4][64];
   __shared__ float xo[OUT ? 16 * 64 : 1];
@@ -415,7 +436,7 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int row_base = blockIdx.x * (16 * RT);
+  const int row_base = tile * (16 * RT);
   const int r = lane & 15, kg = lane >> 4;
   const int U = K >> 5, GN = K / G;
   const int bcol = lane & 15;
@@ -725,10 +746,10 @@ static hipError_t gemv_mfma_launch(const uint32_t* codes, const uint32_t* meta, 
   const dim3 grid((unsigned)tiles), block(64 * WPB);
 #define MF(O, C, S, SV, SI, SN)                                                                               \
   hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, O, C, S>), grid, block, 0, s, codes, meta, (int)N, (int)K, \
-                     x, (int)B, y, y_bf16, SV, SI, SN, bk)
+                     x, (int)B, y, y_bf16, SV, SI, SN, bk, MultiSegs{})
 #define MFP(O, SV, SI, SN)                                                                                     \
   hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, WPB, O, false, false, true>), grid, block, 0, s, codes, meta,   \
-                     (int)N, (int)K, x, (int)B, y, y_bf16, SV, SI, SN, bk)
+                     (int)N, (int)K, x, (int)B, y, y_bf16, SV, SI, SN, bk, MultiSegs{})
   const bool split = K < kGemvSplitBelowK;
   if constexpr (CB) {
     if (split) MF(false, true, true, nullptr, nullptr, 0);
@@ -800,6 +821,55 @@ static hipError_t gemv_mfma_t(const uint32_t* codes, const uint32_t* meta, int64
 #undef L
   return hipErrorInvalidValue;
 #endif
+}
+
+// Grouped launch for B >= 2: the matrices' tiles in one grid, the tile
+// count chosen as for one matrix but over the matrices' tiles together.
+template <int BITS, int G, int RT>
+static hipError_t gemv_mfma_multi_launch(const MultiSegs& ms, int64_t K, const uint16_t* x, int64_t B, int y_bf16,
+                                         hipStream_t s) {
+  MultiSegs mt = ms;
+  int64_t tiles = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (i < ms.nseg) {
+      mt.start[i] = (int)tiles;
+      tiles += (ms.nrows[i] + 16 * RT - 1) / (16 * RT);
+    } else {
+      mt.start[i] = INT32_MAX;
+    }
+  }
+  const dim3 grid((unsigned)tiles), block(64 * 4);
+  const uint32_t* c0 = static_cast<const uint32_t*>(ms.codes[0]);
+  const uint32_t* m0 = static_cast<const uint32_t*>(ms.meta[0]);
+  const Books nob{nullptr, nullptr, 0};
+  if (K < kGemvSplitBelowK)
+    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, 4, false, false, true, false, true>), grid, block, 0, s, c0, m0,
+                       (int)ms.nrows[0], (int)K, x, (int)B, ms.y[0], y_bf16, nullptr, nullptr, 0, nob, mt);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<BITS, G, RT, 4, false, false, false, true, true>), grid, block, 0, s, c0, m0,
+                       (int)ms.nrows[0], (int)K, x, (int)B, ms.y[0], y_bf16, nullptr, nullptr, 0, nob, mt);
+  return hipGetLastError();
+}
+
+template <int BITS, int G>
+static hipError_t gemv_mfma_multi_t(const MultiSegs& ms, int64_t K, const uint16_t* x, int64_t B, int y_bf16,
+                                    hipStream_t s) {
+  constexpr bool kAllow7 = BITS != 3;
+  constexpr int64_t kCUs = 256;
+  int rt = 1;
+  int64_t best = INT64_MAX;
+  for (int r : {1, 2, 4, 7}) {
+    if (r == 7 && !kAllow7) continue;
+    int64_t tiles = 0;
+    for (int i = 0; i < ms.nseg; ++i) tiles += (ms.nrows[i] + 16 * r - 1) / (16 * r);
+    const int64_t cost = (tiles + kCUs - 1) / kCUs * (r + 1);
+    if (cost <= best) { best = cost; rt = r; }
+  }
+  if constexpr (kAllow7)
+    if (rt == 7) return gemv_mfma_multi_launch<BITS, G, 7>(ms, K, x, B, y_bf16, s);
+  if (rt == 4) return gemv_mfma_multi_launch<BITS, G, 4>(ms, K, x, B, y_bf16, s);
+  if (rt == 2) return gemv_mfma_multi_launch<BITS, G, 2>(ms, K, x, B, y_bf16, s);
+  return gemv_mfma_multi_launch<BITS, G, 1>(ms, K, x, B, y_bf16, s);
 }
 
 }  // namespace qg

@@ -19,7 +19,7 @@ struct MultiSegs {
   int nseg;
 };
 hipError_t launch_gemv_group_multi(const MultiSegs& ms, int64_t K, int bits, int group, const void* x,
-                                   int x_dtype, void* y0, int y_dtype, hipStream_t s);
+                                   int x_dtype, int64_t B, void* y0, int y_dtype, hipStream_t s);
 
 // status word shared by the packers (per device)
 int* pack_status_ptr(hipError_t* err);

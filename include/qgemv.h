@@ -118,7 +118,8 @@ int qgemv_group(const void* codes, const void* meta, int64_t N, int64_t K,
 
 /* Several group-RTN matrices that share K, bits, group and the input x
  * (a decoder layer's q, k, v or its gate and up projections), multiplied in
- * one launch for B = 1 (one launch per matrix for B > 1): y_i = x W_i^T for
+ * one launch (for B > 1 one matrix-core launch over all the matrices' row
+ * tiles; each y_i equals a qgemv_group call bit for bit): y_i = x W_i^T for
  * each entry of mats (a HOST array of 1..4 entries; each codes/meta/y as in
  * qgemv_group, y_i [B][N_i]).  Same limits, dtypes and alignment as
  * qgemv_group (x 16-byte aligned); the sum of the N_i is below 2^31.

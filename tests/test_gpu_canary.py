@@ -115,8 +115,9 @@ def test_gemv_group(gpu, B, y_dtype):
     assert err <= 2e-3, err
 
 
-def test_gemv_group_multi(gpu):
-    K, bits, group = 448, 4, 64
+@pytest.mark.parametrize("B,K", [(1, 448), (6, 448), (6, 576)])
+def test_gemv_group_multi(gpu, B, K):
+    bits, group = 4, 64
     shapes = [70, 33]
     mats, refs = [], []
     for i, N in enumerate(shapes):
@@ -124,10 +125,10 @@ def test_gemv_group_multi(gpu):
         _, _, _, words, meta, W_hat = group_reference(W, bits, group)
         mats.append((dev(words.view(np.uint8).reshape(-1)), dev(meta.view(np.int32).reshape(-1)), N))
         refs.append(W_hat)
-    X = gen_x_bf16(1, K, rng_for(904, 0))
+    X = gen_x_bf16(B, K, rng_for(904, B))
     xd = dev_bf16(X)
     a, b = _twice(lambda y0, y1: gpu.qgemv_group_multi(mats, K, bits, group, xd, ys=[y0, y1]),
-                  lambda: (_out((1, 70), torch.float32), _out((1, 33), torch.float32)), "qgemv_group_multi")
+                  lambda: (_out((B, 70), torch.float32), _out((B, 33), torch.float32)), "qgemv_group_multi")
     Xv = oracle.product.bf16_to_f64(X)
     for i in range(2):
         _same(a[i], b[i], f"y{i}")

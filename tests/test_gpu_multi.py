@@ -52,7 +52,7 @@ def test_against_oracle(gpu, bits, group, xkind, shapes):
 
 
 def test_batched_and_bf16_output(gpu):
-    """B > 1 runs one launch per matrix through the same entry point; bf16
+    """B > 1 runs one matrix-core launch over all the matrices' tiles; bf16
     outputs round once."""
     K, bits, group = 1024, 5, 32
     mats = _mats(gpu, [200, 40], K, bits, group, 7)
@@ -106,3 +106,52 @@ def test_mixed_width_layer_shapes(gpu, bits, group):
         q, s, o = oracle.rtn.quantize(W[rows], bits, group)
         W_hat = oracle.rtn.dequantize(q, s, o, group)
         check_err(host(y)[0, rows], oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
+
+
+# Batched grouped launches: ragged matrices (tiles that end inside the
+# matrix, one-row matrices), K below 512 (weights as hi + lo) and at or
+# above it (pair loads, g64 blocks and g32), batch 2..16, and matrix counts
+# 1..4; every output equals a separate qgemv_group call bit for bit and
+# meets the oracle's bound.
+BATCHED_CASES = [
+    (4, 64, 16, 1024, [45, 7, 300]),
+    (4, 64, 5, 448, [100]),
+    (3, 32, 8, 576, [64, 1, 33, 17]),
+    (6, 32, 2, 512, [200, 16, 16]),
+    (2, 32, 9, 1024, [513, 511]),
+    (5, 64, 16, 320, [31, 64, 97]),
+]
+
+
+@pytest.mark.parametrize("bits,group,B,K,shapes", BATCHED_CASES)
+def test_batched_grouped_launch(gpu, bits, group, B, K, shapes):
+    say(f"grouped batched b={bits} g={group} B={B} K={K} N={shapes}")
+    mats = _mats(gpu, shapes, K, bits, group, 40 + bits + B)
+    xb = gen_x_bf16(B, K, rng_for(334, B * 100 + bits))
+    xv = oracle.product.bf16_to_f64(xb)
+    xd = dev_bf16(xb)
+    ys = gpu.qgemv_group_multi([(c, m, n) for c, m, n, _ in mats], K, bits, group, xd)
+    for (c, m, n, W_hat), y in zip(mats, ys):
+        y1 = gpu.qgemv_group(c, m, n, K, bits, group, xd)
+        assert torch.equal(y, y1), "grouped launch differs from a separate call"
+        check_err(host(y).reshape(B, n), oracle.product.matmul_ref(W_hat, xv),
+                  oracle.product.abs_denominator(W_hat, xv))
+
+
+def test_batched_grouped_layer_shapes(gpu):
+    """q/k/v of the 4-bit layer set at batch 16 in one launch: sampled rows
+    against the oracle, every output equal to a separate call."""
+    K = 8192
+    Ws = [layer_weights(n) for n in ("q", "k", "v")]
+    packed = [gpu.qpack_group(dev(W), 4, 64) for W in Ws]
+    xb = gen_x_bf16(16, K, rng_for(335, 16))
+    xv = oracle.product.bf16_to_f64(xb)
+    xd = dev_bf16(xb)
+    ys = gpu.qgemv_group_multi([(c, m, W.shape[0]) for (c, m), W in zip(packed, Ws)], K, 4, 64, xd)
+    for (c, m), W, y in zip(packed, Ws, ys):
+        N = W.shape[0]
+        assert torch.equal(y, gpu.qgemv_group(c, m, N, K, 4, 64, xd))
+        rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(N).choice(N, 32, replace=False)]))
+        q, s, o = oracle.rtn.quantize(W[rows], 4, 64)
+        W_hat = oracle.rtn.dequantize(q, s, o, 64)
+        check_err(host(y)[:, rows], oracle.product.matmul_ref(W_hat, xv), oracle.product.abs_denominator(W_hat, xv))
