@@ -202,6 +202,26 @@ void test_centroids_and_rotation() {
   REJECT(Q_EINVAL, qtq_rotation(0, G.data(), Q.data()));
 }
 
+// The batched GEMV's workgroup counts: row tiles per workgroup chosen so
+// the workgroups spread evenly over 256 CUs (7 tiles of 16 rows at N = 28672,
+// 4 for 3-bit codes, 2 at 8192, 1 at 1024; grouped launches count the
+// matrices' tiles together), 4 waves each.
+void test_tile_choice() {
+  struct Case { int64_t N; int bits, g; unsigned grid; };
+  for (const Case& c : {Case{28672, 4, 64, 256}, Case{28672, 2, 32, 256}, Case{28672, 3, 32, 448},
+                        Case{8192, 6, 32, 256}, Case{1024, 4, 64, 64}, Case{28600, 4, 64, 256}}) {
+    ACCEPT(qgemv_group(dp(2), dp(3), c.N, 8192, c.bits, c.g, dp(6), Q_BF16, 16, dp(7), Q_F32, S));
+    CHECK(fake_hip_last_grid_x() == c.grid && fake_hip_last_block_x() == 256,
+          "batched GEMV N %lld %d-bit: grid %u block %u, expected grid %u", (long long)c.N, c.bits,
+          fake_hip_last_grid_x(), fake_hip_last_block_x(), c.grid);
+  }
+  qgroup_mat qkv[3] = {{dp(2), dp(3), 8192, dp(7)}, {dp(8), dp(9), 1024, dp(10)}, {dp(11), dp(12), 1024, dp(13)}};
+  const long before = fake_hip_launches();
+  ACCEPT(qgemv_group_multi(qkv, 3, 8192, 4, 64, dp(6), Q_BF16, 16, Q_F32, S));
+  CHECK(fake_hip_launches() == before + 1, "grouped batched GEMV: %ld launches", fake_hip_launches() - before);
+  CHECK(fake_hip_last_grid_x() == 160, "grouped q/k/v: grid %u, expected 160 (4 tiles each)", fake_hip_last_grid_x());
+}
+
 void test_group_paths() {
   for (int bits = 2; bits <= 6; ++bits)
     for (int g : {32, 64})
@@ -447,6 +467,7 @@ int main() {
   test_codebooks();
   test_centroids_and_rotation();
   test_group_paths();
+  test_tile_choice();
   test_binlr_paths();
   test_prefill_paths();
   test_key_cache_paths();

@@ -34,6 +34,7 @@ std::map<const void*, std::vector<unsigned char>> g_vars;   // host shadow -> "d
 long g_launches = 0;
 long g_bad_launches = 0;
 std::string g_last_kernel;
+dim3 g_last_grid, g_last_block;
 
 constexpr size_t kMaxLds = 160 * 1024;
 
@@ -44,6 +45,8 @@ extern "C" {
 long fake_hip_launches(void) { return g_launches; }
 long fake_hip_bad_launches(void) { return g_bad_launches; }
 const char* fake_hip_last_kernel(void) { return g_last_kernel.c_str(); }
+unsigned fake_hip_last_grid_x(void) { return g_last_grid.x; }
+unsigned fake_hip_last_block_x(void) { return g_last_block.x; }
 
 void** __hipRegisterFatBinary(const void*) {
   static void* handle = nullptr;
@@ -81,6 +84,8 @@ hipError_t hipLaunchKernel(const void* f, dim3 grid, dim3 block, void** args, si
   ++g_launches;
   auto it = g_kernels.find(f);
   g_last_kernel = it == g_kernels.end() ? "<unregistered>" : it->second;
+  g_last_grid = grid;
+  g_last_block = block;
   const unsigned long long threads = (unsigned long long)block.x * block.y * block.z;
   const bool ok = it != g_kernels.end() && args != nullptr && grid.x >= 1 && grid.y >= 1 && grid.z >= 1 &&
                   grid.x <= 0x7fffffffu && grid.y <= 65535 && grid.z <= 65535 && threads >= 1 && threads <= 1024 &&
