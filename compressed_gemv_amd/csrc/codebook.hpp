@@ -23,7 +23,8 @@ struct Books { const uint8_t* ids; const uint8_t* dict; int n; };   // n = 0: pl
 // 4-bit codes: four codes per two permutes (entries 0..7 and 8..15) plus a
 // third that keeps, byte by byte, the half that code bit 3 names.  A final
 // permute or masked OR writes the 0x43 high bytes (bf16 128 + e, exact for
-// e <= 127).
+// e <= 127), or, with F16, zero high bytes: the fp16 subnormal e * 2^-24,
+// which v_fma_mix_f32 scales and offsets in one instruction.
 // Constants of the lookups, held in opaque registers (made once per kernel)
 // so the masked ORs compile to single v_and_or_b32 (gfx9 VOP3 takes no
 // literal operands).
@@ -34,10 +35,10 @@ __device__ __forceinline__ CbConst cb_consts() {
   return k;
 }
 
-template <int B>
+template <int B, bool F16 = false>
 __device__ __forceinline__ void decode_unit_cb(const uint32_t (&w)[B], const uint32_t (&T)[4],
                                                uint32_t (&pr)[16], const CbConst& kc) {
-  constexpr uint32_t k43 = 0x43434343u;
+  constexpr uint32_t k43 = F16 ? 0u : 0x43434343u;
   if constexpr (B == 2) {
 #pragma unroll
     for (int wi = 0; wi < 2; ++wi)
@@ -49,7 +50,10 @@ __device__ __forceinline__ void decode_unit_cb(const uint32_t (&w)[B], const uin
         pr[8 * wi + j + 4] = __builtin_amdgcn_perm(k43, r, 0x04030401u);
       }
   } else if constexpr (B == 3) {
-    auto look = [&](uint32_t t) { return (__builtin_amdgcn_perm(T[1], T[0], t) & kc.lo16) | kc.bias; };
+    auto look = [&](uint32_t t) {
+      const uint32_t v = __builtin_amdgcn_perm(T[1], T[0], t) & kc.lo16;
+      return F16 ? v : (v | kc.bias);
+    };
 #pragma unroll
     for (int k = 0; k < 15; ++k) pr[k] = look((w[k / 5] >> (3 * (k % 5))) & 0x00070007u);
     uint32_t t = 0;

@@ -393,8 +393,9 @@ __global__ __launch_bounds__(512) void gemv_b1_kernel(
 // OUT: outlier side columns as in the B = 1 kernel, added to each output
 // in the final reduction (the activations of the outlier channels are
 // staged in LDS first).
-// CB: codes read through per-group books; the pairs of decode_unit_cb give
-// e[q] exactly and one fma per weight gives fl32(s 2^(b-7) e[q] + o).
+// CB: codes read through per-group books; decode_unit_cb gives e[q] exactly
+// as the fp16 subnormal e[q] 2^-24 and one v_fma_mix_f32 per weight gives
+// fl32(s 2^(b-7) e[q] + o).
 // MULTI: up to four matrices sharing K, width, group and x in one launch
 // (a layer's q/k/v or gate/up): workgroup w belongs to matrix m with
 // segs.start[m] <= w < segs.start[m + 1] (starts counted in workgroups,
@@ -535,13 +536,15 @@ __global__ __launch_bounds__(64 * WPB) void gemv_mfma_kernel(
         const uint32_t* tp = dict + ((bk_[t] & 15u) << BITS) / 4;   // ids < 16 (packer)
 #pragma unroll
         for (int i = 0; i < (1 << BITS) / 4; ++i) T[i] = tp[i];
-        decode_unit_cb<BITS>(bw[t], T, pr, kc);
-        const float sc = s * (1.0f / (float)(1 << (7 - BITS)));
+        // entries as fp16 subnormals e * 2^-24: one v_fma_mix_f32 per weight
+        // gives fl32(s 2^(b-7) e + o), as for plain codes
+        decode_unit_cb<BITS, true>(bw[t], T, pr, kc);
+        const float sc = s * (float)(1 << (24 - (7 - BITS)));
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const PairInfo pi = UN::pair(k);
-          wv[pi.ca] = __builtin_fmaf(bf16_lo_to_f32(pr[k]) - 128.0f, sc, o);
-          wv[pi.cb] = __builtin_fmaf(bf16_hi_to_f32(pr[k]) - 128.0f, sc, o);
+          wv[pi.ca] = __builtin_fmaf(f16_lo(pr[k]), sc, o);
+          wv[pi.cb] = __builtin_fmaf(f16_hi(pr[k]), sc, o);
         }
       } else {
         decode_unit_h<BITS>(bw[t], pr);
