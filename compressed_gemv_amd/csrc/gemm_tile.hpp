@@ -142,15 +142,16 @@ struct DecCB {
     const uint32_t* tp = lds_dict + ((r.k & 15u) << BITS) / 4;   // ids < 16 (packer)
 #pragma unroll
     for (int i = 0; i < (1 << BITS) / 4; ++i) T[i] = tp[i];
+    // entries as fp16 subnormals e * 2^-24: one v_fma_mix_f32 per weight
     uint32_t pr[16];
-    decode_unit_cb<BITS>(r.w, T, pr, kc);
-    const float s = f16_bits_to_f32(r.m & 0xFFFFu) * (1.0f / (float)(1 << (7 - BITS)));
+    decode_unit_cb<BITS, true>(r.w, T, pr, kc);
+    const float s = f16_bits_to_f32(r.m & 0xFFFFu) * (float)(1 << (24 - (7 - BITS)));
     const float o = f16_bits_to_f32(r.m >> 16);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const PairInfo pi = Unit<BITS>::pair(k);
-      wv[pi.ca] = __builtin_fmaf(bf16_lo_to_f32(pr[k]) - 128.0f, s, o);
-      wv[pi.cb] = __builtin_fmaf(bf16_hi_to_f32(pr[k]) - 128.0f, s, o);
+      wv[pi.ca] = __builtin_fmaf(f16_lo(pr[k]), s, o);
+      wv[pi.cb] = __builtin_fmaf(f16_hi(pr[k]), s, o);
     }
   }
   __device__ __forceinline__ void decode(const Raw& r, uint32_t (&outp)[16]) const {
